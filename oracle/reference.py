@@ -1,0 +1,322 @@
+"""fp64 CPU oracle for paged-KV scaled dot-product attention.
+
+TEST INFRASTRUCTURE ONLY.  Only `tests/`, `__graft_entry__.smoke()` and the
+`cpu_baseline` leg of `bench.py` may import this module.  It shares no code with
+the HIP library (no kernels, headers, helpers or tables) and never reads
+anything the GPU produced: attention is computed from the logical per-sequence
+K/V rows as the input generator drew them, not from the paged cache or a block
+table (the independence rule of the CSA2 Vanilla golden PR, "Description":
+geometry from independent sources; the golden never reads kernel-produced
+slot or page tables).
+
+Everything is float64.  Inputs arrive as raw storage bits and are widened
+exactly (bf16 -> f32 is a 16-bit shift; f16 and f32 widen exactly to f64).
+
+What the method computes (the Spyre paged-attention PR, "Description", six
+steps; the vllm-omni piecewise block-causal PR for the block-causal mask):
+  scatter  : cache[slot // B][slot % B] = new row, raw copy, slot < 0 skipped
+  gather   : logical row p of sequence s = cache[table[s][p // B]][p % B]
+  positions: query row i of a chunk of q_s new tokens sits at a = (L_s - q_s) + i
+  visible  : key p < L_s and   NONE: always
+                               CAUSAL: p <= a (bottom-right aligned)
+                               BLOCK_CAUSAL(span): p <= a or p // span == a // span
+  scores   : z_p = scale * <q, k_p>, q head h reads kv head h // (H / Hkv)
+  softmax  : stable: m = max z, w = exp(z - m), out = sum w v / sum w, lse = m + log sum w
+  empty row: no visible key -> out = 0, lse = -inf
+
+Parity status of each function is stated in its docstring; every function here
+is pinned by `tests/test_oracle_pins.py` against something other than itself.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+MASK_NONE, MASK_CAUSAL, MASK_BLOCK_CAUSAL = 0, 1, 2
+
+
+# ----------------------------------------------------------------------------------------
+# exact widening of storage bits
+# ----------------------------------------------------------------------------------------
+
+def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Raw storage bits -> float64, exactly (no rounding happens in any branch)."""
+    bits = np.asarray(bits)
+    if dtype == "f32":
+        return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------------------
+# step 1: slot_mapping scatter (raw copy) -- Spyre PR, "Description", step 1
+# ----------------------------------------------------------------------------------------
+
+def kv_cache_write(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
+                   value: np.ndarray, slot_mapping: np.ndarray, block_size: int):
+    """Return copies of the caches [NB, B, Hkv, D] with each token's row written at its slot.
+
+    A negative slot marks a padding token and is skipped (reading A1).  Slots must be
+    unique within one call and inside the pool.  Untouched slots keep their old bits.
+    """
+    kc, vc = key_cache.copy(), value_cache.copy()
+    nb = kc.shape[0]
+    seen = set()
+    for t in range(slot_mapping.shape[0]):
+        slot = int(slot_mapping[t])
+        if slot < 0:
+            continue
+        assert slot < nb * block_size, "slot outside the block pool"
+        assert slot not in seen, "duplicate slot within one call"
+        seen.add(slot)
+        blk, off = slot // block_size, slot % block_size
+        kc[blk, off] = key[t]
+        vc[blk, off] = value[t]
+    return kc, vc
+
+
+# ----------------------------------------------------------------------------------------
+# step 2: block-table gather -- Spyre PR, "Description", step 2
+# ----------------------------------------------------------------------------------------
+
+def gather_sequence(cache: np.ndarray, table_row: np.ndarray, seq_len: int, block_size: int):
+    """Logical rows 0..L-1 of one sequence: row p lives in block table_row[p // B], slot p % B."""
+    out = np.empty((seq_len,) + cache.shape[2:], cache.dtype)
+    for p in range(seq_len):
+        out[p] = cache[int(table_row[p // block_size]), p % block_size]
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# steps 3-6: masked, scaled, stable-softmax attention per sequence
+# ----------------------------------------------------------------------------------------
+
+def kv_head_of(h: int, num_heads: int, num_kv_heads: int) -> int:
+    """Query head h reads the kv head that repeat_interleave would have copied into slot h
+    (Spyre PR, "Description": GQA by repeat_interleave on the KV heads)."""
+    group = num_heads // num_kv_heads
+    return h // group
+
+
+def is_visible(p: int, a: int, seq_len: int, mask: int, span_len: int) -> bool:
+    """Key position p is visible to the query at absolute position a.
+
+    CAUSAL is bottom-right aligned (vllm-omni piecewise PR: rightDownCausal contract,
+    Sq <= Skv); BLOCK_CAUSAL is the dense `(q >= kv) or same block` rule of that PR's
+    reference, with blocks tiling absolute positions from 0 in steps of span_len.
+    """
+    if p >= seq_len:
+        return False
+    if mask == MASK_NONE:
+        return True
+    if mask == MASK_CAUSAL:
+        return p <= a
+    if mask == MASK_BLOCK_CAUSAL:
+        return p <= a or (p // span_len) == (a // span_len)
+    raise ValueError(mask)
+
+
+def visibility_matrix(positions: np.ndarray, seq_len: int, mask: int, span_len: int):
+    """Boolean [len(positions), seq_len] matrix of is_visible, built entry by entry."""
+    vis = np.zeros((len(positions), seq_len), bool)
+    for i, a in enumerate(positions):
+        for p in range(seq_len):
+            vis[i, p] = is_visible(p, int(a), seq_len, mask, span_len)
+    return vis
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray, scale: float):
+    """One sequence, one query head: q [n, D], k/v [L, D], vis [n, L] -> out [n, D], lse [n].
+
+    z = scale * q k^T (a matmul as a library step), excluded keys dropped, then the
+    stable softmax: subtract the row max, exponentiate, normalise.  A row with no
+    visible key gives zeros and lse = -inf (reading A6).
+    """
+    n, D = q.shape
+    out = np.zeros((n, v.shape[1]), np.float64)
+    lse = np.full(n, -np.inf)
+    if n == 0 or k.shape[0] == 0:
+        return out, lse
+    z = scale * (q @ k.T)
+    for i in range(n):
+        sel = vis[i]
+        if not sel.any():
+            continue
+        zi = z[i, sel]
+        m = zi.max()
+        w = np.exp(zi - m)
+        l = w.sum()
+        out[i] = (w @ v[sel]) / l
+        lse[i] = m + math.log(l)
+    return out, lse
+
+
+def paged_attention(query: np.ndarray, keys: Sequence[np.ndarray], values: Sequence[np.ndarray],
+                    cu_seqlens_q: np.ndarray, seq_lens: np.ndarray, num_kv_heads: int,
+                    scale: float, mask: int, span_len: int = 0,
+                    rows: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None):
+    """Attention of a flat (THD) query batch over per-sequence logical K/V.
+
+    query [T, H, D] float64; keys[s], values[s] [L_s, Hkv, D] float64.  Sequence s owns
+    query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1, which are its newest tokens, so
+    row i of the chunk sits at absolute position a = L_s - q_s + i (chunked prefill;
+    decode is the case q_s = 1).  Returns out [T, H, D] and lse [T, H]; with `rows`
+    (flat row indices) / `heads` given, only those entries are computed (the rest stay
+    zero / -inf) so that large batches can be sampled.
+    """
+    T, H, D = query.shape
+    out = np.zeros((T, H, values[0].shape[-1] if len(values) else D), np.float64)
+    lse = np.full((T, H), -np.inf)
+    want_rows = None if rows is None else set(int(r) for r in rows)
+    head_list = range(H) if heads is None else [int(h) for h in heads]
+    for s in range(len(seq_lens)):
+        L = int(seq_lens[s])
+        r0, r1 = int(cu_seqlens_q[s]), int(cu_seqlens_q[s + 1])
+        q_s = r1 - r0
+        ctx = L - q_s
+        assert ctx >= 0, "a query chunk longer than its sequence"
+        row_ids = [r for r in range(r0, r1) if want_rows is None or r in want_rows]
+        if not row_ids:
+            continue
+        positions = np.array([ctx + (r - r0) for r in row_ids], np.int64)
+        vis = visibility_matrix(positions, L, mask, span_len)
+        for h in head_list:
+            kvh = kv_head_of(h, H, num_kv_heads)
+            o, l = attend(query[row_ids, h, :], keys[s][:, kvh, :], values[s][:, kvh, :], vis, scale)
+            out[row_ids, h, :] = o
+            lse[row_ids, h] = l
+    return out, lse
+
+
+def split_logical(rows: np.ndarray, cu_seq_lens: np.ndarray):
+    """Per-sequence views of a sequence-major row array [sum L, ...]."""
+    return [rows[cu_seq_lens[s]:cu_seq_lens[s + 1]] for s in range(len(cu_seq_lens) - 1)]
+
+
+def workload_attention(w, rows=None, heads=None):
+    """Oracle output for a generated workload (float64), from its logical K/V."""
+    q = widen(w.query, w.dtype)
+    k = split_logical(widen(w.key, w.dtype), w.cu_seq_lens)
+    v = split_logical(widen(w.value, w.dtype), w.cu_seq_lens)
+    return paged_attention(q, k, v, w.cu_seqlens_q, w.seq_lens, w.num_kv_heads, w.scale,
+                           w.mask, w.span_len, rows=rows, heads=heads)
+
+
+# ----------------------------------------------------------------------------------------
+# cross-split merge by log-sum-exp (the flash-decoding combine)
+# ----------------------------------------------------------------------------------------
+
+def lse_merge(outs: Sequence[np.ndarray], lses: Sequence[np.ndarray]):
+    """Combine attention results over disjoint key subsets: weights exp(lse_j - max lse)."""
+    lses = np.stack(lses)            # [J, ...]
+    outs = np.stack(outs)            # [J, ..., D]
+    M = lses.max(axis=0)
+    finite = np.isfinite(M)
+    Msafe = np.where(finite, M, 0.0)
+    w = np.where(np.isfinite(lses), np.exp(lses - Msafe), 0.0)
+    tot = w.sum(axis=0)
+    num = (w[..., None] * outs).sum(axis=0)
+    out = np.where(tot[..., None] > 0, num / np.where(tot > 0, tot, 1.0)[..., None], 0.0)
+    lse = np.where(tot > 0, Msafe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------------------
+# second formulations and the brute-force twin (used as pins)
+# ----------------------------------------------------------------------------------------
+
+def brute_force(query, keys, values, cu_seqlens_q, seq_lens, num_kv_heads, scale, mask, span_len=0):
+    """Scalar triple loops with math.exp, no numpy arithmetic: tiny inputs only.
+
+    Independent of the helpers above on purpose: the head map, the chunk positions and
+    the mask rules are written out again here from the definition, in a different form
+    (the block-causal rule as "key's block no later than the query's block").
+    """
+    T, H, D = query.shape
+    out = [[[0.0] * D for _ in range(H)] for _ in range(T)]
+    for s in range(len(seq_lens)):
+        L = int(seq_lens[s])
+        r0, r1 = int(cu_seqlens_q[s]), int(cu_seqlens_q[s + 1])
+        for r in range(r0, r1):
+            a = L - (r1 - r0) + (r - r0)
+            for h in range(H):
+                kvh = h // (H // num_kv_heads)
+                zs = []
+                for p in range(L):
+                    if mask == MASK_CAUSAL and p > a:
+                        continue
+                    if mask == MASK_BLOCK_CAUSAL and (p // span_len) > (a // span_len):
+                        continue
+                    acc = 0.0
+                    for d in range(D):
+                        acc += float(query[r, h, d]) * float(keys[s][p, kvh, d])
+                    zs.append((p, scale * acc))
+                if not zs:
+                    continue
+                m = max(z for _, z in zs)
+                den = 0.0
+                num = [0.0] * D
+                for p, z in zs:
+                    e = math.exp(z - m)
+                    den += e
+                    for d in range(D):
+                        num[d] += e * float(values[s][p, kvh, d])
+                for d in range(D):
+                    out[r][h][d] = num[d] / den
+    return np.array(out, np.float64).reshape(T, H, D)
+
+
+def fused_head_attention(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray,
+                         scale: float, num_kv_heads: int):
+    """The block-diagonal fused-head form of the Spyre PR ("Description"): all heads in one
+    2D product.  K (after repeat_interleave) is stacked to [H*L, D], Q^T to [D, H*n];
+    kq = K Q^T is [H*L, H*n]; cross-head entries are excluded by a block-diagonal mask and
+    semantic exclusions by `vis`; softmax runs over the KV axis (axis 0) and the weights
+    multiply the stacked V.  q_rows [n, H, D], k/v [L, Hkv, D] -> [n, H, D]."""
+    n, H, D = q_rows.shape
+    L = k.shape[0]
+    g = H // num_kv_heads
+    ke = np.repeat(k, g, axis=1)                     # [L, H, D]
+    ve = np.repeat(v, g, axis=1)
+    kst = ke.transpose(1, 0, 2).reshape(H * L, D)    # head-major stack
+    vst = ve.transpose(1, 0, 2).reshape(H * L, -1)
+    qt = q_rows.transpose(1, 0, 2).reshape(H * n, D).T
+    kq = scale * (kst @ qt)                          # [H*L, H*n]
+    allowed = np.zeros((H * L, H * n), bool)
+    for h in range(H):
+        allowed[h * L:(h + 1) * L, h * n:(h + 1) * n] = vis.T
+    kq = np.where(allowed, kq, -np.inf)
+    col_max = kq.max(axis=0)
+    col_max = np.where(np.isfinite(col_max), col_max, 0.0)
+    w = np.exp(kq - col_max)                         # exp(-inf) = 0 off the diagonal blocks
+    den = w.sum(axis=0)
+    o = (w.T @ vst) / np.where(den > 0, den, 1.0)[:, None]   # [H*n, D]
+    o = np.where((den > 0)[:, None], o, 0.0)
+    return o.reshape(H, n, -1).transpose(1, 0, 2)
+
+
+def piecewise_segments(spans: Sequence[tuple], seq_len: int):
+    """Segment plan of the vllm-omni piecewise PR for one sequence.
+
+    `spans` lists (start, end, kind) covering [0, seq_len), kind 'causal' or 'full'.  Each
+    span becomes one segment (q_start, q_end, kv_end, causal): a causal segment attends
+    K[:q_end] bottom-right causally (kv_end == q_end), a full segment attends the whole
+    prefix K[:q_end] without a mask.
+    """
+    segs = []
+    for (s, e, kind) in spans:
+        e = min(e, seq_len)
+        if s >= e:
+            continue
+        segs.append((s, e, e, kind == "causal"))
+    return segs
+
+
+def uniform_spans(seq_len: int, span_len: int):
+    """BLOCK_CAUSAL as a span list: full spans of span_len tiling [0, L) (last one partial)."""
+    return [(s, min(s + span_len, seq_len), "full") for s in range(0, seq_len, span_len)]

@@ -1,0 +1,431 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each test names the passage or the mathematical fact it rests on.  The last block
+plants plausible mistakes into the oracle (on the CPU, by monkeypatching) and checks
+that at least one pin catches each of them, following the fail-before / pass-after
+evidence protocol of the vllm-omni piecewise block-causal PR (review thread).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from torch.nn.attention.bias import causal_lower_right
+
+import oracle
+from oracle import reference as ref
+from paged_kv_scaled_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_seq(rng, L, H, Hkv, D):
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, Hkv, D))
+    v = rng.standard_normal((L, Hkv, D))
+    return q, k, v
+
+
+def _one_seq(q, k, v, q_len, mask, span=0, scale=0.3, Hkv=None):
+    """Oracle for one sequence whose last q_len tokens are the queries."""
+    L = k.shape[0]
+    cu = np.array([0, q_len], np.int32)
+    return ref.paged_attention(q, [k], [v], cu, np.array([L], np.int32), Hkv or k.shape[1],
+                               scale, mask, span)
+
+
+def _sdpa(q, k, v, scale, attn_mask=None, is_causal=False, gqa=False):
+    """torch CPU float64 SDPA on [n, H, D] / [L, Hkv, D] arrays (the textbook routine)."""
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(k).permute(1, 0, 2)[None]
+    tv = torch.from_numpy(v).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=attn_mask, is_causal=is_causal,
+                                       scale=scale, enable_gqa=gqa)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+# ----------------------------------------------------------------------------------------
+# exact widening of the storage bits
+# ----------------------------------------------------------------------------------------
+
+def test_widen_known_bit_patterns():
+    bf = np.array([0x3F80, 0xC000, 0x3E80, 0x0000, 0x8000, 0x4049], np.uint16)
+    assert list(ref.widen(bf, "bf16")) == [1.0, -2.0, 0.25, 0.0, -0.0, 3.140625]
+    h = np.array([0x3C00, 0xC000, 0x3400, 0x7BFF], np.uint16)
+    assert list(ref.widen(h, "f16")) == [1.0, -2.0, 0.25, 65504.0]
+    f = np.array([0x3F800000, 0x40490FDB], np.uint32)
+    assert ref.widen(f, "f32")[0] == 1.0
+    assert ref.widen(f, "f32")[1] == float(np.float32(np.pi))
+
+
+def test_generator_rounding_matches_torch():
+    """The generator's RNE cast agrees with torch's own float32 -> bf16/f16 conversion."""
+    x = np.random.default_rng(7).standard_normal(100000).astype(np.float32) * 3
+    x[:4] = [1.00390625, 1.01171875, -1.00390625, 0.0]   # ties at bf16 precision
+    tb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(wl.round_to_storage(x, "bf16"), tb)
+    th = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(wl.round_to_storage(x, "f16"), th)
+    # the widened value is the torch value exactly
+    assert np.array_equal(ref.widen(tb, "bf16"),
+                          torch.from_numpy(x).to(torch.bfloat16).double().numpy())
+
+
+# ----------------------------------------------------------------------------------------
+# brute force (P12) and the textbook routine (P7)
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(24))
+def test_brute_force_agrees(seed):
+    w = wl.random_small(seed, "f32")
+    q = ref.widen(w.query, "f32")
+    ks = ref.split_logical(ref.widen(w.key, "f32"), w.cu_seq_lens)
+    vs = ref.split_logical(ref.widen(w.value, "f32"), w.cu_seq_lens)
+    o, _ = ref.paged_attention(q, ks, vs, w.cu_seqlens_q, w.seq_lens, w.num_kv_heads, w.scale,
+                               w.mask, w.span_len)
+    b = ref.brute_force(q, ks, vs, w.cu_seqlens_q, w.seq_lens, w.num_kv_heads, w.scale, w.mask,
+                        w.span_len)
+    assert np.max(np.abs(o - b)) <= 1e-12
+
+
+def test_tiny_prefill_brute_force():
+    w = wl.tiny_prefill()
+    o, _ = ref.workload_attention(w)
+    q = ref.widen(w.query, "f32")
+    ks = ref.split_logical(ref.widen(w.key, "f32"), w.cu_seq_lens)
+    vs = ref.split_logical(ref.widen(w.value, "f32"), w.cu_seq_lens)
+    b = ref.brute_force(q, ks, vs, w.cu_seqlens_q, w.seq_lens, 2, 0.25, wl.MASK_CAUSAL)
+    assert np.max(np.abs(o - b)) <= 1e-12
+
+
+@pytest.mark.parametrize("mask", [ref.MASK_NONE, ref.MASK_CAUSAL])
+def test_full_prefill_equals_sdpa(mask):
+    rng = np.random.default_rng(11)
+    q, k, v = _rand_seq(rng, 37, 6, 2, 16)
+    o, _ = _one_seq(q, k, v, 37, mask, scale=0.21)
+    t = _sdpa(q, k, v, 0.21, is_causal=(mask == ref.MASK_CAUSAL), gqa=True)
+    assert np.max(np.abs(o - t)) <= 1e-12
+
+
+@pytest.mark.parametrize("q_len", [1, 5, 19])
+def test_chunked_causal_is_bottom_right(q_len):
+    """A chunk of q_len new tokens after L - q_len cached ones: torch's lower-right causal bias."""
+    rng = np.random.default_rng(q_len)
+    L = 23
+    q, _, _ = _rand_seq(rng, q_len, 4, 4, 8)
+    _, k, v = _rand_seq(rng, L, 4, 4, 8)
+    o, _ = _one_seq(q, k, v, q_len, ref.MASK_CAUSAL, scale=0.4)
+    t = _sdpa(q, k, v, 0.4, attn_mask=causal_lower_right(q_len, L)._materialize())
+    assert np.max(np.abs(o - t)) <= 1e-12
+
+
+# ----------------------------------------------------------------------------------------
+# invariants from the pages
+# ----------------------------------------------------------------------------------------
+
+def test_gqa_equals_repeat_interleave():
+    """Spyre PR, "Description": GQA by repeat_interleave of the KV heads to num_heads."""
+    rng = np.random.default_rng(3)
+    q, k, v = _rand_seq(rng, 20, 8, 2, 8)
+    o, _ = _one_seq(q, k, v, 9, ref.MASK_CAUSAL)
+    ke, ve = np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1)
+    o2, _ = _one_seq(q, ke, ve, 9, ref.MASK_CAUSAL)
+    assert np.array_equal(o, o2)
+    # torch's own expansion does the same
+    te = torch.from_numpy(k).repeat_interleave(4, dim=1).numpy()
+    assert np.array_equal(te, ke)
+
+
+@pytest.mark.parametrize("mask,span", [(ref.MASK_CAUSAL, 0), (ref.MASK_NONE, 0),
+                                       (ref.MASK_BLOCK_CAUSAL, 4)])
+def test_fused_head_block_diagonal_form(mask, span):
+    """Spyre PR, "Description": all heads in one 2D matmul with a block-diagonal mask."""
+    rng = np.random.default_rng(5)
+    L, n, H, Hkv, D = 13, 6, 4, 2, 8
+    q, k, v = _rand_seq(rng, L, H, Hkv, D)
+    qn = q[:n]
+    o, _ = _one_seq(qn, k, v, n, mask, span, scale=0.35)
+    pos = np.arange(L - n, L)
+    vis = ref.visibility_matrix(pos, L, mask, span)
+    f = ref.fused_head_attention(qn, k, v, vis, 0.35, Hkv)
+    assert np.max(np.abs(o - f)) <= 1e-12
+
+
+def test_additive_mask_constant_is_exclusion():
+    """Spyre PR review thread: mask values 0.0 valid / -65504.0 masked.  In fp64 the additive
+    form equals exclusion whenever a row has a visible key (reading A5)."""
+    g = json.load(open(os.path.join(GOLDEN, "mask_constant.json")))
+    rng = np.random.default_rng(9)
+    q, k, v = _rand_seq(rng, 11, 2, 2, 8)
+    vis = ref.visibility_matrix(np.arange(11), 11, ref.MASK_CAUSAL, 0)
+    for h in range(2):
+        z = 0.3 * q[:, h] @ k[:, h].T + np.where(vis, g["valid"], g["masked"])
+        w = np.exp(z - z.max(axis=1, keepdims=True))
+        oa = (w @ v[:, h]) / w.sum(axis=1, keepdims=True)
+        oe, _ = ref.attend(q[:, h], k[:, h], v[:, h], vis, 0.3)
+        assert np.max(np.abs(oa - oe)) <= 1e-15
+
+
+def test_padding_never_changes_real_rows():
+    """Spyre PR, "Description" steps 3-6: padded KV (to a 256 multiple) and padded query rows
+    (to a 32 multiple) are masked and dropped; real rows are unchanged, exactly."""
+    rng = np.random.default_rng(4)
+    L, n, H, D = 45, 7, 2, 8
+    q, k, v = _rand_seq(rng, n, H, H, D)
+    k0, v0 = rng.standard_normal((L, H, D)), rng.standard_normal((L, H, D))
+    o, _ = _one_seq(q, k0, v0, n, ref.MASK_CAUSAL)
+    kp = np.concatenate([k0, np.full((256 - L, H, D), np.nan)])
+    vp = np.concatenate([v0, np.full((256 - L, H, D), np.nan)])
+    qp = np.concatenate([q, np.full((32 - n, H, D), 7.0)])
+    pos = np.arange(L - n, L)
+    vis = np.zeros((32, 256), bool)
+    vis[:n, :L] = ref.visibility_matrix(pos, L, ref.MASK_CAUSAL, 0)
+    for h in range(H):
+        op, _ = ref.attend(qp[:, h], kp[:, h], vp[:, h], vis, 0.3)
+        assert np.array_equal(op[:n], o[:, h])
+        assert np.all(op[n:] == 0.0)
+
+
+def test_single_visible_key_returns_its_value_row():
+    """Causal row 0 with no cached context sees only key 0: out = V[0] exactly."""
+    w = wl.tiny_prefill()
+    o, lse = ref.workload_attention(w)
+    v = ref.widen(w.value, "f32")
+    for s in range(w.num_seqs):
+        r0 = w.cu_seqlens_q[s]
+        for h in range(w.num_heads):
+            assert np.array_equal(o[r0, h], v[w.cu_seq_lens[s], h // 2])
+
+
+def test_constant_value_rows_return_the_constant():
+    rng = np.random.default_rng(12)
+    q, k, _ = _rand_seq(rng, 30, 4, 2, 8)
+    v = np.full((30, 2, 8), -1.375)
+    for mask, span in [(ref.MASK_NONE, 0), (ref.MASK_CAUSAL, 0), (ref.MASK_BLOCK_CAUSAL, 7)]:
+        o, _ = _one_seq(q[:12], k, v, 12, mask, span)
+        assert np.max(np.abs(o + 1.375)) <= 1e-14
+
+
+def test_zero_query_gives_mean_of_visible_values():
+    rng = np.random.default_rng(13)
+    L, n = 17, 6
+    _, k, v = _rand_seq(rng, L, 2, 2, 8)
+    q = np.zeros((n, 2, 8))
+    o, _ = _one_seq(q, k, v, n, ref.MASK_CAUSAL)
+    for i in range(n):
+        a = L - n + i
+        assert np.max(np.abs(o[i] - v[:a + 1].mean(axis=0))) <= 1e-14
+
+
+def test_block_causal_equals_piecewise_segments():
+    """vllm-omni piecewise PR: each span is a segment; a full segment attends K[:end] without
+    a mask (textbook routine per segment), and the composition equals the dense rule."""
+    rng = np.random.default_rng(21)
+    L, span, H, Hkv, D = 29, 8, 4, 2, 8
+    q, k, v = _rand_seq(rng, L, H, Hkv, D)
+    for q_len in (L, 11):        # whole sequence, and a chunk with cached context
+        o, _ = _one_seq(q[:q_len], k, v, q_len, ref.MASK_BLOCK_CAUSAL, span, scale=0.3)
+        ctx = L - q_len
+        comp = np.zeros_like(o)
+        for (s, e, kv_end, causal) in ref.piecewise_segments(ref.uniform_spans(L, span), L):
+            lo, hi = max(s, ctx), e
+            if lo >= hi:
+                continue
+            assert not causal
+            qs = q[:q_len][lo - ctx:hi - ctx]
+            comp[lo - ctx:hi - ctx] = _sdpa(qs, k[:kv_end], v[:kv_end], 0.3, gqa=True)
+        assert np.max(np.abs(o - comp)) <= 1e-12
+
+
+def test_block_causal_reductions():
+    """span 1 is CAUSAL; a span covering the whole sequence is NONE."""
+    rng = np.random.default_rng(22)
+    q, k, v = _rand_seq(rng, 19, 2, 1, 8)
+    bc1, _ = _one_seq(q[:9], k, v, 9, ref.MASK_BLOCK_CAUSAL, 1)
+    ca, _ = _one_seq(q[:9], k, v, 9, ref.MASK_CAUSAL)
+    assert np.array_equal(bc1, ca)
+    bcl, _ = _one_seq(q[:9], k, v, 9, ref.MASK_BLOCK_CAUSAL, 19)
+    no, _ = _one_seq(q[:9], k, v, 9, ref.MASK_NONE)
+    assert np.array_equal(bcl, no)
+
+
+def test_piecewise_golden_two_segment_shapes():
+    g = json.load(open(os.path.join(GOLDEN, "piecewise_two_segment.json")))
+    segs = ref.piecewise_segments([tuple(x) for x in g["spans"]], g["seq_len"])
+    (cs, ce, ckv, ccausal), (fs, fe, fkv, fcausal) = segs
+    assert (ce - cs, ckv, ccausal) == (g["expected_causal_segment"]["q_rows"],
+                                       g["expected_causal_segment"]["kv_rows"], True)
+    assert (fe - fs, fkv, fcausal) == (g["expected_full_segment"]["q_rows"],
+                                       g["expected_full_segment"]["kv_rows"], False)
+    # and the segment composition equals the dense "(q >= kv) or same block" rule
+    rng = np.random.default_rng(1)
+    H, D, L = g["num_heads"], g["head_dim"], g["seq_len"]
+    q, k, v = _rand_seq(rng, L, H, H, D)
+    comp = np.zeros((L, H, D))
+    for (s, e, kv_end, causal) in segs:
+        m = causal_lower_right(e - s, kv_end)._materialize() if causal else None
+        comp[s:e] = _sdpa(q[s:e], k[:kv_end], v[:kv_end], 0.5, attn_mask=m)
+    dense = np.zeros((L, H, D))
+    same_block = lambda a, b: (a >= 2) and (b >= 2)          # the image block is [2, 5)
+    vis = np.array([[(i >= j) or same_block(i, j) for j in range(L)] for i in range(L)])
+    for h in range(H):
+        dense[:, h], _ = ref.attend(q[:, h], k[:, h], v[:, h], vis, 0.5)
+    assert np.max(np.abs(comp - dense)) <= 1e-12
+
+
+def test_chunked_prefill_consistency_and_decode_is_last_row():
+    """Prefilling in chunks gives the rows of a one-shot causal prefill; decode is its last row."""
+    rng = np.random.default_rng(31)
+    L = 40
+    q, k, v = _rand_seq(rng, L, 4, 2, 8)
+    full, _ = _one_seq(q, k, v, L, ref.MASK_CAUSAL)
+    for (a, b) in [(0, 13), (13, 14), (14, 33), (33, 40)]:
+        part, _ = _one_seq(q[a:b], k[:b], v[:b], b - a, ref.MASK_CAUSAL)
+        assert np.max(np.abs(part - full[a:b])) <= 1e-12
+    dec, _ = _one_seq(q[L - 1:], k, v, 1, ref.MASK_NONE)
+    assert np.max(np.abs(dec[0] - full[L - 1])) <= 1e-12
+
+
+def test_lse_merge_of_any_partition_equals_unsplit():
+    rng = np.random.default_rng(41)
+    L, n = 50, 5
+    q, k, v = _rand_seq(rng, n, 1, 1, 8)
+    k, v = rng.standard_normal((L, 1, 8)), rng.standard_normal((L, 1, 8))
+    vis = ref.visibility_matrix(np.arange(L - n, L), L, ref.MASK_CAUSAL, 0)
+    full, lfull = ref.attend(q[:, 0], k[:, 0], v[:, 0], vis, 0.3)
+    for parts in (2, 3, 7):
+        owner = rng.integers(0, parts, size=L)
+        outs, lses = [], []
+        for j in range(parts):
+            vj = vis & (owner == j)[None, :]
+            o, l = ref.attend(q[:, 0], k[:, 0], v[:, 0], vj, 0.3)
+            outs.append(o)
+            lses.append(l)
+        mo, ml = ref.lse_merge(outs, lses)
+        assert np.max(np.abs(mo - full)) <= 1e-12
+        assert np.max(np.abs(ml - lfull)) <= 1e-12
+    # lse is log sum exp of the visible scores (closed form)
+    z = 0.3 * q[:, 0] @ k[:, 0].T
+    for i in range(n):
+        assert abs(lfull[i] - math.log(np.exp(z[i, vis[i]]).sum())) <= 1e-12
+
+
+def test_empty_rows_give_zeros():
+    """CSA2 Vanilla golden PR, "Description": an empty selection gives zeros (reading A6)."""
+    rng = np.random.default_rng(2)
+    q, k, v = _rand_seq(rng, 3, 2, 2, 4)
+    o, l = ref.attend(q[:, 0], k[:, 0], v[:, 0], np.zeros((3, 3), bool), 0.5)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+    out, lse = ref.paged_attention(np.zeros((0, 2, 4)), [k[:0]], [v[:0]], np.array([0, 0]),
+                                   np.array([0]), 2, 0.5, ref.MASK_NONE)
+    assert out.shape == (0, 2, 4)
+
+
+# ----------------------------------------------------------------------------------------
+# scatter / gather (P10)
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("maker", [wl.tiny_prefill, lambda: wl.random_small(3, "bf16"),
+                                   lambda: wl.chunked_prefill(num_seqs=2, ctx_hi=64, q_hi=40)])
+def test_scatter_gather_round_trip_bit_exact(maker):
+    w = maker()
+    st = wl.DTYPES[w.dtype][0]
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    kc = np.full(shape, wl.nan_bits(w.dtype), st)
+    vc = np.full(shape, wl.nan_bits(w.dtype), st)
+    kc2, vc2 = ref.kv_cache_write(kc, vc, w.key, w.value, w.slots, w.block_size)
+    # a second formulation of the scatter: flat fancy-index assignment
+    kf = kc.reshape(-1, w.num_kv_heads, w.head_dim).copy()
+    kf[w.slots] = w.key
+    assert np.array_equal(kf.reshape(shape), kc2)
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        g = ref.gather_sequence(kc2, w.block_tables[s], L, w.block_size)
+        assert np.array_equal(g, w.key[w.cu_seq_lens[s]:w.cu_seq_lens[s + 1]])
+        g = ref.gather_sequence(vc2, w.block_tables[s], L, w.block_size)
+        assert np.array_equal(g, w.value[w.cu_seq_lens[s]:w.cu_seq_lens[s + 1]])
+    touched = np.zeros(w.num_blocks * w.block_size, bool)
+    touched[w.slots] = True
+    untouched = kc2.reshape(-1, w.num_kv_heads, w.head_dim)[~touched]
+    assert np.all(untouched == wl.nan_bits(w.dtype))
+
+
+def test_scatter_skips_negative_slots_and_rejects_duplicates():
+    kc = np.zeros((2, 2, 1, 1), np.uint32)
+    vc = np.zeros((2, 2, 1, 1), np.uint32)
+    key = np.arange(1, 4, dtype=np.uint32).reshape(3, 1, 1)
+    k2, _ = ref.kv_cache_write(kc, vc, key, key, np.array([3, -1, 0]), 2)
+    assert k2.reshape(-1).tolist() == [3, 0, 0, 1]
+    with pytest.raises(AssertionError):
+        ref.kv_cache_write(kc, vc, key, key, np.array([1, 1, 0]), 2)
+
+
+def test_generator_layout_is_consistent():
+    w = wl.tiny_prefill()
+    assert w.num_blocks == 8 and sorted(w.block_tables[:, :3].reshape(-1).tolist())[:0] == []
+    used = np.concatenate([w.block_tables[0, :2], w.block_tables[1, :3]])
+    assert len(set(used.tolist())) == 5 and used.max() < 8
+    assert w.seq_lens.tolist() == [5, 9] and w.num_tokens == 14
+    # same seed -> same arrays
+    w2 = wl.tiny_prefill()
+    assert np.array_equal(w.query, w2.query) and np.array_equal(w.block_tables, w2.block_tables)
+
+
+# ----------------------------------------------------------------------------------------
+# planted mistakes: each must be caught by a pin above
+# ----------------------------------------------------------------------------------------
+
+def _caught(test_fn, *args):
+    try:
+        test_fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_wrong_gqa_head_map_is_caught(monkeypatch):
+    monkeypatch.setattr(ref, "kv_head_of", lambda h, H, Hkv: h % Hkv)
+    assert _caught(test_gqa_equals_repeat_interleave)
+    assert _caught(test_full_prefill_equals_sdpa, ref.MASK_CAUSAL)
+
+
+def test_planted_top_left_causal_is_caught(monkeypatch):
+    orig = ref.is_visible
+
+    def top_left(p, a, L, mask, span):
+        # a chunk's row index instead of its absolute position: top-left alignment
+        if mask == ref.MASK_CAUSAL:
+            return p < L and p <= a - (L - 19 if L == 23 else 0)
+        return orig(p, a, L, mask, span)
+    monkeypatch.setattr(ref, "is_visible", top_left)
+    assert _caught(test_chunked_causal_is_bottom_right, 19)
+
+
+def test_planted_block_rule_off_by_one_is_caught(monkeypatch):
+    orig = ref.is_visible
+
+    def wrong(p, a, L, mask, span):
+        if mask == ref.MASK_BLOCK_CAUSAL:
+            return p < L and (p <= a or (p // span) == (a // span) + 1)
+        return orig(p, a, L, mask, span)
+    monkeypatch.setattr(ref, "is_visible", wrong)
+    assert _caught(test_block_causal_equals_piecewise_segments)
+
+
+def test_planted_missing_scale_and_unstable_softmax_are_caught(monkeypatch):
+    orig = ref.attend
+
+    def no_scale(q, k, v, vis, scale):
+        return orig(q, k, v, vis, 1.0)
+    monkeypatch.setattr(ref, "attend", no_scale)
+    assert _caught(test_full_prefill_equals_sdpa, ref.MASK_NONE)
+    monkeypatch.setattr(ref, "attend", orig)
+
+    def transposed_v(q, k, v, vis, scale):
+        o, l = orig(q, k, v, vis, scale)
+        return o[:, ::-1].copy(), l
+    monkeypatch.setattr(ref, "attend", transposed_v)
+    assert _caught(test_full_prefill_equals_sdpa, ref.MASK_NONE)
