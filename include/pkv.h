@@ -1,0 +1,195 @@
+/*
+ * pkv.h -- C ABI of libpkv: scaled dot-product attention over a paged KV cache
+ * (variable-length batches) for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument named for a tensor is a DEVICE pointer owned by the
+ *   caller.  The library allocates no device memory and keeps no state apart
+ *   from a thread-local error string (pkv_last_error).
+ * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *   Every call only enqueues work on that stream: it never synchronises and
+ *   never copies device memory to the host, so device-resident lengths and
+ *   tables are trusted, and host "hints" (max_seq_len, max_q_len) size grids.
+ *   (Spyre paged-attention PR, "Description"/review: no .item() host syncs in
+ *   the forward; ROCm TransformerEngine small-seq PR: host max_seqlen sizes
+ *   work on shape queries.)
+ * - Everything that can be checked on the host is checked BEFORE anything is
+ *   enqueued; a rejected call returns a negative pkv_status, writes nothing and
+ *   leaves a message in pkv_last_error() (CSA2 Vanilla golden PR,
+ *   "Description": unsupported modes are rejected before anything is written;
+ *   review thread: a retry must not fail on stale state).
+ * - Element types: dtype applies to query, key, value, caches and output alike.
+ * - Cache layout: key_cache and value_cache are each [num_blocks, block_size,
+ *   num_kv_heads, head_dim] with the first dimension strided by
+ *   cache_block_stride ELEMENTS; inside a block the layout is dense.  A combined
+ *   (num_blocks, 2, block_size, num_kv_heads, head_dim) tensor (the final
+ *   layout of the Spyre paged-attention PR) is passed as two views with
+ *   cache_block_stride = 2*block_size*num_kv_heads*head_dim.
+ * - Slot encoding: slot = block_id * block_size + offset_in_block (int64);
+ *   a negative slot marks a padding token that is skipped.
+ * - GQA: query head h reads kv head h / (num_heads / num_kv_heads), the mapping
+ *   repeat_interleave produces (Spyre PR, "Description").
+ * - Masks: query row i of a sequence with L tokens and q new tokens sits at
+ *   absolute position a = L - q + i and sees key p < L when
+ *     PKV_MASK_NONE         always (padding / length only)
+ *     PKV_MASK_CAUSAL       p <= a  (bottom-right aligned, vllm-omni piecewise
+ *                           block-causal PR: rightDownCausal contract)
+ *     PKV_MASK_BLOCK_CAUSAL p <= a or p / span_len == a / span_len (that PR's
+ *                           dense "(q >= kv) or same block" reference, blocks
+ *                           tiling absolute positions from 0)
+ *   A row with no visible key produces zeros.
+ * - Precision: bf16/fp16 inputs, fp32 scores, softmax statistics and
+ *   accumulators; probabilities are rounded to the input type for the
+ *   probability-times-V products; output rounded to nearest even.
+ *
+ * Device-content preconditions (not checked, undefined behaviour if violated):
+ *   slots in [0, num_blocks*block_size) or negative, unique within one call;
+ *   block_tables entries in [0, num_blocks) for the blocks a sequence uses;
+ *   seq_lens[s] <= max_blocks_per_seq*block_size and <= max_seq_len;
+ *   cu_seqlens_q non-decreasing with q_s = cu[s+1]-cu[s] <= min(seq_lens[s], max_q_len);
+ *   cu_seqlens_q[num_seqs] == num_tokens.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes          */
+  PKV_ERR_UNSUPPORTED = -2, /* valid but not compiled: head_dim, dtype              */
+  PKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the size query     */
+  PKV_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch             */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+typedef enum { PKV_MASK_NONE = 0, PKV_MASK_CAUSAL = 1, PKV_MASK_BLOCK_CAUSAL = 2 } pkv_mask_mode;
+
+/* Supported head_dim values (compiled kernel set). */
+#define PKV_HEAD_DIM_SUPPORTED(d) ((d) == 16 || (d) == 64 || (d) == 128)
+
+/*
+ * pkv_kv_cache_write -- step 1 of the Spyre paged-attention PR ("Description":
+ * write new key/value tokens into the paged cache by vectorised scatter through
+ * slot_mapping).
+ *
+ * key, value      [num_tokens, num_kv_heads, head_dim]; token t starts at
+ *                 t*kv_token_stride elements (heads and dims dense inside a token).
+ * slot_mapping    int64 [num_tokens]; slot < 0 skips the token.
+ * key_cache,
+ * value_cache     written at block slot/block_size, offset slot%block_size.
+ * The copy is a raw bit copy (bit-exact).  num_tokens == 0 is a successful no-op.
+ * Errors: INVALID_ARG for null pointers, block_size not a power of two in
+ * [1, 256], non-positive sizes, kv_token_stride < num_kv_heads*head_dim, or
+ * cache_block_stride < block_size*num_kv_heads*head_dim; UNSUPPORTED for dtype.
+ */
+int pkv_kv_cache_write(const void* key, const void* value, int64_t kv_token_stride,
+                       const int64_t* slot_mapping, int32_t num_tokens, void* key_cache,
+                       void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                       pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_kv_cache_gather -- step 2 of the Spyre PR ("gather the relevant KV entries
+ * from scattered blocks into compact tensors").  Test and debugging aid: the
+ * attention kernels fuse this gather into their loads and never materialise it.
+ *
+ * cu_seq_lens     int32 [num_seqs+1], prefix sums of the sequence lengths.
+ * key_out,
+ * value_out       [total_tokens, num_kv_heads, head_dim] dense; sequence s fills
+ *                 rows cu_seq_lens[s] .. cu_seq_lens[s+1]-1 with its logical
+ *                 positions 0..L_s-1.  total_tokens == cu_seq_lens[num_seqs].
+ * Errors as pkv_kv_cache_write, plus INVALID_ARG for max_seq_len < 0.
+ */
+int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_lens,
+                        const void* key_cache, const void* value_cache,
+                        int64_t cache_block_stride, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_tokens,
+                        int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t max_seq_len, pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_decode_workspace_size -- bytes of device workspace pkv_paged_attention_decode
+ * needs for these sizes (0 when every sequence fits one split).  The caller
+ * allocates it ahead of time (ROCm TransformerEngine small-seq PR: workspace
+ * and aux buffers are pre-allocated from host max sequence lengths).
+ * Returns 0 for invalid sizes as well; the decode call then validates.
+ */
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len);
+
+/*
+ * pkv_paged_attention_decode -- single-token decode: one query token per
+ * sequence attending all L_s cached tokens (the new token already written
+ * by pkv_kv_cache_write).  Flash decoding: the keys of a sequence are cut into
+ * splits, each split reduces to (partial output, max, sum) in the workspace,
+ * and a log-sum-exp merge combines them.  The small-seq varlen cross-attention
+ * case of the ROCm TransformerEngine PR (s_q = 1, s_kv <= 16, one sequence per
+ * query token) is this call with num_seqs = number of query tokens.
+ *
+ * out, query      [num_seqs, num_heads, head_dim] dense.
+ * block_tables    int32 [num_seqs, max_blocks_per_seq] (row stride max_blocks_per_seq).
+ * seq_lens        int32 [num_seqs]; 0 yields a zero output row.
+ * max_seq_len     host hint >= every seq_lens[s]; sizes the split grid.
+ * workspace       device buffer of at least pkv_decode_workspace_size(...) bytes
+ *                 (may be NULL when that size is 0).  Contents need no
+ *                 initialisation; calls sharing one workspace must be ordered.
+ * Errors: INVALID_ARG (null pointers, num_heads % num_kv_heads != 0, sizes),
+ * UNSUPPORTED (head_dim, dtype), WORKSPACE (too small).
+ */
+int pkv_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, int64_t cache_block_stride,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                               int32_t block_size, float scale, int32_t max_seq_len,
+                               void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                               void* stream);
+
+/*
+ * pkv_paged_attention_prefill -- prefill and chunked prefill over a flat (THD)
+ * query batch: sequence s owns query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1,
+ * which are its newest q_s tokens, so row i sits at position L_s - q_s + i
+ * (Spyre PR "Description" steps 3-6 without padding: rows are addressed in
+ * place and written back in query order).
+ *
+ * out, query      [num_tokens, num_heads, head_dim] dense.
+ * cu_seqlens_q    int32 [num_seqs+1].
+ * seq_lens        int32 [num_seqs], total keys per sequence including the new ones.
+ * mask, span_len  see the mask rules above; span_len > 0 required for BLOCK_CAUSAL.
+ * max_q_len,
+ * max_seq_len     host hints >= every q_s and L_s; they size the grid.
+ * bf16/fp16 with head_dim 64 or 128 run on MFMA; fp32 and head_dim 16 run on a
+ * vector-ALU kernel with fp32 probabilities.
+ * Errors: INVALID_ARG (null pointers, num_heads % num_kv_heads, sizes, mask,
+ * span_len), UNSUPPORTED (head_dim, dtype).
+ */
+int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_seqlens_q,
+                                const int32_t* seq_lens, const void* key_cache,
+                                const void* value_cache, int64_t cache_block_stride,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                int32_t block_size, float scale, pkv_mask_mode mask,
+                                int32_t span_len, int32_t max_q_len, int32_t max_seq_len,
+                                pkv_dtype dtype, void* stream);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until the
+ * next pkv_* call on the same thread. */
+const char* pkv_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,251 @@
+// C ABI of libpkv: host-side validation, then kernel launches on the caller's stream.
+// Every check runs before anything is enqueued, and a rejected call touches no memory
+// (CSA2 Vanilla golden PR, "Description": rejected before anything is written).
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/pkv.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+bool is_pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+int check_dtype(int dtype) {
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "dtype %d is not one of PKV_F32, PKV_F16, PKV_BF16", dtype);
+  return PKV_OK;
+}
+
+// Geometry shared by every call that reads or writes the cache.
+int check_cache(const void* kc, const void* vc, int64_t block_stride, int32_t num_blocks,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim) {
+  if (!kc || !vc) return fail(PKV_ERR_INVALID_ARG, "key_cache/value_cache must not be NULL");
+  if (num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be > 0 (got %d)", num_blocks);
+  if (!is_pow2_in(block_size, 1, 256))
+    return fail(PKV_ERR_INVALID_ARG, "block_size must be a power of two in [1, 256] (got %d)",
+                block_size);
+  if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be > 0 (got %d)", num_kv_heads);
+  if (!PKV_HEAD_DIM_SUPPORTED(head_dim))
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d is not compiled (16, 64, 128)", head_dim);
+  const int64_t min_stride = (int64_t)block_size * num_kv_heads * head_dim;
+  if (block_stride < min_stride)
+    return fail(PKV_ERR_INVALID_ARG,
+                "cache_block_stride %lld is smaller than block_size*num_kv_heads*head_dim = %lld",
+                (long long)block_stride, (long long)min_stride);
+  return PKV_OK;
+}
+
+int check_heads(int32_t num_heads, int32_t num_kv_heads) {
+  if (num_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_heads must be > 0 (got %d)", num_heads);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_heads (%d) must be a multiple of num_kv_heads (%d)",
+                num_heads, num_kv_heads);
+  return PKV_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(PKV_ERR_LAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return (1 << 16) | 0; }
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv_kv_cache_write(const void* key, const void* value, int64_t kv_token_stride,
+                       const int64_t* slot_mapping, int32_t num_tokens, void* key_cache,
+                       void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                       pkv_dtype dtype, void* stream) {
+  clear_error();
+  int rc;
+  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
+                        num_kv_heads, head_dim)) != PKV_OK)
+    return rc;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "key, value and slot_mapping must not be NULL");
+  if (kv_token_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PKV_ERR_INVALID_ARG, "kv_token_stride %lld < num_kv_heads*head_dim = %lld",
+                (long long)kv_token_stride, (long long)num_kv_heads * head_dim);
+  pkv::ScatterArgs a{key, value, kv_token_stride, slot_mapping, num_tokens, key_cache,
+                     value_cache, cache_block_stride, num_blocks, block_size, num_kv_heads,
+                     head_dim, (int)dtype};
+  return launched(pkv::launch_kv_scatter(a, (hipStream_t)stream), "pkv_kv_cache_write");
+}
+
+int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_lens,
+                        const void* key_cache, const void* value_cache,
+                        int64_t cache_block_stride, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_tokens,
+                        int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t max_seq_len, pkv_dtype dtype, void* stream) {
+  clear_error();
+  int rc;
+  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
+  if (num_seqs < 0 || total_tokens < 0 || max_seq_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs, total_tokens and max_seq_len must be >= 0");
+  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
+                        num_kv_heads, head_dim)) != PKV_OK)
+    return rc;
+  if (num_seqs == 0 || total_tokens == 0) return PKV_OK;
+  if (!key_out || !value_out || !cu_seq_lens || !block_tables)
+    return fail(PKV_ERR_INVALID_ARG, "key_out, value_out, cu_seq_lens and block_tables must not be NULL");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
+                (long long)max_blocks_per_seq * block_size, max_seq_len);
+  pkv::GatherArgs a{key_out, value_out, cu_seq_lens, key_cache, value_cache, cache_block_stride,
+                    block_tables, max_blocks_per_seq, num_seqs, total_tokens, num_blocks,
+                    block_size, num_kv_heads, head_dim, max_seq_len, (int)dtype};
+  return launched(pkv::launch_kv_gather(a, (hipStream_t)stream), "pkv_kv_cache_gather");
+}
+
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      !PKV_HEAD_DIM_SUPPORTED(head_dim) || max_seq_len < 0)
+    return 0;
+  return pkv::decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len).workspace_bytes;
+}
+
+int pkv_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, int64_t cache_block_stride,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                               int32_t block_size, float scale, int32_t max_seq_len,
+                               void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                               void* stream) {
+  clear_error();
+  int rc;
+  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
+  if (num_seqs < 0 || max_seq_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs and max_seq_len must be >= 0");
+  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
+                        num_kv_heads, head_dim)) != PKV_OK)
+    return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads)) != PKV_OK) return rc;
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID_ARG, "scale is NaN");
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !block_tables || !seq_lens)
+    return fail(PKV_ERR_INVALID_ARG, "out, query, block_tables and seq_lens must not be NULL");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
+                (long long)max_blocks_per_seq * block_size, max_seq_len);
+  const pkv::DecodePlan plan =
+      pkv::decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return fail(PKV_ERR_WORKSPACE, "decode workspace of %zu bytes required (got %zu at %p)",
+                plan.workspace_bytes, workspace_bytes, workspace);
+  pkv::AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.seq_lens = seq_lens;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_stride = cache_block_stride;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.scale = scale;
+  a.mask = PKV_MASK_NONE;
+  a.max_seq_len = max_seq_len;
+  a.max_q_len = 1;
+  a.dtype = (int)dtype;
+  a.workspace = workspace;
+  return launched(pkv::launch_decode(a, plan, (hipStream_t)stream), "pkv_paged_attention_decode");
+}
+
+int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_seqlens_q,
+                                const int32_t* seq_lens, const void* key_cache,
+                                const void* value_cache, int64_t cache_block_stride,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                int32_t block_size, float scale, pkv_mask_mode mask,
+                                int32_t span_len, int32_t max_q_len, int32_t max_seq_len,
+                                pkv_dtype dtype, void* stream) {
+  clear_error();
+  int rc;
+  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
+  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || max_seq_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs, num_tokens, max_q_len, max_seq_len must be >= 0");
+  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
+                        num_kv_heads, head_dim)) != PKV_OK)
+    return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads)) != PKV_OK) return rc;
+  if (mask != PKV_MASK_NONE && mask != PKV_MASK_CAUSAL && mask != PKV_MASK_BLOCK_CAUSAL)
+    return fail(PKV_ERR_INVALID_ARG, "unknown mask mode %d", (int)mask);
+  if (mask == PKV_MASK_BLOCK_CAUSAL && span_len <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "BLOCK_CAUSAL needs span_len > 0 (got %d)", span_len);
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID_ARG, "scale is NaN");
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !query || !cu_seqlens_q || !seq_lens || !block_tables)
+    return fail(PKV_ERR_INVALID_ARG,
+                "out, query, cu_seqlens_q, seq_lens and block_tables must not be NULL");
+  if (max_q_len > max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_q_len (%d) > max_seq_len (%d)", max_q_len, max_seq_len);
+  if (num_tokens > 0 && max_q_len == 0)
+    return fail(PKV_ERR_INVALID_ARG, "max_q_len must be > 0 when num_tokens > 0");
+  if ((int64_t)max_q_len * num_seqs < num_tokens)
+    return fail(PKV_ERR_INVALID_ARG, "num_tokens (%d) > num_seqs*max_q_len (%lld)", num_tokens,
+                (long long)max_q_len * num_seqs);
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
+                (long long)max_blocks_per_seq * block_size, max_seq_len);
+  pkv::AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.seq_lens = seq_lens;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_stride = cache_block_stride;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.scale = scale;
+  a.mask = (int)mask;
+  a.span_len = mask == PKV_MASK_BLOCK_CAUSAL ? span_len : 1;
+  a.max_q_len = max_q_len;
+  a.max_seq_len = max_seq_len;
+  a.dtype = (int)dtype;
+  if (pkv::prefill_mfma_supported((int)dtype, head_dim))
+    return launched(pkv::launch_prefill_mfma(a, (hipStream_t)stream), "pkv_paged_attention_prefill");
+  return launched(pkv::launch_prefill_valu(a, (hipStream_t)stream), "pkv_paged_attention_prefill");
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Shared device helpers of libpkv (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// Storage tags: the kernels see raw 16-bit or 32-bit words.
+struct BF16 { using storage = uint16_t; static constexpr int bytes = 2; };
+struct F16  { using storage = uint16_t; static constexpr int bytes = 2; };
+struct F32  { using storage = uint32_t; static constexpr int bytes = 4; };
+
+// ---- scalar conversions ---------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Two fp32 -> packed pair of the storage type, round to nearest even.
+__device__ __forceinline__ uint32_t pack2(BF16, float a, float b) {
+  bf16x2_t v = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pack2(F16, float a, float b) {
+  f16x2_t v = __builtin_convertvector((f32x2_t){a, b}, f16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Widen the two halves of a packed word.
+__device__ __forceinline__ float lo_of(BF16, uint32_t w) { return bf16_lo(w); }
+__device__ __forceinline__ float hi_of(BF16, uint32_t w) { return bf16_hi(w); }
+__device__ __forceinline__ float lo_of(F16, uint32_t w) { return f16_lo(w); }
+__device__ __forceinline__ float hi_of(F16, uint32_t w) { return f16_hi(w); }
+
+// acc + a.x*b.x + a.y*b.y on packed 16-bit pairs (fp32 accumulate): v_dot2_f32_{bf16,f16}.
+__device__ __forceinline__ float dot2(BF16, uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+__device__ __forceinline__ float dot2(F16, uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                acc, false);
+}
+
+// ---- cross-lane helpers ---------------------------------------------------------------
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) {
+  return __shfl_xor(x, m, kWave);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace pkv

@@ -1,0 +1,79 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+// Every argument here has already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum Dtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
+
+struct ScatterArgs {
+  const void* key;
+  const void* value;
+  int64_t token_stride;        // elements
+  const int64_t* slots;
+  int32_t num_tokens;
+  void* key_cache;
+  void* value_cache;
+  int64_t block_stride;        // elements
+  int32_t num_blocks, block_size, num_kv_heads, head_dim;
+  int dtype;
+};
+
+struct GatherArgs {
+  void* key_out;
+  void* value_out;
+  const int32_t* cu_seq_lens;
+  const void* key_cache;
+  const void* value_cache;
+  int64_t block_stride;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq, num_seqs, total_tokens, num_blocks, block_size, num_kv_heads,
+      head_dim, max_seq_len;
+  int dtype;
+};
+
+struct AttnArgs {
+  void* out;
+  const void* query;
+  const int32_t* cu_seqlens_q;   // prefill only
+  const int32_t* seq_lens;
+  const void* key_cache;
+  const void* value_cache;
+  int64_t block_stride;          // elements
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq, num_seqs, num_tokens, num_heads, num_kv_heads, head_dim,
+      num_blocks, block_size;
+  float scale;
+  int mask;
+  int32_t span_len, max_q_len, max_seq_len;
+  int dtype;
+  void* workspace;               // decode only
+};
+
+// Decode split plan: a pure function of the sizes, shared by the workspace query
+// and the launch so that both agree.
+struct DecodePlan {
+  int heads_per_wave;   // query heads of one kv group handled by one wave (power of 2)
+  int groups_per_kv;    // waves needed to cover the g = H / Hkv heads of one kv head
+  int split_len;        // keys per split
+  int num_splits;       // splits of the longest sequence
+  size_t workspace_bytes;
+};
+DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                       int max_seq_len);
+
+hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream);
+hipError_t launch_kv_gather(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, hipStream_t stream);
+// Returns hipErrorNotSupported when no MFMA variant covers the shape.
+hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_prefill_valu(const AttnArgs& a, hipStream_t stream);
+bool prefill_mfma_supported(int dtype, int head_dim);
+
+}  // namespace pkv

@@ -1,0 +1,108 @@
+"""Shared helpers of the GPU tests: upload a generated workload, run the library, compare.
+
+Nothing here computes attention; expected values always come from `oracle/`.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from paged_kv_scaled_amd import binding as B
+from paged_kv_scaled_amd import workloads as wl
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+INT_DT = {"f32": (torch.int32, np.int32), "f16": (torch.int16, np.int16), "bf16": (torch.int16, np.int16)}
+
+# Bars for bf16/fp16 outputs against the fp64 oracle (max-abs, relative L2).
+MAX_ABS, REL_L2 = 2e-2, 1e-2
+# fp32 inputs run on the fp32 vector path: far tighter.
+MAX_ABS_F32, REL_L2_F32 = 1e-5, 1e-6
+
+
+def to_dev(bits: np.ndarray, dtype: str, device="cuda"):
+    tdt, ndt = INT_DT[dtype]
+    return torch.from_numpy(np.ascontiguousarray(bits).view(ndt)).to(device).view(TORCH_DT[dtype])
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    ndt = {torch.float32: np.uint32, torch.float16: np.uint16, torch.bfloat16: np.uint16}[t.dtype]
+    idt = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16}[t.dtype]
+    return t.detach().contiguous().view(idt).cpu().numpy().view(ndt)
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class Dev:
+    """Device copies of a workload plus a NaN-sentinel cache."""
+
+    def __init__(self, w: wl.Workload, fill: str = "nan", combined: bool = False):
+        self.w = w
+        dt = TORCH_DT[w.dtype]
+        shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+        if combined:
+            # the (num_blocks, 2, block_size, Hkv, D) layout passed as two strided views
+            base = torch.empty((w.num_blocks, 2) + shape[1:], dtype=dt, device="cuda")
+            self.kc, self.vc = base[:, 0], base[:, 1]
+        else:
+            self.kc = torch.empty(shape, dtype=dt, device="cuda")
+            self.vc = torch.empty(shape, dtype=dt, device="cuda")
+        if fill == "nan":
+            self.kc.fill_(float("nan"))
+            self.vc.fill_(float("nan"))
+        else:
+            self.kc.zero_()
+            self.vc.zero_()
+        self.query = to_dev(w.query, w.dtype)
+        self.key = to_dev(w.key, w.dtype)
+        self.value = to_dev(w.value, w.dtype)
+        self.slots = torch.from_numpy(w.slots).cuda()
+        self.tables = torch.from_numpy(w.block_tables).cuda()
+        self.seq_lens = torch.from_numpy(w.seq_lens).cuda()
+        self.cu_q = torch.from_numpy(w.cu_seqlens_q).cuda()
+        self.cu_k = torch.from_numpy(w.cu_seq_lens).cuda()
+
+    def write_all(self, split_new: bool = True):
+        """Scatter every logical row into the cache: the cached context first, then the
+        new tokens of this call (two kv_cache_write calls, as a serving step does)."""
+        w = self.w
+        if split_new:
+            for rows in (w.context_rows(), w.new_token_rows()):
+                if rows.size == 0:
+                    continue
+                idx = torch.from_numpy(rows).cuda()
+                B.kv_cache_write(self.key[idx], self.value[idx], self.slots[idx], self.kc, self.vc)
+        else:
+            B.kv_cache_write(self.key, self.value, self.slots, self.kc, self.vc)
+
+    def decode(self, out=None):
+        w = self.w
+        out = out if out is not None else torch.empty_like(self.query)
+        ws_bytes = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                           w.max_seq_len)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        B.paged_attention_decode(out, self.query, self.kc, self.vc, self.tables, self.seq_lens,
+                                 w.scale, w.max_seq_len, ws if ws_bytes else None)
+        return out
+
+    def prefill(self, out=None):
+        w = self.w
+        out = out if out is not None else torch.empty_like(self.query)
+        B.paged_attention_prefill(out, self.query, self.cu_q, self.seq_lens, self.kc, self.vc,
+                                  self.tables, w.scale, w.mask, w.span_len, w.max_q_len,
+                                  w.max_seq_len)
+        return out
+
+
+def compare(got: np.ndarray, want: np.ndarray, dtype: str, what: str = ""):
+    """max-abs and relative-L2 against the oracle, with the bar for the dtype."""
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    diff = got - want
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    nrm = float(np.linalg.norm(want))
+    rel = float(np.linalg.norm(diff) / nrm) if nrm > 0 else float(np.linalg.norm(diff))
+    ma, rl = (MAX_ABS_F32, REL_L2_F32) if dtype == "f32" else (MAX_ABS, REL_L2)
+    assert max_abs <= ma and rel <= rl, f"{what}: max_abs {max_abs:.3e} (bar {ma}), rel_l2 {rel:.3e} (bar {rl})"
+    return max_abs, rel

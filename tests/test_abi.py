@@ -1,0 +1,146 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/pkv.h declares, and
+rejects invalid arguments on the host before anything is enqueued (no GPU needed: every
+call here fails validation, so no HIP runtime call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_scaled_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("pkv_kv_cache_write", "pkv_paged_attention_decode", "pkv_paged_attention_prefill",
+                 "pkv_kv_cache_gather", "pkv_decode_workspace_size", "pkv_last_error"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert set(declared_symbols()) == set(B.SIGNATURES)
+
+
+def test_version(lib):
+    assert lib.pkv_version() >> 16 == 1
+
+
+def _write(lib, **kw):
+    a = dict(key=FAKE, value=FAKE, stride=256, slots=FAKE, T=4, kc=FAKE, vc=FAKE, bstride=16 * 256,
+             nb=8, bs=16, hkv=2, d=128, dt=B.PKV_BF16)
+    a.update(kw)
+    return lib.pkv_kv_cache_write(a["key"], a["value"], a["stride"], a["slots"], a["T"], a["kc"],
+                                  a["vc"], a["bstride"], a["nb"], a["bs"], a["hkv"], a["d"],
+                                  a["dt"], NULL)
+
+
+def test_write_rejections(lib):
+    assert _write(lib, key=NULL) == B.PKV_ERR_INVALID_ARG
+    assert "NULL" in B.last_error()
+    assert _write(lib, kc=NULL) == B.PKV_ERR_INVALID_ARG
+    assert _write(lib, bs=12) == B.PKV_ERR_INVALID_ARG
+    assert "power of two" in B.last_error()
+    assert _write(lib, bs=512, bstride=512 * 256) == B.PKV_ERR_INVALID_ARG
+    assert _write(lib, d=96, stride=192, bstride=16 * 192) == B.PKV_ERR_UNSUPPORTED
+    assert _write(lib, dt=7) == B.PKV_ERR_UNSUPPORTED
+    assert _write(lib, stride=100) == B.PKV_ERR_INVALID_ARG
+    assert _write(lib, bstride=100) == B.PKV_ERR_INVALID_ARG
+    assert _write(lib, T=-1) == B.PKV_ERR_INVALID_ARG
+    assert _write(lib, nb=0) == B.PKV_ERR_INVALID_ARG
+    # an empty batch is a successful no-op, even with NULL inputs
+    assert _write(lib, T=0, key=NULL, value=NULL, slots=NULL) == B.PKV_OK
+    assert B.last_error() == ""
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bstride=16 * 8 * 128, bt=FAKE, mb=256, sl=FAKE,
+             S=64, H=32, Hkv=8, D=128, nb=9000, bs=16, scale=0.088, maxL=4096, ws=FAKE, wsb=0,
+             dt=B.PKV_BF16)
+    a.update(kw)
+    return lib.pkv_paged_attention_decode(a["out"], a["q"], a["kc"], a["vc"], a["bstride"], a["bt"],
+                                          a["mb"], a["sl"], a["S"], a["H"], a["Hkv"], a["D"],
+                                          a["nb"], a["bs"], a["scale"], a["maxL"], a["ws"],
+                                          a["wsb"], a["dt"], NULL)
+
+
+def test_decode_rejections(lib):
+    need = lib.pkv_decode_workspace_size(64, 32, 8, 128, 4096)
+    assert need > 0
+    assert _decode(lib, wsb=need - 1) == B.PKV_ERR_WORKSPACE
+    assert _decode(lib, ws=NULL, wsb=need) == B.PKV_ERR_WORKSPACE
+    assert "workspace" in B.last_error()
+    assert _decode(lib, H=30) == B.PKV_ERR_INVALID_ARG
+    assert "multiple" in B.last_error()
+    assert _decode(lib, out=NULL, wsb=need) == B.PKV_ERR_INVALID_ARG
+    assert _decode(lib, D=80, bstride=16 * 8 * 80) == B.PKV_ERR_UNSUPPORTED
+    assert _decode(lib, mb=100, wsb=need) == B.PKV_ERR_INVALID_ARG      # 100*16 < 4096
+    assert _decode(lib, scale=float("nan"), wsb=need) == B.PKV_ERR_INVALID_ARG
+    assert _decode(lib, S=0) == B.PKV_OK
+
+
+def test_decode_workspace_size_plan(lib):
+    # one split per sequence -> no workspace
+    assert lib.pkv_decode_workspace_size(30720, 16, 16, 128, 16) == 0
+    # 64 x 32 heads x 16 splits of 256 keys x (128 + 2) floats
+    assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 4096) == 64 * 32 * 16 * 130 * 4
+    assert lib.pkv_decode_workspace_size(64, 30, 8, 128, 4096) == 0    # invalid -> 0
+    assert lib.pkv_decode_workspace_size(1, 8, 8, 128, 131072) > 0
+
+
+def _prefill(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, cu=FAKE, sl=FAKE, kc=FAKE, vc=FAKE, bstride=16 * 8 * 128, bt=FAKE,
+             mb=512, S=4, T=32768, H=64, Hkv=8, D=128, nb=2049, bs=16, scale=0.088,
+             mask=B.PKV_MASK_BLOCK_CAUSAL, span=2048, maxq=8192, maxL=8192, dt=B.PKV_BF16)
+    a.update(kw)
+    return lib.pkv_paged_attention_prefill(a["out"], a["q"], a["cu"], a["sl"], a["kc"], a["vc"],
+                                           a["bstride"], a["bt"], a["mb"], a["S"], a["T"], a["H"],
+                                           a["Hkv"], a["D"], a["nb"], a["bs"], a["scale"],
+                                           a["mask"], a["span"], a["maxq"], a["maxL"], a["dt"],
+                                           NULL)
+
+
+def test_prefill_rejections(lib):
+    assert _prefill(lib, span=0) == B.PKV_ERR_INVALID_ARG
+    assert "span_len" in B.last_error()
+    assert _prefill(lib, mask=5) == B.PKV_ERR_INVALID_ARG
+    assert _prefill(lib, H=60) == B.PKV_ERR_INVALID_ARG
+    assert _prefill(lib, cu=NULL) == B.PKV_ERR_INVALID_ARG
+    assert _prefill(lib, maxq=9000) == B.PKV_ERR_INVALID_ARG            # > max_seq_len
+    assert _prefill(lib, T=40000) == B.PKV_ERR_INVALID_ARG              # > S * max_q_len
+    assert _prefill(lib, mb=100) == B.PKV_ERR_INVALID_ARG
+    assert _prefill(lib, D=32, bstride=16 * 8 * 32) == B.PKV_ERR_UNSUPPORTED
+    assert _prefill(lib, dt=3) == B.PKV_ERR_UNSUPPORTED
+    assert _prefill(lib, T=0) == B.PKV_OK
+
+
+def test_gather_rejections(lib):
+    r = lib.pkv_kv_cache_gather(NULL, FAKE, FAKE, FAKE, FAKE, 16 * 256, FAKE, 4, 2, 10, 8, 16, 2,
+                                128, 40, B.PKV_BF16, NULL)
+    assert r == B.PKV_ERR_INVALID_ARG
+    r = lib.pkv_kv_cache_gather(FAKE, FAKE, FAKE, FAKE, FAKE, 16 * 256, FAKE, 2, 2, 10, 8, 16, 2,
+                                128, 40, B.PKV_BF16, NULL)
+    assert r == B.PKV_ERR_INVALID_ARG                                   # 2*16 < 40
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        B.load(str(tmp_path / "missing.so"))

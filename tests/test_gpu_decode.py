@@ -1,0 +1,131 @@
+"""paged_attention_decode on the GPU against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import reference as ref
+from paged_kv_scaled_amd import binding as B
+from paged_kv_scaled_amd import workloads as wl
+
+from gpu_helpers import Dev, as_f64, compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, combined=False, rows=None):
+    d = Dev(w, combined=combined)
+    d.write_all()
+    out = d.decode()
+    torch.cuda.synchronize()
+    want, _ = ref.workload_attention(w, rows=rows)
+    got = as_f64(out)
+    if rows is not None:
+        got, want = got[rows], want[rows]
+    return compare(got, want, w.dtype, w.name)
+
+
+def test_decode_batch_full_size(gpu):
+    """64 sequences, contexts 256..4096, 32 q / 8 kv heads, D 128, bf16: every output."""
+    _run(wl.decode_batch())
+
+
+def test_smallseq_full_size_sampled(gpu):
+    """30720 sequences with s_kv in {2..16}, MHA 16 heads: 1024 sampled sequences."""
+    w = wl.smallseq_varlen()
+    rows = np.sort(np.random.default_rng(5).choice(w.num_seqs, 1024, replace=False))
+    _run(w, rows=rows)
+
+
+def test_smallseq_small_all_rows(gpu):
+    _run(wl.smallseq_varlen(num_seqs=700))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_decode_dtypes(gpu, dtype):
+    _run(wl.decode_batch(seed=11, num_seqs=5, lo=1, hi=1500, dtype=dtype))
+
+
+def test_decode_combined_cache_layout(gpu):
+    _run(wl.decode_batch(seed=12, num_seqs=4, lo=100, hi=900), combined=True)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_random_shapes(gpu, seed):
+    """Random GQA ratios (incl. 3), head_dim 16/64/128, block sizes 1..4, lengths 1..12."""
+    rng = np.random.default_rng(100 + seed)
+    d = int(rng.choice([16, 64, 128]))
+    dt = str(rng.choice(["bf16", "f16", "f32"]))
+    _run(wl.random_small(seed, dt, head_dim=d, decode=True, max_len=40))
+
+
+def test_decode_long_sequence_many_splits(gpu):
+    """One 40k-token sequence next to short ones: many splits plus the LSE merge."""
+    lens = np.array([40000, 3, 1, 700], np.int32)
+    w = wl.build("long_decode", 21, "bf16", lens, np.ones(4, np.int32), 16, 2, 128, 16,
+                 wl.MASK_NONE, decode=True)
+    _run(w)
+
+
+def test_decode_gqa_wide(gpu):
+    """g = 16 (two 8-head waves per kv head) and g = 6 (a partly filled wave)."""
+    for H, Hkv in [(32, 2), (12, 2)]:
+        lens = np.array([300, 1000, 17], np.int32)
+        w = wl.build("gqa_wide", 22, "bf16", lens, np.ones(3, np.int32), H, Hkv, 64, 16,
+                     wl.MASK_NONE, decode=True)
+        _run(w)
+
+
+def test_decode_empty_and_single_token_sequences(gpu):
+    lens = np.array([0, 1, 0, 2, 513], np.int32)
+    w = wl.build("edge_decode", 23, "bf16", lens, np.minimum(lens, 1), 8, 2, 128, 16,
+                 wl.MASK_NONE, decode=True)
+    # sequences with L = 0 own no query row in the generator; give every sequence one
+    # query row (decode layout [S, H, D]) by rebuilding the query array
+    q = wl.round_to_storage(np.random.default_rng(3).standard_normal((5, 8, 128)).astype(np.float32), "bf16")
+    w.query = q
+    w.q_lens = np.ones(5, np.int32)
+    w.cu_seqlens_q = np.arange(6, dtype=np.int32)
+    d = Dev(w)
+    B.kv_cache_write(d.key, d.value, d.slots, d.kc, d.vc)
+    out = d.decode()
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    # single visible key: the output is that key's V row, bit-exact after rounding
+    v = ref.widen(w.value, "bf16")
+    for h in range(8):
+        assert np.array_equal(got[1, h], v[w.cu_seq_lens[1], h // 4])
+    # sequences with keys: the oracle's decode (the query is the newest of L_s tokens)
+    keys = ref.split_logical(ref.widen(w.key, "bf16"), w.cu_seq_lens)
+    vals = ref.split_logical(v, w.cu_seq_lens)
+    live = [1, 3, 4]
+    want, _ = ref.paged_attention(ref.widen(q[live], "bf16"), [keys[i] for i in live],
+                                  [vals[i] for i in live], np.arange(4, dtype=np.int32),
+                                  lens[live], 2, w.scale, wl.MASK_NONE)
+    compare(got[live], want, "bf16", "edge_decode")
+
+
+def test_decode_constant_value_rows(gpu):
+    """Constant V returns the constant for any query (closed form), exactly in bf16."""
+    w = wl.decode_batch(seed=13, num_seqs=6, lo=1, hi=2000)
+    w.value[:] = wl.round_to_storage(np.full(1, -0.625, np.float32), "bf16")[0]
+    d = Dev(w)
+    d.write_all()
+    out = d.decode()
+    torch.cuda.synchronize()
+    assert np.all(as_f64(out) == -0.625)
+
+
+def test_decode_rejects_small_workspace(gpu):
+    w = wl.decode_batch(seed=14, num_seqs=8, lo=2000, hi=4096)
+    d = Dev(w)
+    need = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq_len)
+    assert need > 0
+    out = torch.full_like(d.query, 3.0)
+    ws = torch.empty(need - 4, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.PkvError) as e:
+        B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens, w.scale,
+                                 w.max_seq_len, ws)
+    assert e.value.code == B.PKV_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)

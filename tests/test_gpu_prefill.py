@@ -1,0 +1,121 @@
+"""paged_attention_prefill on the GPU against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import reference as ref
+from paged_kv_scaled_amd import binding as B
+from paged_kv_scaled_amd import workloads as wl
+
+from gpu_helpers import Dev, as_f64, compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, combined=False, rows=None, heads=None):
+    d = Dev(w, combined=combined)
+    d.write_all()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    want, _ = ref.workload_attention(w, rows=rows, heads=heads)
+    if rows is not None:
+        got, want = got[rows], want[rows]
+    if heads is not None:
+        got, want = got[:, heads], want[:, heads]
+    return got, want, compare(got, want, w.dtype, w.name)
+
+
+def test_tiny_prefill(gpu):
+    """2 sequences (5, 9), GQA 2:1, D 16, fp32, causal, shuffled 8-block pool (3 unmapped)."""
+    w = wl.tiny_prefill()
+    got, want, _ = _run(w)
+    # causal row 0 of each sequence sees one key: its V row, exactly
+    v = ref.widen(w.value, "f32")
+    for s in range(2):
+        r0 = w.cu_seqlens_q[s]
+        for h in range(4):
+            assert np.array_equal(got[r0, h], v[w.cu_seq_lens[s], h // 2])
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_prefill_random_shapes(gpu, seed):
+    rng = np.random.default_rng(200 + seed)
+    d = int(rng.choice([16, 64, 128]))
+    dt = str(rng.choice(["bf16", "f16", "f32"]))
+    _run(wl.random_small(seed, dt, head_dim=d, max_len=70))
+
+
+@pytest.mark.parametrize("mask", [wl.MASK_NONE, wl.MASK_CAUSAL, wl.MASK_BLOCK_CAUSAL])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_chunked_masks(gpu, mask, dtype):
+    """Chunked prefill with cached context: several tiles and ragged tails."""
+    w = wl.chunked_prefill(seed=30 + mask, num_seqs=4, ctx_hi=300, q_lo=1, q_hi=200, dtype=dtype)
+    w.mask = mask
+    w.span_len = 48
+    _run(w)
+
+
+def test_chunked_prefill_scaled(gpu):
+    """The chunked-prefill shape (8 seqs, ctx <= 2048, chunk 32..512, 32q/8kv, D 128)."""
+    _run(wl.chunked_prefill())
+
+
+def test_long_block_causal_sampled(gpu):
+    """4 x 8192 tokens, 64 q heads, block-causal spans of 2048: sampled rows and heads."""
+    w = wl.long_block_causal()
+    rng = np.random.default_rng(7)
+    rows = []
+    for s in range(w.num_seqs):
+        base = s * 8192
+        # span edges, first/last rows and random rows
+        pick = [0, 1, 2047, 2048, 4095, 4096, 6143, 6144, 8191] + list(rng.integers(0, 8192, 7))
+        rows += [base + p for p in pick]
+    heads = [0, 7, 8, 33, 63]
+    _run(w, rows=np.array(sorted(set(rows))), heads=heads)
+
+
+def test_block_causal_span_one_equals_causal(gpu):
+    w = wl.chunked_prefill(seed=40, num_seqs=3, ctx_hi=100, q_lo=5, q_hi=90)
+    d = Dev(w)
+    d.write_all()
+    o1 = d.prefill()
+    w.mask, w.span_len = wl.MASK_BLOCK_CAUSAL, 1
+    o2 = d.prefill()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_prefill_combined_cache_layout(gpu):
+    w = wl.chunked_prefill(seed=41, num_seqs=3, ctx_hi=150, q_hi=100)
+    _run(w, combined=True)
+
+
+def test_prefill_empty_query_segments(gpu):
+    """Sequences with no new tokens (empty q segments) next to normal ones."""
+    lens = np.array([30, 0, 45, 12], np.int32)
+    ql = np.array([0, 0, 20, 12], np.int32)
+    w = wl.build("empty_segments", 42, "bf16", lens, ql, 8, 2, 128, 16, wl.MASK_CAUSAL)
+    _run(w)
+
+
+def test_prefill_constant_value_rows(gpu):
+    w = wl.chunked_prefill(seed=43, num_seqs=3, ctx_hi=200, q_hi=150)
+    w.value[:] = wl.round_to_storage(np.full(1, 1.5, np.float32), "bf16")[0]
+    d = Dev(w)
+    d.write_all()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    assert np.all(as_f64(out) == 1.5)
+
+
+def test_prefill_rejects_bad_arguments_before_writing(gpu):
+    w = wl.chunked_prefill(seed=44, num_seqs=2, ctx_hi=50, q_hi=40)
+    d = Dev(w)
+    out = torch.full_like(d.query, 7.0)
+    with pytest.raises(B.PkvError) as e:
+        B.paged_attention_prefill(out, d.query, d.cu_q, d.seq_lens, d.kc, d.vc, d.tables, w.scale,
+                                  wl.MASK_BLOCK_CAUSAL, 0, w.max_q_len, w.max_seq_len)
+    assert e.value.code == B.PKV_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
