@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Throughput of paged-KV attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode_batch,...]
+
+Default workload (the `value`): the decode batch -- 64 sequences with contexts
+U[256, 4096], 32 query / 8 kv heads, head_dim 128, block_size 16, bf16.  One step is
+one pass of the hot path over the batch: slot_mapping scatter of the 64 new K/V tokens
+into the paged cache, then paged decode attention (block-table gather fused into its
+loads, GQA by index, split-K with the log-sum-exp merge).  `value` is algorithmic bytes
+per step (each K/V row of every sequence read once, Q read, O written, tables and
+lengths, plus the scatter's reads and writes) over the measured step time.
+
+The other workloads (chunked prefill, s_q=1 small-seq varlen, long block-causal
+prefill) are measured with the same library and reported in `workloads`.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+METRIC = "decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% MFMA peak); GPU vs CPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic bytes of one decode launch: K and V rows of every sequence once, Q in,
+    O out, the block-table entries used and the lengths."""
+    import numpy as np
+    eb = 2 if w.dtype != "f32" else 4
+    L = w.seq_lens.astype(np.int64)
+    kv = int(L.sum()) * w.num_kv_heads * w.head_dim * eb * 2
+    qo = 2 * w.num_seqs * w.num_heads * w.head_dim * eb
+    tables = int(((L + w.block_size - 1) // w.block_size).sum()) * 4
+    return kv + qo + tables + w.num_seqs * 4
+
+
+def scatter_bytes(w, rows) -> int:
+    eb = 2 if w.dtype != "f32" else 4
+    return 2 * len(rows) * w.num_kv_heads * w.head_dim * eb * 2 + len(rows) * 8
+
+
+def prefill_flops(w) -> float:
+    """4*D per visible (query, key) pair per head: QK^T and PV, masked pairs excluded."""
+    import numpy as np
+    tot = 0
+    for s in range(w.num_seqs):
+        L, q = int(w.seq_lens[s]), int(w.q_lens[s])
+        a = np.arange(L - q, L, dtype=np.int64)
+        if w.mask == 0:
+            vis = np.full(q, L, np.int64)
+        elif w.mask == 1:
+            vis = np.minimum(L, a + 1)
+        else:
+            vis = np.minimum(L, (a // w.span_len + 1) * w.span_len)
+        tot += int(vis.sum())
+    return 4.0 * w.head_dim * w.num_heads * tot
+
+
+def prefill_bytes(w) -> int:
+    import numpy as np
+    eb = 2 if w.dtype != "f32" else 4
+    kv = int(w.seq_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * eb * 2
+    return kv + 2 * w.num_tokens * w.num_heads * w.head_dim * eb
+
+
+class Timer:
+    """HIP events on the current stream (the stream the library launches on)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((e0, e))
+
+    def ms(self):
+        self.torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def flush_llc(buf):
+    """Overwrite a 512 MB buffer so neither L2 nor the 256 MB MALL hold the inputs."""
+    buf.add_(1)
+
+
+def run_decode_step_bench(w, steps, warmup):
+    """The default step: scatter the new tokens, then decode."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import Dev
+    from paged_kv_scaled_amd import binding as B
+
+    d = Dev(w, fill="zero")
+    ctx = w.context_rows()
+    new = w.new_token_rows()
+    ci = torch.from_numpy(ctx).cuda()
+    B.kv_cache_write(d.key[ci], d.value[ci], d.slots[ci], d.kc, d.vc)      # untimed context
+    ni = torch.from_numpy(new).cuda()
+    nk, nv, ns = d.key[ni].contiguous(), d.value[ni].contiguous(), d.slots[ni].contiguous()
+    out = torch.empty_like(d.query)
+    wsb = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, w.max_seq_len)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+    def step(tw=None, ts=None):
+        e0 = ts.start() if ts else None
+        B.kv_cache_write(nk, nv, ns, d.kc, d.vc)
+        e1 = tw.start() if tw else None
+        B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens, w.scale,
+                                 w.max_seq_len, ws if wsb else None)
+        if tw:
+            tw.stop(e1)
+            ts.stop(e0)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    # event-timed pass: per-launch decode durations and whole-step durations
+    tw, ts = Timer(), Timer()
+    for _ in range(steps):
+        step(tw, ts)
+    dec_ms = tw.ms()
+    step_ms = ts.ms()
+    return dict(wall_ms=wall_ms, dec_ms=dec_ms, step_ms=step_ms, num_new=len(new), ws_bytes=wsb)
+
+
+def run_attention_bench(w, kind, steps, warmup, flush=False):
+    """Per-launch event timing of one attention entry point (cache written untimed)."""
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import Dev
+    from paged_kv_scaled_amd import binding as B
+
+    d = Dev(w, fill="zero")
+    d.write_all(split_new=False)
+    out = torch.empty_like(d.query)
+    if kind == "decode":
+        wsb = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, w.max_seq_len)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        call = lambda: B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens,
+                                                w.scale, w.max_seq_len, ws if wsb else None)
+    else:
+        call = lambda: B.paged_attention_prefill(out, d.query, d.cu_q, d.seq_lens, d.kc, d.vc,
+                                                 d.tables, w.scale, w.mask, w.span_len,
+                                                 w.max_q_len, w.max_seq_len)
+    buf = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda") if flush else None
+    for _ in range(warmup):
+        call()
+    tm = Timer()
+    for _ in range(steps):
+        if flush:
+            flush_llc(buf)
+        e = tm.start()
+        call()
+        tm.stop(e)
+    ms = tm.ms()
+    # scatter of the whole batch as its own HBM workload
+    ts = Timer()
+    for _ in range(max(3, steps // 4)):
+        e = ts.start()
+        B.kv_cache_write(d.key, d.value, d.slots, d.kc, d.vc)
+        ts.stop(e)
+    return ms, ts.ms()
+
+
+def med(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle as it stands, single BLAS thread, on a bounded prefix of the batch:
+    whole sequences are added until about budget_s seconds of oracle work have run."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import reference as ref
+
+    q = ref.widen(w.query, w.dtype)
+    k = ref.split_logical(ref.widen(w.key, w.dtype), w.cu_seq_lens)
+    v = ref.split_logical(ref.widen(w.value, w.dtype), w.cu_seq_lens)
+    done, nbytes = 0, 0
+    eb = 2
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for s in range(w.num_seqs):
+            r0, r1 = int(w.cu_seqlens_q[s]), int(w.cu_seqlens_q[s + 1])
+            ref.paged_attention(q[r0:r1], [k[s]], [v[s]], np.array([0, r1 - r0], np.int32),
+                                w.seq_lens[s:s + 1], w.num_kv_heads, w.scale, w.mask, w.span_len)
+            done += 1
+            L = int(w.seq_lens[s])
+            nbytes += L * w.num_kv_heads * w.head_dim * eb * 2 + 2 * (r1 - r0) * w.num_heads * w.head_dim * eb
+            if time.perf_counter() - t0 > budget_s:
+                break
+    el = time.perf_counter() - t0
+    return dict(value=round(nbytes / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"first {done} of {w.num_seqs} sequences of the decode batch "
+                       f"(all {w.num_heads} heads), fp64 numpy, 1 BLAS thread, {el:.1f} s",
+                seconds=round(el, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(sharding is described, not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from paged_kv_scaled_amd import binding as B
+    from paged_kv_scaled_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    B.load()
+    names = [n for n in args.workloads.split(",") if n]
+    result_wl = {}
+
+    # ---- default workload: decode batch step -------------------------------------------
+    log("generating decode_batch")
+    w = wl.decode_batch()
+    r = run_decode_step_bench(w, args.steps, args.warmup)
+    dbytes = decode_bytes(w)
+    sbytes = scatter_bytes(w, w.new_token_rows())
+    step_bytes = dbytes + sbytes
+    ms_step = r["wall_ms"] / args.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    dec_ms = med(r["dec_ms"])
+    achieved = dbytes / (dec_ms * 1e-3) / 1e9
+    log(f"decode_batch: step {ms_step*1e3:.1f} us, decode launch {dec_ms*1e3:.1f} us, "
+        f"{achieved:.0f} GB/s ({achieved/HBM_PEAK_GBS*100:.1f}% of HBM peak)")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "paged_attention_decode (decode_split_kernel + decode_merge_kernel)",
+                "bytes_per_launch": dbytes, "launch_us_median": round(dec_ms * 1e3, 2),
+                "launch_us_min": round(min(r["dec_ms"]) * 1e3, 2)}
+
+    # ---- other workloads ------------------------------------------------------------------
+    for name in names:
+        if name == "decode_batch":
+            continue
+        log(f"generating {name}")
+        wk = wl.CONFIGS[name]()
+        kind = "decode" if wk.decode else "prefill"
+        flush = kind == "prefill"
+        ms, sc_ms = run_attention_bench(wk, kind, args.steps, args.warmup, flush=flush)
+        m = med(ms)
+        entry = {"launch_us_median": round(m * 1e3, 2), "launch_us_min": round(min(ms) * 1e3, 2)}
+        if kind == "decode":
+            by = decode_bytes(wk)
+            entry.update(metric="decode attn HBM GB/s", value=round(by / (m * 1e-3) / 1e9, 1),
+                         unit="GB/s", frac_of_peak=round(by / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         bytes_per_launch=by)
+        else:
+            fl = prefill_flops(wk)
+            tf = fl / (m * 1e-3) / 1e12
+            entry.update(metric="prefill attn TFLOP/s", value=round(tf, 2), unit="TFLOP/s",
+                         frac_of_peak=round(tf / BF16_PEAK_TFLOPS, 4), flops_per_launch=fl,
+                         bytes_min=prefill_bytes(wk))
+        sb = scatter_bytes(wk, np.arange(wk.key.shape[0]))
+        entry["scatter_GBps"] = round(sb / (med(sc_ms) * 1e-3) / 1e9, 1)
+        log(f"{name}: {entry}")
+        result_wl[name] = entry
+        del wk
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu["gpu_over_cpu"] = round(value / cpu["value"], 1) if cpu["value"] > 0 else None
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, shuffled block pool)",
+        "config": {"workload": "decode_batch", "num_seqs": 64, "context": "U[256,4096]",
+                   "num_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
+                   "seed": 1, "sum_seq_lens": int(w.seq_lens.sum()),
+                   "step": "kv_cache_write(64 new tokens) + paged_attention_decode",
+                   "bytes_per_step": step_bytes, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "workloads": result_wl,
+        "step_us_event_median": round(med(r["step_ms"]) * 1e3, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -123,7 +123,7 @@ int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_le
  * Returns 0 for invalid sizes as well; the decode call then validates.
  */
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t max_seq_len);
+                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len);
 
 /*
  * pkv_paged_attention_decode -- single-token decode: one query token per

@@ -25,7 +25,7 @@ SIGNATURES = {
                                           _I32, ctypes.c_int, _P]),
     "pkv_kv_cache_gather": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32, _I32,
                                            _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
-    "pkv_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pkv_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32,
                                                   _I32, _I32, _I32, _I32, _F, _I32, _P, _SZ,
                                                   ctypes.c_int, _P]),
@@ -124,9 +124,9 @@ def kv_cache_gather(key_out, value_out, cu_seq_lens, key_cache, value_cache, blo
 
 
 def decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
-                          max_seq_len: int) -> int:
+                          block_size: int, max_seq_len: int) -> int:
     return int(load().pkv_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                 max_seq_len))
+                                                 block_size, max_seq_len))
 
 
 def paged_attention_decode(out, query, key_cache, value_cache, block_tables, seq_lens,

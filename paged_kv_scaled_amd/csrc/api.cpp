@@ -122,11 +122,12 @@ int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_le
 }
 
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t max_seq_len) {
+                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
-      !PKV_HEAD_DIM_SUPPORTED(head_dim) || max_seq_len < 0)
+      !PKV_HEAD_DIM_SUPPORTED(head_dim) || !is_pow2_in(block_size, 1, 256) || max_seq_len < 0)
     return 0;
-  return pkv::decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len).workspace_bytes;
+  return pkv::decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len)
+      .workspace_bytes;
 }
 
 int pkv_paged_attention_decode(void* out, const void* query, const void* key_cache,
@@ -154,7 +155,7 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
     return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
                 (long long)max_blocks_per_seq * block_size, max_seq_len);
   const pkv::DecodePlan plan =
-      pkv::decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
+      pkv::decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len);
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(PKV_ERR_WORKSPACE, "decode workspace of %zu bytes required (got %zu at %p)",
                 plan.workspace_bytes, workspace_bytes, workspace);

@@ -1,4 +1,4 @@
-// Single-token decode over a paged KV cache: split-K flash decoding + log-sum-exp merge.
+// Single-token decode over a paged KV cache: flash decoding + log-sum-exp merge.
 //
 // What is computed (Spyre paged-attention PR, "Description": gather from scattered
 // blocks, GQA by repeat_interleave, per-sequence attention): for each sequence s and
@@ -7,20 +7,29 @@
 // cross attention is the same call with one sequence per query token.
 //
 // How (MI355X design, HBM-bound, vector ALU only):
-//  * one wave = one work item (sequence, group of HPW query heads sharing a kv head,
-//    split of split_len keys); waves walk items in a grid-stride loop;
+//  * a wave handles one group of HPW query heads sharing a kv head over a contiguous
+//    segment of one sequence's keys;
 //  * lanes = (token t of a round, column c): a round covers TPR tokens, each token's
-//    D-element row of one kv head is read by LPT lanes with 16-byte loads, so a wave
-//    load instruction reads TPR contiguous row segments; the block-table gather is the
-//    address computation of those loads (no gathered copy exists);
+//    D-element row of one kv head is read by LPT lanes with 16-byte loads, so one wave
+//    load instruction reads TPR contiguous row segments.  The block-table gather is the
+//    address computation of those loads (no gathered copy exists); the segment's block
+//    ids sit in one register per lane and are fetched with a lane shuffle;
 //  * q . k with packed dot2 (v_dot2_f32_bf16 / _f16) and a DPP reduction over the LPT
 //    lanes of a token; every lane keeps a private online-softmax state (m, l, acc) over
-//    the tokens it sees, the max is only moved when it grows by more than 2^8 (the
-//    probabilities stay <= 256, exact after the final division);
+//    the tokens it sees; the max only moves when a score exceeds it by more than 2^8
+//    (probabilities stay <= 256, exact after the final division);
 //  * probabilities of two rounds are paired and multiplied into V with dot2 as well;
-//  * at the end of the item the lanes of a column merge their states (shuffles), and
-//    the wave writes either the final output (one split) or (acc, m, l) to the
-//    workspace for the merge kernel.
+//  * at the end of a segment the lanes of a column merge their states (shuffles).
+//
+// Work decomposition (two modes, picked on the host from the sizes):
+//  * stream mode (long contexts, up to 1024 sequences): the concatenated key axis of
+//    all sequences is cut into `nranges` equal ranges per head group, one wave each,
+//    so every wave does the same work whatever the length mix.  A sequence that lies
+//    inside one range is finished by that wave; a range boundary inside a sequence
+//    leaves (acc, m, l) partials that the merge kernel combines;
+//  * split mode (short sequences or very large batches): fixed splits of split_len keys
+//    per sequence, waves walk (sequence, split, head group) items in a grid-stride loop;
+//    sequences with one split are written directly.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,7 +38,11 @@ namespace pkv {
 namespace {
 
 constexpr int kDecodeThreads = 256;
+constexpr int kWavesPerBlock = kDecodeThreads / kWave;
 constexpr float kLazyRescale = 8.0f;   // log2 units
+constexpr int kStreamMaxSeqs = 1024;   // stream mode scans seq_lens in every wave
+constexpr int kStreamWaves = 4096;     // waves of the stream grid (all head groups)
+constexpr int kStreamMinRange = 64;    // shortest range, keys
 
 template <typename T, int D>
 struct DecodeShape {
@@ -41,7 +54,16 @@ struct DecodeShape {
   static constexpr int TPR = kWave / LPT;          // tokens per round
   static constexpr int WPL = VPL * 4;              // 32-bit words per lane per row
   static constexpr int EPL = VPL * EPV;            // elements per lane per row
+  static constexpr int STEP = 2 * TPR;             // keys per step (two rounds)
   static_assert(NV >= 1 && NV % LPT == 0, "head_dim / dtype combination");
+};
+
+// Steps whose loads are issued together: keep the K/V registers of one batch of steps
+// at about 64 per lane (2 rounds x 2 tensors x WPL words per step).
+template <typename T, int D, int HPW>
+struct DecodeSteps {
+  static constexpr int words = 4 * DecodeShape<T, D>::WPL;
+  static constexpr int value = (HPW >= 8 || words > 32) ? 1 : (words > 16 || HPW >= 4 ? 2 : 4);
 };
 
 struct DecodeParams {
@@ -52,10 +74,10 @@ struct DecodeParams {
   int64_t block_stride;     // elements
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* ws_acc;            // [S, H, nsplit, D]
-  float* ws_ml;             // [S, H, nsplit, 2]  (max in log2 units, sum)
-  int64_t total_items;
-  int32_t mb, S, H, Hkv, g, block_shift, split_len, nsplit, groups_per_kv;
+  float* ws_acc;            // [H, slots_per_head, D]
+  float* ws_ml;             // [H, slots_per_head, 2]  (max in log2 units, sum)
+  int64_t total_items;      // split mode: S*nsplit*HG; stream mode: HG*nranges
+  int32_t mb, S, H, Hkv, g, block_shift, split_len, nsplit, groups_per_kv, nranges;
   float scale_log2;
 };
 
@@ -67,39 +89,48 @@ struct Step {
   bool valid[2];
 };
 
+// Block ids of 64 consecutive pages, one per lane (lane i: page chunk_base + i).
+struct TableWindow {
+  int32_t ids;
+  int chunk_base;
+};
+
+__device__ __forceinline__ void table_window_load(TableWindow& tw, const int32_t* __restrict__ table,
+                                                  int first_page, int last_page, int lane) {
+  tw.chunk_base = first_page;
+  tw.ids = table[min(first_page + lane, last_page)];
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void load_step(Step<T, D>& st, const DecodeParams& p,
-                                          const int32_t* __restrict__ table, int64_t head_off,
-                                          int base, int end, int t, int c) {
+                                          const TableWindow& tw, int64_t head_off, int base,
+                                          int end, int t, int c) {
   using C = DecodeShape<T, D>;
   const int64_t row_elems = (int64_t)p.Hkv * D;
   const int bmask = (1 << p.block_shift) - 1;
+  // Loads are branch-free: a lane past the end of the segment re-reads its last key
+  // (finite data) and gets probability 0.  Divergent branches around the loads would
+  // make the compiler wait for every load in flight.
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int pos = base + r * C::TPR + t;
-    st.valid[r] = pos < end;
-    if (st.valid[r]) {
-      const int64_t blk = table[pos >> p.block_shift];
-      const int64_t row = blk * p.block_stride + (int64_t)(pos & bmask) * row_elems + head_off;
-      const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(
-          reinterpret_cast<const typename T::storage*>(p.kc) + row);
-      const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(
-          reinterpret_cast<const typename T::storage*>(p.vc) + row);
+    const int pos_raw = base + r * C::TPR + t;
+    st.valid[r] = pos_raw < end;
+    const int pos = min(pos_raw, end - 1);
+    const int idx = ((pos >> p.block_shift) - tw.chunk_base) & (kWave - 1);
+    const int64_t blk = __shfl(tw.ids, idx, kWave);
+    const int64_t row = blk * p.block_stride + (int64_t)(pos & bmask) * row_elems + head_off;
+    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const typename T::storage*>(p.kc) + row);
+    const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const typename T::storage*>(p.vc) + row);
 #pragma unroll
-      for (int v = 0; v < C::VPL; ++v) {
-        const u32x4_t kk = kp[v * C::LPT + c];
-        const u32x4_t vv = vp[v * C::LPT + c];
+    for (int v = 0; v < C::VPL; ++v) {
+      const u32x4_t kk = __builtin_nontemporal_load(kp + v * C::LPT + c);
+      const u32x4_t vv = __builtin_nontemporal_load(vp + v * C::LPT + c);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          st.k[r][v * 4 + w] = kk[w];
-          st.v[r][v * 4 + w] = vv[w];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < C::WPL; ++w) {
-        st.k[r][w] = 0u;
-        st.v[r][w] = 0u;
+      for (int w = 0; w < 4; ++w) {
+        st.k[r][v * 4 + w] = kk[w];
+        st.v[r][v * 4 + w] = vv[w];
       }
     }
   }
@@ -115,7 +146,8 @@ __device__ __forceinline__ float reduce_token(float x) {
 }
 
 template <typename T, int D, int HPW>
-__device__ __forceinline__ void compute_step(const Step<T, D>& st, const uint32_t (&q)[HPW][DecodeShape<T, D>::WPL],
+__device__ __forceinline__ void compute_step(const Step<T, D>& st,
+                                             const uint32_t (&q)[HPW][DecodeShape<T, D>::WPL],
                                              float (&m)[HPW], float (&l)[HPW],
                                              float (&acc)[HPW][DecodeShape<T, D>::EPL],
                                              float scale_log2) {
@@ -187,17 +219,148 @@ __device__ __forceinline__ void compute_step(const Step<T, D>& st, const uint32_
   }
 }
 
+// Attention state of one wave over keys [lo, hi) of sequence s for the query heads
+// h0 .. h0+nh-1 of kv head kvh.  On return every lane of column c holds the merged
+// (m, l, acc) for the dimensions of that column (acc relative to m, unnormalised).
+template <typename T, int D, int HPW, int NSTEP>
+__device__ __forceinline__ void attend_segment(const DecodeParams& p, int s, int kvh, int h0,
+                                               int nh, int lo, int hi, int lane, float (&m)[HPW],
+                                               float (&l)[HPW],
+                                               float (&acc)[HPW][DecodeShape<T, D>::EPL]) {
+  using C = DecodeShape<T, D>;
+  using S = typename T::storage;
+  const int t = lane / C::LPT, c = lane % C::LPT;
+  uint32_t q[HPW][C::WPL];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    // heads past the group re-read the group's first head and are never written
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const S*>(p.query) + ((int64_t)s * p.H + h0 + (hh < nh ? hh : 0)) * D);
+#pragma unroll
+    for (int v = 0; v < C::VPL; ++v) {
+      const u32x4_t qq = qp[v * C::LPT + c];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) q[hh][v * 4 + w] = qq[w];
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::EPL; ++e) acc[hh][e] = 0.f;
+  }
+  if (lo < hi) {
+    const int32_t* table = p.block_tables + (int64_t)s * p.mb;
+    const int64_t head_off = (int64_t)kvh * D;
+    const int last_page = (hi - 1) >> p.block_shift;
+    TableWindow tw;
+    table_window_load(tw, table, lo >> p.block_shift, last_page, lane);
+    // Each iteration issues the loads of NSTEP steps before computing any of them;
+    // no register buffer is carried across iterations.
+    for (int base = lo; base < hi; base += NSTEP * C::STEP) {
+      const int it_last = (min(base + NSTEP * C::STEP, hi) - 1) >> p.block_shift;
+      if (it_last >= tw.chunk_base + kWave)
+        table_window_load(tw, table, base >> p.block_shift, last_page, lane);
+      Step<T, D> st[NSTEP];
+#pragma unroll
+      for (int k = 0; k < NSTEP; ++k)
+        load_step<T, D>(st[k], p, tw, head_off, base + k * C::STEP, hi, t, c);
+#pragma unroll
+      for (int k = 0; k < NSTEP; ++k) compute_step<T, D, HPW>(st[k], q, m, l, acc, p.scale_log2);
+    }
+  }
+  // merge the private states of the TPR token lanes of each column
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    float M = m[hh];
+#pragma unroll
+    for (int off = C::LPT; off < kWave; off <<= 1) M = fmaxf(M, shfl_xor_f(M, off));
+    const float f = (m[hh] == -INFINITY) ? 0.f : fast_exp2(m[hh] - M);
+    float ll = l[hh] * f;
+#pragma unroll
+    for (int off = C::LPT; off < kWave; off <<= 1) ll += shfl_xor_f(ll, off);
+#pragma unroll
+    for (int e = 0; e < C::EPL; ++e) {
+      float x = acc[hh][e] * f;
+#pragma unroll
+      for (int off = C::LPT; off < kWave; off <<= 1) x += shfl_xor_f(x, off);
+      acc[hh][e] = x;
+    }
+    m[hh] = M;
+    l[hh] = ll;
+  }
+}
+
+// Final output rows of heads h0.. (lanes of round-token 0 write, one 16-byte vector each).
 template <typename T, int D, int HPW>
+__device__ __forceinline__ void write_output(const DecodeParams& p, int s, int h0, int nh, int c,
+                                             const float (&l)[HPW],
+                                             const float (&acc)[HPW][DecodeShape<T, D>::EPL]) {
+  using C = DecodeShape<T, D>;
+  using S = typename T::storage;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    if (hh >= nh) continue;
+    const float inv = l[hh] > 0.f ? 1.f / l[hh] : 0.f;
+    u32x4_t* op = reinterpret_cast<u32x4_t*>(reinterpret_cast<S*>(p.out) +
+                                             ((int64_t)s * p.H + h0 + hh) * D);
+#pragma unroll
+    for (int v = 0; v < C::VPL; ++v) {
+      u32x4_t o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (T::bytes == 2) {
+          const int e = (v * 4 + w) * 2;
+          o[w] = pack2(T{}, acc[hh][e] * inv, acc[hh][e + 1] * inv);
+        } else {
+          o[w] = __float_as_uint(acc[hh][v * 4 + w] * inv);
+        }
+      }
+      op[v * C::LPT + c] = o;
+    }
+  }
+}
+
+// Partial state of heads h0.. into workspace slot `slot` of each head.
+template <typename T, int D, int HPW>
+__device__ __forceinline__ void write_partial(const DecodeParams& p, int64_t slots_per_head,
+                                              int64_t slot, int h0, int nh, int c,
+                                              const float (&m)[HPW], const float (&l)[HPW],
+                                              const float (&acc)[HPW][DecodeShape<T, D>::EPL]) {
+  using C = DecodeShape<T, D>;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    if (hh >= nh) continue;
+    const int64_t idx = (int64_t)(h0 + hh) * slots_per_head + slot;
+    f32x4_t* wp = reinterpret_cast<f32x4_t*>(p.ws_acc + idx * D);
+#pragma unroll
+    for (int v = 0; v < C::VPL; ++v) {
+#pragma unroll
+      for (int q4 = 0; q4 < C::EPV / 4; ++q4) {
+        const int e = v * C::EPV + q4 * 4;
+        wp[(v * C::LPT + c) * (C::EPV / 4) + q4] =
+            (f32x4_t){acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]};
+      }
+    }
+    if (c == 0) {
+      p.ws_ml[idx * 2] = m[hh];
+      p.ws_ml[idx * 2 + 1] = l[hh];
+    }
+  }
+}
+
+// ---- split mode ------------------------------------------------------------------------
+
+template <typename T, int D, int HPW, int NSTEP>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_split_kernel(const DecodeParams p) {
   using C = DecodeShape<T, D>;
-  using S = typename T::storage;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = lane / C::LPT, c = lane % C::LPT;
-  const int64_t wave = (int64_t)blockIdx.x * (kDecodeThreads / kWave) + (threadIdx.x / kWave);
-  const int64_t nwaves = (int64_t)gridDim.x * (kDecodeThreads / kWave);
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int HG = p.Hkv * p.groups_per_kv;
-
   for (int64_t item = wave; item < p.total_items; item += nwaves) {
     const int hg = (int)(item % HG);
     const int64_t sj = item / HG;
@@ -211,153 +374,121 @@ decode_split_kernel(const DecodeParams p) {
     const int kvh = hg / p.groups_per_kv, sub = hg % p.groups_per_kv;
     const int h0 = kvh * p.g + sub * HPW;
     const int nh = min(HPW, p.g - sub * HPW);
-
-    uint32_t q[HPW][C::WPL];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      if (hh < nh) {
-        const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
-            reinterpret_cast<const S*>(p.query) + ((int64_t)s * p.H + h0 + hh) * D);
-#pragma unroll
-        for (int v = 0; v < C::VPL; ++v) {
-          const u32x4_t qq = qp[v * C::LPT + c];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) q[hh][v * 4 + w] = qq[w];
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < C::WPL; ++w) q[hh][w] = 0u;
-      }
-    }
-
     float m[HPW], l[HPW], acc[HPW][C::EPL];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      m[hh] = -INFINITY;
-      l[hh] = 0.f;
-#pragma unroll
-      for (int e = 0; e < C::EPL; ++e) acc[hh][e] = 0.f;
-    }
-
-    const int32_t* table = p.block_tables + (int64_t)s * p.mb;
-    const int64_t head_off = (int64_t)kvh * D;
-    constexpr int STEP = 2 * C::TPR;
-    if (start < end) {
-      Step<T, D> a, b;
-      load_step<T, D>(a, p, table, head_off, start, end, t, c);
-      int base = start;
-      while (true) {
-        if (base + STEP < end) load_step<T, D>(b, p, table, head_off, base + STEP, end, t, c);
-        compute_step<T, D, HPW>(a, q, m, l, acc, p.scale_log2);
-        base += STEP;
-        if (base >= end) break;
-        if (base + STEP < end) load_step<T, D>(a, p, table, head_off, base + STEP, end, t, c);
-        compute_step<T, D, HPW>(b, q, m, l, acc, p.scale_log2);
-        base += STEP;
-        if (base >= end) break;
-      }
-    }
-
-    // merge the private states of the TPR token lanes of each column
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      float M = m[hh];
-#pragma unroll
-      for (int off = C::LPT; off < kWave; off <<= 1) M = fmaxf(M, shfl_xor_f(M, off));
-      const float f = (m[hh] == -INFINITY) ? 0.f : fast_exp2(m[hh] - M);
-      float ll = l[hh] * f;
-#pragma unroll
-      for (int off = C::LPT; off < kWave; off <<= 1) ll += shfl_xor_f(ll, off);
-#pragma unroll
-      for (int e = 0; e < C::EPL; ++e) {
-        float x = acc[hh][e] * f;
-#pragma unroll
-        for (int off = C::LPT; off < kWave; off <<= 1) x += shfl_xor_f(x, off);
-        acc[hh][e] = x;
-      }
-      m[hh] = M;
-      l[hh] = ll;
-    }
-
+    attend_segment<T, D, HPW, NSTEP>(p, s, kvh, h0, nh, start, end, lane, m, l, acc);
     if (t == 0) {
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        if (hh >= nh) continue;
-        const int h = h0 + hh;
-        if (ns == 1) {
-          const float inv = l[hh] > 0.f ? 1.f / l[hh] : 0.f;
-          u32x4_t* op = reinterpret_cast<u32x4_t*>(reinterpret_cast<S*>(p.out) +
-                                                   ((int64_t)s * p.H + h) * D);
-#pragma unroll
-          for (int v = 0; v < C::VPL; ++v) {
-            u32x4_t o;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              if constexpr (T::bytes == 2) {
-                const int e = (v * 4 + w) * 2;
-                o[w] = pack2(T{}, acc[hh][e] * inv, acc[hh][e + 1] * inv);
-              } else {
-                o[w] = __float_as_uint(acc[hh][v * 4 + w] * inv);
-              }
-            }
-            op[v * C::LPT + c] = o;
-          }
-        } else {
-          const int64_t slot = ((int64_t)s * p.H + h) * p.nsplit + j;
-          f32x4_t* wp = reinterpret_cast<f32x4_t*>(p.ws_acc + slot * D);
-#pragma unroll
-          for (int v = 0; v < C::VPL; ++v) {
-#pragma unroll
-            for (int q4 = 0; q4 < C::EPV / 4; ++q4) {
-              const int e = v * C::EPV + q4 * 4;
-              wp[(v * C::LPT + c) * (C::EPV / 4) + q4] =
-                  (f32x4_t){acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]};
-            }
-          }
-          if (c == 0) {
-            p.ws_ml[slot * 2] = m[hh];
-            p.ws_ml[slot * 2 + 1] = l[hh];
-          }
-        }
-      }
+      if (ns == 1)
+        write_output<T, D, HPW>(p, s, h0, nh, c, l, acc);
+      else
+        write_partial<T, D, HPW>(p, (int64_t)p.S * p.nsplit, (int64_t)s * p.nsplit + j, h0, nh,
+                                 c, m, l, acc);
     }
   }
 }
 
-// One wave per (sequence, head): combine the splits of sequences that had more than one.
-template <typename T, int D>
-__global__ void __launch_bounds__(kDecodeThreads)
-decode_merge_kernel(const DecodeParams p) {
-  using S = typename T::storage;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t sh = (int64_t)blockIdx.x * (kDecodeThreads / kWave) + (threadIdx.x / kWave);
-  if (sh >= (int64_t)p.S * p.H) return;
-  const int s = (int)(sh / p.H);
-  const int L = p.seq_lens[s];
-  const int ns = L > 0 ? (L + p.split_len - 1) / p.split_len : 1;
-  if (ns <= 1) return;
-  const float* ml = p.ws_ml + sh * p.nsplit * 2;
-  float M = -INFINITY;
-  for (int j = lane; j < ns; j += kWave) M = fmaxf(M, ml[2 * j]);
+// ---- stream mode -----------------------------------------------------------------------
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) M = fmaxf(M, shfl_xor_f(M, off));
-  constexpr int DPL = (D + kWave - 1) / kWave;
-  float num[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) num[i] = 0.f;
-  float den = 0.f;
-  const float* acc = p.ws_acc + sh * p.nsplit * D;
-  for (int j = 0; j < ns; ++j) {
-    const float mj = ml[2 * j];
-    const float w = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
-    den += w * ml[2 * j + 1];
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      const int d = lane + i * kWave;
-      if (d < D) num[i] += w * acc[(int64_t)j * D + d];
-    }
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  return x;
+}
+
+// Total keys of the batch, and the range length every stream kernel derives from it.
+__device__ __forceinline__ int64_t stream_total(const DecodeParams& p, int lane) {
+  int64_t total = 0;
+  for (int c0 = 0; c0 < p.S; c0 += kWave) {
+    int x = (c0 + lane < p.S) ? p.seq_lens[c0 + lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
+    total += x;
+  }
+  return total;
+}
+
+__device__ __forceinline__ int64_t stream_range_len(int64_t total, int nranges) {
+  const int64_t r = (total + nranges - 1) / nranges;
+  return r < kStreamMinRange ? kStreamMinRange : r;
+}
+
+// First sequence whose keys reach past position x of the concatenated key axis, and the
+// position where that sequence starts.
+__device__ __forceinline__ void stream_locate(const DecodeParams& p, int64_t x, int lane, int& s0,
+                                              int64_t& start0) {
+  int count = 0;
+  int64_t carry = 0, before = 0;
+  for (int c0 = 0; c0 < p.S; c0 += kWave) {
+    const bool in = c0 + lane < p.S;
+    const int Ls = in ? p.seq_lens[c0 + lane] : 0;
+    const int64_t incl = carry + wave_inclusive_scan(Ls, lane);
+    const bool done = in && incl <= x;                 // sequence ends at or before x
+    count += __popcll(__ballot(done));
+    int64_t b = done ? incl : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int64_t o = __shfl_xor(b, off, kWave);
+      b = o > b ? o : b;
+    }
+    before = b > before ? b : before;
+    carry = __shfl(incl, kWave - 1, kWave);
+  }
+  s0 = count;
+  start0 = before;
+}
+
+template <typename T, int D, int HPW, int NSTEP>
+__global__ void __launch_bounds__(kDecodeThreads)
+decode_stream_kernel(const DecodeParams p) {
+  using C = DecodeShape<T, D>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = lane / C::LPT, c = lane % C::LPT;
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+  if (wave >= p.total_items) return;
+  const int HG = p.Hkv * p.groups_per_kv;
+  const int hg = (int)(wave % HG);
+  const int r = (int)(wave / HG);
+  const int64_t total = stream_total(p, lane);
+  const int64_t R = stream_range_len(total, p.nranges);
+  const int64_t lo = (int64_t)r * R;
+  const int64_t hi = min(total, lo + R);
+  if (lo >= hi) return;
+  const int kvh = hg / p.groups_per_kv, sub = hg % p.groups_per_kv;
+  const int h0 = kvh * p.g + sub * HPW;
+  const int nh = min(HPW, p.g - sub * HPW);
+  int s;
+  int64_t P;
+  stream_locate(p, lo, lane, s, P);
+  bool first = true;
+  for (; s < p.S && P < hi; ++s) {
+    const int L = p.seq_lens[s];
+    const int seg_lo = (int)((lo > P ? lo : P) - P);
+    const int seg_hi = (int)((hi < P + L ? hi : P + L) - P);
+    if (seg_hi > seg_lo) {
+      float m[HPW], l[HPW], acc[HPW][C::EPL];
+      attend_segment<T, D, HPW, NSTEP>(p, s, kvh, h0, nh, seg_lo, seg_hi, lane, m, l, acc);
+      if (t == 0) {
+        if (seg_lo == 0 && seg_hi == L)
+          write_output<T, D, HPW>(p, s, h0, nh, c, l, acc);
+        else
+          write_partial<T, D, HPW>(p, (int64_t)p.nranges * 2, (int64_t)r * 2 + (first ? 0 : 1),
+                                   h0, nh, c, m, l, acc);
+      }
+      first = false;
+    }
+    P += L;
+  }
+}
+
+// ---- merge -----------------------------------------------------------------------------
+
+template <typename T, int D>
+__device__ __forceinline__ void store_row(const DecodeParams& p, int64_t sh, int lane,
+                                          const float* num, float inv) {
+  using S = typename T::storage;
+  constexpr int DPL = (D + kWave - 1) / kWave;
   S* o = reinterpret_cast<S*>(p.out) + sh * D;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) {
@@ -372,45 +503,98 @@ decode_merge_kernel(const DecodeParams p) {
   }
 }
 
+// Combine the partials of one head: slots `first + j * stride`, j < n.
+template <typename T, int D>
+__device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, int h,
+                                            int64_t slots_per_head, int n, int lane,
+                                            int64_t slot0, int64_t slot1, int64_t slot_step) {
+  constexpr int DPL = (D + kWave - 1) / kWave;
+  // slot of partial j: j == 0 -> slot0, else slot1 + (j - 1) * slot_step
+  auto slot_of = [&](int j) -> int64_t {
+    return (int64_t)h * slots_per_head + (j == 0 ? slot0 : slot1 + (int64_t)(j - 1) * slot_step);
+  };
+  float M = -INFINITY;
+  for (int j = lane; j < n; j += kWave) M = fmaxf(M, p.ws_ml[slot_of(j) * 2]);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) M = fmaxf(M, shfl_xor_f(M, off));
+  float num[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) num[i] = 0.f;
+  float den = 0.f;
+  for (int j = 0; j < n; ++j) {
+    const int64_t sl = slot_of(j);
+    const float mj = p.ws_ml[sl * 2];
+    const float w = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
+    den += w * p.ws_ml[sl * 2 + 1];
+    const float* acc = p.ws_acc + sl * D;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int d = lane + i * kWave;
+      if (d < D) num[i] += w * acc[d];
+    }
+  }
+  store_row<T, D>(p, sh, lane, num, den > 0.f ? 1.f / den : 0.f);
+}
+
+// Split mode: one wave per (sequence, head) with more than one split.
+template <typename T, int D>
+__global__ void __launch_bounds__(kDecodeThreads)
+decode_merge_split_kernel(const DecodeParams p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t sh = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+  if (sh >= (int64_t)p.S * p.H) return;
+  const int s = (int)(sh / p.H), h = (int)(sh % p.H);
+  const int L = p.seq_lens[s];
+  const int ns = L > 0 ? (L + p.split_len - 1) / p.split_len : 1;
+  if (ns <= 1) return;
+  const int64_t base = (int64_t)s * p.nsplit;
+  merge_slots<T, D>(p, sh, h, (int64_t)p.S * p.nsplit, ns, lane, base, base + 1, 1);
+}
+
+// Stream mode: one wave per (sequence, head).  Sequences inside one range were written
+// by the stream kernel; empty sequences get zeros; the others combine one partial per
+// range they touch (the first range's partial is its second slot unless the sequence
+// starts exactly at that range's start).
+template <typename T, int D>
+__global__ void __launch_bounds__(kDecodeThreads)
+decode_merge_stream_kernel(const DecodeParams p) {
+  constexpr int DPL = (D + kWave - 1) / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t sh = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+  if (sh >= (int64_t)p.S * p.H) return;
+  const int s = (int)(sh / p.H), h = (int)(sh % p.H);
+  const int L = p.seq_lens[s];
+  if (L == 0) {
+    float zero[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) zero[i] = 0.f;
+    store_row<T, D>(p, sh, lane, zero, 0.f);
+    return;
+  }
+  const int64_t total = stream_total(p, lane);
+  const int64_t R = stream_range_len(total, p.nranges);
+  // start of sequence s on the concatenated axis
+  int64_t P = 0;
+  for (int c0 = 0; c0 < s; c0 += kWave) {
+    int x = (c0 + lane < s) ? p.seq_lens[c0 + lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
+    P += x;
+  }
+  const int64_t r0 = P / R, r1 = (P + L - 1) / R;
+  if (r0 == r1) return;
+  const int64_t slot0 = r0 * 2 + ((r0 * R < P) ? 1 : 0);
+  merge_slots<T, D>(p, sh, h, (int64_t)p.nranges * 2, (int)(r1 - r0 + 1), lane, slot0,
+                    (r0 + 1) * 2, 2);
+}
+
+// ---- dispatch --------------------------------------------------------------------------
+
 int heads_per_wave(int g) {
   if (g <= 1) return 1;
   if (g == 2) return 2;
   if (g <= 4) return 4;
   return 8;
-}
-
-template <typename T, int D, int HPW>
-void launch_split(const DecodeParams& dp, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<T, D, HPW>), dim3(blocks), dim3(kDecodeThreads), 0,
-                     stream, dp);
-}
-
-template <typename T, int D>
-void launch_split_hpw(const DecodeParams& dp, int hpw, int blocks, hipStream_t stream) {
-  switch (hpw) {
-    case 1: launch_split<T, D, 1>(dp, blocks, stream); break;
-    case 2: launch_split<T, D, 2>(dp, blocks, stream); break;
-    case 4: launch_split<T, D, 4>(dp, blocks, stream); break;
-    default: launch_split<T, D, 8>(dp, blocks, stream); break;
-  }
-}
-
-template <typename T>
-void launch_split_d(const DecodeParams& dp, int d, int hpw, int blocks, hipStream_t stream) {
-  switch (d) {
-    case 16: launch_split_hpw<T, 16>(dp, hpw, blocks, stream); break;
-    case 64: launch_split_hpw<T, 64>(dp, hpw, blocks, stream); break;
-    default: launch_split_hpw<T, 128>(dp, hpw, blocks, stream); break;
-  }
-}
-
-template <typename T>
-void launch_merge_d(const DecodeParams& dp, int d, int blocks, hipStream_t stream) {
-  switch (d) {
-    case 16: hipLaunchKernelGGL((decode_merge_kernel<T, 16>), dim3(blocks), dim3(kDecodeThreads), 0, stream, dp); break;
-    case 64: hipLaunchKernelGGL((decode_merge_kernel<T, 64>), dim3(blocks), dim3(kDecodeThreads), 0, stream, dp); break;
-    default: hipLaunchKernelGGL((decode_merge_kernel<T, 128>), dim3(blocks), dim3(kDecodeThreads), 0, stream, dp); break;
-  }
 }
 
 int log2_exact(int x) {
@@ -419,29 +603,84 @@ int log2_exact(int x) {
   return s;
 }
 
+template <typename T, int D, int HPW>
+void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream) {
+  using C = DecodeShape<T, D>;
+  constexpr int NS = DecodeSteps<T, D, HPW>::value;
+  if (pl.stream) {
+    const int blocks = (int)((dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, NS>), dim3(blocks), dim3(kDecodeThreads),
+                       0, stream, dp);
+    return;
+  }
+  const int64_t wanted = (dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int blocks = (int)(wanted < 8192 ? wanted : 8192);
+  if (pl.max_seq_len <= C::STEP)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, HPW, 1>), dim3(blocks), dim3(kDecodeThreads),
+                       0, stream, dp);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, HPW, NS>), dim3(blocks), dim3(kDecodeThreads),
+                       0, stream, dp);
+}
+
+template <typename T, int D>
+void launch_hpw(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream) {
+  switch (pl.heads_per_wave) {
+    case 1: launch_main<T, D, 1>(dp, pl, stream); break;
+    case 2: launch_main<T, D, 2>(dp, pl, stream); break;
+    case 4: launch_main<T, D, 4>(dp, pl, stream); break;
+    default: launch_main<T, D, 8>(dp, pl, stream); break;
+  }
+}
+
+template <typename T, int D>
+void launch_merge(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream) {
+  const int blocks = (int)(((int64_t)dp.S * dp.H + kWavesPerBlock - 1) / kWavesPerBlock);
+  if (pl.stream)
+    hipLaunchKernelGGL((decode_merge_stream_kernel<T, D>), dim3(blocks), dim3(kDecodeThreads), 0,
+                       stream, dp);
+  else
+    hipLaunchKernelGGL((decode_merge_split_kernel<T, D>), dim3(blocks), dim3(kDecodeThreads), 0,
+                       stream, dp);
+}
+
+template <typename T>
+void launch_all(const DecodeParams& dp, const DecodePlan& pl, int d, bool merge,
+                hipStream_t stream) {
+  switch (d) {
+    case 16: merge ? launch_merge<T, 16>(dp, pl, stream) : launch_hpw<T, 16>(dp, pl, stream); break;
+    case 64: merge ? launch_merge<T, 64>(dp, pl, stream) : launch_hpw<T, 64>(dp, pl, stream); break;
+    default: merge ? launch_merge<T, 128>(dp, pl, stream) : launch_hpw<T, 128>(dp, pl, stream); break;
+  }
+}
+
 }  // namespace
 
 DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                       int max_seq_len) {
+                       int block_size, int max_seq_len) {
   DecodePlan pl{};
   const int g = num_kv_heads > 0 ? num_heads / num_kv_heads : 1;
   pl.heads_per_wave = heads_per_wave(g);
   pl.groups_per_kv = (g + pl.heads_per_wave - 1) / pl.heads_per_wave;
-  const int64_t items_per_split = (int64_t)num_seqs * num_kv_heads * pl.groups_per_kv;
-  // Splits of >= 256 keys; lengthen them until the item count is at most 16384
-  // (about 16 waves per CU on 256 CUs), so the per-split merge traffic stays small.
-  int split = 256;
-  while (split < max_seq_len &&
-         items_per_split * (((int64_t)max_seq_len + split - 1) / split) > 16384)
+  const int64_t groups = (int64_t)num_kv_heads * pl.groups_per_kv;
+  // Split mode: splits of >= 256 keys within 64 blocks, lengthened until the item count
+  // is at most 16384 (about 16 waves per CU on 256 CUs).
+  const int max_split = kWave * block_size;
+  int split = 256 < max_split ? 256 : max_split;
+  while (split < max_seq_len && split * 2 <= max_split &&
+         (int64_t)num_seqs * groups * (((int64_t)max_seq_len + split - 1) / split) > 16384)
     split *= 2;
   pl.split_len = split;
+  pl.max_seq_len = max_seq_len;
   pl.num_splits = max_seq_len > 0 ? (max_seq_len + split - 1) / split : 1;
   if (pl.num_splits < 1) pl.num_splits = 1;
-  pl.workspace_bytes = 0;
-  if (pl.num_splits > 1) {
-    const size_t slots = (size_t)num_seqs * num_heads * pl.num_splits;
-    pl.workspace_bytes = slots * (size_t)head_dim * sizeof(float) + slots * 2 * sizeof(float);
-  }
+  // Stream mode whenever some sequence needs more than one split and the batch is small
+  // enough for every wave to scan the lengths.
+  pl.stream = pl.num_splits > 1 && num_seqs <= kStreamMaxSeqs;
+  pl.num_ranges = pl.stream ? (int)(kStreamWaves / groups > 1 ? kStreamWaves / groups : 1) : 0;
+  const size_t slots = pl.stream ? (size_t)num_heads * pl.num_ranges * 2
+                                 : (pl.num_splits > 1 ? (size_t)num_seqs * num_heads * pl.num_splits : 0);
+  pl.workspace_bytes = slots * (size_t)head_dim * sizeof(float) + slots * 2 * sizeof(float);
   return pl;
 }
 
@@ -464,25 +703,24 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& pl, hipStream_t st
   dp.split_len = pl.split_len;
   dp.nsplit = pl.num_splits;
   dp.groups_per_kv = pl.groups_per_kv;
+  dp.nranges = pl.num_ranges;
   dp.scale_log2 = a.scale * kLog2e;
-  const size_t slots = (size_t)a.num_seqs * a.num_heads * pl.num_splits;
-  dp.ws_acc = pl.num_splits > 1 ? reinterpret_cast<float*>(a.workspace) : nullptr;
-  dp.ws_ml = pl.num_splits > 1 ? dp.ws_acc + slots * a.head_dim : nullptr;
-  dp.total_items = (int64_t)a.num_seqs * pl.num_splits * a.num_kv_heads * pl.groups_per_kv;
-  const int64_t wanted = (dp.total_items + 3) / 4;
-  const int blocks = (int)(wanted < 8192 ? wanted : 8192);
+  const size_t slots = pl.workspace_bytes / ((size_t)(a.head_dim + 2) * sizeof(float));
+  dp.ws_acc = pl.workspace_bytes ? reinterpret_cast<float*>(a.workspace) : nullptr;
+  dp.ws_ml = pl.workspace_bytes ? dp.ws_acc + slots * a.head_dim : nullptr;
+  const int64_t groups = (int64_t)a.num_kv_heads * pl.groups_per_kv;
+  dp.total_items = pl.stream ? groups * pl.num_ranges : (int64_t)a.num_seqs * pl.num_splits * groups;
   switch (a.dtype) {
-    case kBF16: launch_split_d<BF16>(dp, a.head_dim, pl.heads_per_wave, blocks, stream); break;
-    case kF16: launch_split_d<F16>(dp, a.head_dim, pl.heads_per_wave, blocks, stream); break;
-    default: launch_split_d<F32>(dp, a.head_dim, pl.heads_per_wave, blocks, stream); break;
+    case kBF16: launch_all<BF16>(dp, pl, a.head_dim, false, stream); break;
+    case kF16: launch_all<F16>(dp, pl, a.head_dim, false, stream); break;
+    default: launch_all<F32>(dp, pl, a.head_dim, false, stream); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.num_splits <= 1) return e;
-  const int mblocks = (int)(((int64_t)a.num_seqs * a.num_heads + 3) / 4);
+  if (e != hipSuccess || !(pl.stream || pl.num_splits > 1)) return e;
   switch (a.dtype) {
-    case kBF16: launch_merge_d<BF16>(dp, a.head_dim, mblocks, stream); break;
-    case kF16: launch_merge_d<F16>(dp, a.head_dim, mblocks, stream); break;
-    default: launch_merge_d<F32>(dp, a.head_dim, mblocks, stream); break;
+    case kBF16: launch_all<BF16>(dp, pl, a.head_dim, true, stream); break;
+    case kF16: launch_all<F16>(dp, pl, a.head_dim, true, stream); break;
+    default: launch_all<F32>(dp, pl, a.head_dim, true, stream); break;
   }
   return hipGetLastError();
 }

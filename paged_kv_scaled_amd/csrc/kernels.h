@@ -61,12 +61,15 @@ struct AttnArgs {
 struct DecodePlan {
   int heads_per_wave;   // query heads of one kv group handled by one wave (power of 2)
   int groups_per_kv;    // waves needed to cover the g = H / Hkv heads of one kv head
-  int split_len;        // keys per split
-  int num_splits;       // splits of the longest sequence
+  int split_len;        // keys per split (split mode)
+  int num_splits;       // splits of the longest sequence (split mode)
+  bool stream;          // equal ranges of the concatenated key axis instead of splits
+  int num_ranges;       // ranges per head group (stream mode)
+  int max_seq_len;
   size_t workspace_bytes;
 };
 DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                       int max_seq_len);
+                       int block_size, int max_seq_len);
 
 hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_kv_gather(const GatherArgs& a, hipStream_t stream);

@@ -83,7 +83,7 @@ def _decode(lib, **kw):
 
 
 def test_decode_rejections(lib):
-    need = lib.pkv_decode_workspace_size(64, 32, 8, 128, 4096)
+    need = lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 4096)
     assert need > 0
     assert _decode(lib, wsb=need - 1) == B.PKV_ERR_WORKSPACE
     assert _decode(lib, ws=NULL, wsb=need) == B.PKV_ERR_WORKSPACE
@@ -99,11 +99,14 @@ def test_decode_rejections(lib):
 
 def test_decode_workspace_size_plan(lib):
     # one split per sequence -> no workspace
-    assert lib.pkv_decode_workspace_size(30720, 16, 16, 128, 16) == 0
-    # 64 x 32 heads x 16 splits of 256 keys x (128 + 2) floats
-    assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 4096) == 64 * 32 * 16 * 130 * 4
-    assert lib.pkv_decode_workspace_size(64, 30, 8, 128, 4096) == 0    # invalid -> 0
-    assert lib.pkv_decode_workspace_size(1, 8, 8, 128, 131072) > 0
+    assert lib.pkv_decode_workspace_size(30720, 16, 16, 128, 16, 16) == 0
+    # stream mode: 32 heads x 512 ranges x 2 partial slots x (128 + 2) floats
+    assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 4096) == 32 * 512 * 2 * 130 * 4
+    # split mode beyond 1024 sequences: splits grow to 64 blocks (1024 keys), 5 of them
+    assert lib.pkv_decode_workspace_size(2000, 8, 8, 128, 16, 5000) == 2000 * 8 * 5 * 130 * 4
+    assert lib.pkv_decode_workspace_size(2000, 8, 8, 128, 16, 300) == 0
+    assert lib.pkv_decode_workspace_size(64, 30, 8, 128, 16, 4096) == 0    # invalid -> 0
+    assert lib.pkv_decode_workspace_size(1, 8, 8, 128, 16, 131072) > 0
 
 
 def _prefill(lib, **kw):

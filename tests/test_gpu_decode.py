@@ -119,7 +119,7 @@ def test_decode_constant_value_rows(gpu):
 def test_decode_rejects_small_workspace(gpu):
     w = wl.decode_batch(seed=14, num_seqs=8, lo=2000, hi=4096)
     d = Dev(w)
-    need = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq_len)
+    need = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, w.max_seq_len)
     assert need > 0
     out = torch.full_like(d.query, 3.0)
     ws = torch.empty(need - 4, dtype=torch.uint8, device="cuda")
