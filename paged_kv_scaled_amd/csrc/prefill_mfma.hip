@@ -1,11 +1,423 @@
-// Prefill attention on bf16/fp16 MFMA (placeholder until the MFMA kernel lands).
+// Prefill / chunked-prefill attention on bf16 / fp16 MFMA (gfx950, v_mfma_f32_32x32x16).
+//
+// What is computed (Spyre paged-attention PR, "Description" steps 2-6 on a flat query
+// batch; bottom-right causal and the block-causal "(q >= kv) or same block" mask of the
+// vllm-omni piecewise block-causal PR): out[t, h] = softmax(scale * q K^T) V over the
+// visible keys of the sequence owning row t, kv head h / (H / Hkv).
+//
+// How:
+//  * a workgroup (4 waves) owns one sequence, one kv head, a group of HW query heads of
+//    that kv head and 32*RB consecutive query rows, with HW * RB = 8 column blocks of
+//    (one head, 32 rows); each wave computes two column blocks, so the K/V tiles it
+//    reads from LDS feed 64 query columns;
+//  * keys are visited in tiles of 64.  K and V rows are gathered through the block table
+//    (page ids staged in LDS) with 16-byte loads into registers one tile ahead, then
+//    written to LDS: K row-major, V transposed (dims x tokens); both XOR-swizzled so the
+//    MFMA operand reads hit distinct banks;
+//  * S^T = K Q^T on MFMA (A = K rows from LDS, B = Q rows held in registers): each lane
+//    then holds 32 scores of one query row, so the row max needs one cross-lane step;
+//  * online softmax in fp32 registers (exp2 with scale*log2(e) folded; the max only
+//    moves when a score exceeds it by more than 2^8, so the O rescale is rare);
+//  * the probabilities stay where the S^T accumulator put them and are used directly as
+//    the B operand of O^T = V^T P^T: the V^T tile stores each 16-token group in the
+//    token order that accumulator layout implies;
+//  * tiles that a wave's rows cannot see are skipped; fully visible tiles skip the mask.
 #include "common.h"
 #include "kernels.h"
 
 namespace pkv {
 
-bool prefill_mfma_supported(int, int) { return false; }
+namespace {
 
-hipError_t launch_prefill_mfma(const AttnArgs&, hipStream_t) { return hipErrorNotSupported; }
+constexpr int kThreads = 256;
+constexpr int kBN = 64;            // keys per tile
+constexpr int kTableChunk = 1024;  // page ids staged in LDS at a time
+constexpr float kLazy = 8.0f;
+
+struct PrefillParams {
+  void* out;
+  const void* query;
+  const int32_t* cu_q;
+  const int32_t* seq_lens;
+  const void* kc;
+  const void* vc;
+  int64_t block_stride;
+  const int32_t* block_tables;
+  int32_t mb, S, H, Hkv, g, block_shift, mask, span;
+  int32_t hw, rb_log2, head_groups, qtiles;   // WG tiling
+  int32_t nblocks;                            // total workgroups
+  float scale_log2;
+};
+
+template <typename T> struct Mfma;
+template <> struct Mfma<BF16> {
+  static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<F16> {
+  static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ int visible_end(int mask, int a, int L, int span) {
+  if (mask == 1) return min(L, a + 1);
+  if (mask == 2) return min(L, (a / span + 1) * span);
+  return L;
+}
+
+// LDS layouts.  K: [kBN tokens][D] with 16-byte chunk kc of row r at kc ^ (r & (NC-1)).
+// V^T: [D dims][kBN tokens], chunk (8 tokens) kc of row r at kc ^ vswz(r).
+template <int D>
+struct Lds {
+  static constexpr int NC = D / 8;                 // 16-byte chunks per K row
+  static constexpr int KBYTES = kBN * D * 2;
+  static constexpr int VROW = kBN * 2;             // bytes per V^T row
+  static constexpr int VBYTES = D * VROW;
+  __device__ static __forceinline__ int k_off(int row, int kc) {
+    return row * (D * 2) + ((kc ^ (row & (NC - 1))) << 4);
+  }
+  __device__ static __forceinline__ int vswz(int row) { return ((row >> 1) ^ (row >> 4)) & 7; }
+  __device__ static __forceinline__ int v_off(int row, int pos) {   // pos: token slot 0..63
+    return row * VROW + (((pos >> 3) ^ vswz(row)) << 4) + ((pos & 7) << 1);
+  }
+};
+
+// Position of token t (0..63) of a tile in the V^T row: inside each 16-token group the
+// 4-token runs 1 and 2 trade places, the order in which the S^T accumulator holds them.
+__device__ __forceinline__ int vt_pos(int t) {
+  const int run = (t >> 2) & 3;
+  const int swapped = (run == 1) ? 2 : (run == 2 ? 1 : run);
+  return (t & ~15) | (swapped << 2) | (t & 3);
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+prefill_mfma_kernel(const PrefillParams p) {
+  using L = Lds<D>;
+  constexpr int NC = L::NC;
+  constexpr int KS = D / 16;          // k-steps of the QK^T product
+  constexpr int DB = D / 32;          // 32-dim blocks of O^T
+  constexpr int KROWS = kThreads / NC;           // K rows loaded per pass
+  constexpr int KLOADS = kBN / KROWS;            // K vectors per thread
+  constexpr int TG = D / 32;                     // tokens per thread for V (2 or 4)
+  __shared__ __align__(16) uint8_t s_k[L::KBYTES];
+  __shared__ __align__(16) uint8_t s_v[L::VBYTES];
+  __shared__ int32_t s_tbl[kTableChunk];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int hl = lane >> 5;           // lane half
+  const int lc = lane & 31;           // lane column
+
+  // ---- workgroup -> (sequence, kv head, head group, query tile), XCD-grouped --------
+  const int nb = p.nblocks;
+  const int bid = blockIdx.x;
+  const int per_xcd = (nb + 7) >> 3;
+  const int logical = (bid & 7) * per_xcd + (bid >> 3);
+  if (logical >= nb) return;
+  const int qt_rev = logical % p.qtiles;
+  int rest = logical / p.qtiles;
+  const int hgrp = rest % p.head_groups;
+  rest /= p.head_groups;
+  const int kvh = rest % p.Hkv;
+  const int s = rest / p.Hkv;
+  const int qt = p.qtiles - 1 - qt_rev;       // the longest tiles start first
+  const int q0 = p.cu_q[s];
+  const int qn = p.cu_q[s + 1] - q0;
+  const int RB = 1 << p.rb_log2;
+  const int wg_rows = 32 * RB;
+  const int row0 = qt * wg_rows;
+  if (row0 >= qn) return;
+  const int Ls = p.seq_lens[s];
+  const int ctx = Ls - qn;
+
+  // ---- this wave's two column blocks ------------------------------------------------
+  int head[2], rbase[2], vis[2];
+  bool hvalid[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cb = wv * 2 + j;
+    const int hw_i = cb % p.hw;
+    const int rb_i = cb / p.hw;
+    const int hin = hgrp * p.hw + hw_i;          // head index inside the kv group
+    hvalid[j] = hin < p.g;
+    head[j] = kvh * p.g + (hvalid[j] ? hin : 0);
+    rbase[j] = row0 + rb_i * 32;
+    const int row = min(rbase[j] + lc, qn - 1);  // rows past the chunk repeat the last one
+    vis[j] = visible_end(p.mask, ctx + row, Ls, p.span);
+  }
+  int wmax = max(vis[0], vis[1]), wmin = min(vis[0], vis[1]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    wmax = max(wmax, __shfl_xor(wmax, off, 64));
+    wmin = min(wmin, __shfl_xor(wmin, off, 64));
+  }
+  // keys the whole workgroup needs: the last row of its tile sees the most
+  const int last_row = min(row0 + wg_rows, qn) - 1;
+  const int kv_end = visible_end(p.mask, ctx + last_row, Ls, p.span);
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[row lc][dims ks*16+hl*8..+8]
+  using S = typename T::storage;
+  u32x4_t qf[2][KS];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = min(rbase[j] + lc, qn - 1);
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const S*>(p.query) + ((int64_t)(q0 + row) * p.H + head[j]) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[j][ks] = qp[ks * 2 + hl];
+  }
+
+  // ---- page ids of this sequence, staged in LDS ------------------------------------
+  const int32_t* table = p.block_tables + (int64_t)s * p.mb;
+  const int last_page = (kv_end - 1) >> p.block_shift;
+  int tbl_base = 0;
+  for (int i = tid; i < kTableChunk; i += kThreads) s_tbl[i] = table[min(i, last_page)];
+  __syncthreads();
+
+  // ---- K / V tile loads into registers (clamped to the last key: finite data) -------
+  const int64_t row_elems = (int64_t)p.Hkv * D;
+  const int64_t head_off = (int64_t)kvh * D;
+  const int bmask = (1 << p.block_shift) - 1;
+  const int kc_ld = tid % NC;
+  const int kr_ld = tid / NC;
+  const int vc_ld = tid % NC;               // 8-dim chunk for V
+  const int vg_ld = tid / NC;               // token group of TG tokens for V
+  u32x4_t kreg[KLOADS], vreg[TG];
+
+  // keys past kv_end (seen by no row of this workgroup) re-read key kv_end-1: finite
+  // data whose page id is inside the staged window
+  auto row_ptr = [&](const void* base, int tok) -> const u32x4_t* {
+    const int pos = min(tok, kv_end - 1);
+    const int64_t blk = s_tbl[(pos >> p.block_shift) - tbl_base];
+    return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const S*>(base) + blk * p.block_stride +
+                                            (int64_t)(pos & bmask) * row_elems + head_off);
+  };
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) kreg[i] = row_ptr(p.kc, k0 + kr_ld + i * KROWS)[kc_ld];
+#pragma unroll
+    for (int i = 0; i < TG; ++i) vreg[i] = row_ptr(p.vc, k0 + vg_ld * TG + i)[vc_ld];
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i)
+      *reinterpret_cast<u32x4_t*>(s_k + L::k_off(kr_ld + i * KROWS, kc_ld)) = kreg[i];
+    // transpose TG tokens x 8 dims into 8 dims x TG tokens
+    const int pos = vt_pos(vg_ld * TG);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int w = d >> 1;
+      const bool hi = d & 1;
+      auto el = [&](int i) -> uint32_t { return hi ? (vreg[i][w] >> 16) : (vreg[i][w] & 0xFFFFu); };
+      const int vrow = vc_ld * 8 + d;
+      if constexpr (TG == 4) {
+        const uint32_t lo = el(0) | (el(1) << 16);
+        const uint32_t hi2 = el(2) | (el(3) << 16);
+        *reinterpret_cast<u32x2_t*>(s_v + L::v_off(vrow, pos)) = (u32x2_t){lo, hi2};
+      } else {
+        *reinterpret_cast<uint32_t*>(s_v + L::v_off(vrow, pos)) = el(0) | (el(1) << 16);
+      }
+    }
+  };
+
+  // ---- accumulators --------------------------------------------------------------------
+  f32x16_t oacc[2][DB];
+  float m[2], lsum[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    m[j] = -INFINITY;
+    lsum[j] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[j][db] = (f32x16_t){};
+  }
+
+  const float c = p.scale_log2;
+  if (kv_end > 0) load_tile(0);
+  for (int k0 = 0; k0 < kv_end; k0 += kBN) {
+    store_tile();
+    __syncthreads();
+    const int k1 = k0 + kBN;
+    if (k1 < kv_end) {
+      // restage page ids when the next tile leaves the staged window
+      if ((((min(k1 + kBN, kv_end) - 1) >> p.block_shift) - tbl_base) >= kTableChunk) {
+        // all waves have stored their previous loads; the window is only read by loads
+        __syncthreads();
+        tbl_base = k1 >> p.block_shift;
+        for (int i = tid; i < kTableChunk; i += kThreads)
+          s_tbl[i] = table[min(tbl_base + i, last_page)];
+        __syncthreads();
+      }
+      load_tile(k1);
+    }
+    if (k0 < wmax) {
+      // ---- S^T = K Q^T for the wave's two column blocks ------------------------------
+      f32x16_t sacc[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) sacc[j][tb] = (f32x16_t){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(s_k + L::k_off(tb * 32 + lc, ks * 2 + hl));
+#pragma unroll
+          for (int j = 0; j < 2; ++j) sacc[j][tb] = Mfma<T>::run(a, qf[j][ks], sacc[j][tb]);
+        }
+      }
+      // ---- online softmax (lane = one query row of each column block) ---------------
+      const bool need_mask = k0 + kBN > wmin;
+      float x[2][2][16];
+      bool grow = false;
+      float tmax[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float v = sacc[j][tb][i] * c;
+            if (need_mask) {
+              const int tok = k0 + tb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+              v = tok < vis[j] ? v : -INFINITY;
+            }
+            x[j][tb][i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        tmax[j] = mx;
+        grow |= mx > m[j] + kLazy;
+      }
+      if (__builtin_expect(__any(grow), 0)) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float mn = fmaxf(m[j], tmax[j]);
+          const float alpha = (m[j] == -INFINITY) ? 0.f : fast_exp2(m[j] - mn);
+          lsum[j] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[j][db] *= alpha;
+          m[j] = mn;
+        }
+      }
+      // probabilities -> packed B fragments of O^T = V^T P^T
+      u32x4_t pf[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float ls = 0.f;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            float pr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              pr[e] = fast_exp2(x[j][tb][h2 * 8 + e] - m[j]);
+              ls += pr[e];
+            }
+            pf[j][tb * 2 + h2] = (u32x4_t){pack2(T{}, pr[0], pr[1]), pack2(T{}, pr[2], pr[3]),
+                                           pack2(T{}, pr[4], pr[5]), pack2(T{}, pr[6], pr[7])};
+          }
+        lsum[j] += ls;
+      }
+      // ---- O^T += V^T P^T --------------------------------------------------------------
+#pragma unroll
+      for (int ks = 0; ks < kBN / 16; ++ks) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4_t a =
+              *reinterpret_cast<const u32x4_t*>(s_v + L::v_off(db * 32 + lc, ks * 16 + hl * 8));
+#pragma unroll
+          for (int j = 0; j < 2; ++j) oacc[j][db] = Mfma<T>::run(a, pf[j][ks], oacc[j][db]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- normalise and write O (lane: one row, 4 runs of 4 dims per 32-dim block) -------
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float lt = lsum[j] + __shfl_xor(lsum[j], 32, 64);
+    const int row = rbase[j] + lc;
+    if (!hvalid[j] || row >= qn) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    S* op = reinterpret_cast<S*>(p.out) + ((int64_t)(q0 + row) * p.H + head[j]) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + g4 * 8 + hl * 4;
+        const f32x16_t& o = oacc[j][db];
+        *reinterpret_cast<u32x2_t*>(op + d0) =
+            (u32x2_t){pack2(T{}, o[g4 * 4 + 0] * inv, o[g4 * 4 + 1] * inv),
+                      pack2(T{}, o[g4 * 4 + 2] * inv, o[g4 * 4 + 3] * inv)};
+      }
+  }
+}
+
+int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+}  // namespace
+
+bool prefill_mfma_supported(int dtype, int head_dim) {
+  return (dtype == kBF16 || dtype == kF16) && (head_dim == 64 || head_dim == 128);
+}
+
+hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
+  if (!prefill_mfma_supported(a.dtype, a.head_dim)) return hipErrorNotSupported;
+  if (a.num_tokens == 0 || a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
+  PrefillParams p{};
+  p.out = a.out;
+  p.query = a.query;
+  p.cu_q = a.cu_seqlens_q;
+  p.seq_lens = a.seq_lens;
+  p.kc = a.key_cache;
+  p.vc = a.value_cache;
+  p.block_stride = a.block_stride;
+  p.block_tables = a.block_tables;
+  p.mb = a.max_blocks_per_seq;
+  p.S = a.num_seqs;
+  p.H = a.num_heads;
+  p.Hkv = a.num_kv_heads;
+  p.g = a.num_heads / a.num_kv_heads;
+  p.block_shift = log2_exact(a.block_size);
+  p.mask = a.mask;
+  p.span = a.span_len;
+  int hw = 1;
+  while (hw * 2 <= p.g && hw < 8) hw *= 2;
+  p.hw = hw;
+  p.rb_log2 = log2_exact(8 / hw);
+  p.head_groups = (p.g + hw - 1) / hw;
+  const int wg_rows = 32 * (8 / hw);
+  p.qtiles = (a.max_q_len + wg_rows - 1) / wg_rows;
+  const int64_t nb = (int64_t)p.qtiles * p.head_groups * p.Hkv * p.S;
+  if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+  p.nblocks = (int)nb;
+  p.scale_log2 = a.scale * kLog2e;
+  const int grid = ((p.nblocks + 7) / 8) * 8;
+  if (a.dtype == kBF16) {
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 128>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 64>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else {
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((prefill_mfma_kernel<F16, 128>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<F16, 64>), dim3(grid), dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace pkv
