@@ -244,7 +244,7 @@ int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_
   a.max_q_len = max_q_len;
   a.max_seq_len = max_seq_len;
   a.dtype = (int)dtype;
-  if (pkv::prefill_mfma_supported((int)dtype, head_dim))
+  if (pkv::prefill_mfma_supported((int)dtype, head_dim, scale))
     return launched(pkv::launch_prefill_mfma(a, (hipStream_t)stream), "pkv_paged_attention_prefill");
   return launched(pkv::launch_prefill_valu(a, (hipStream_t)stream), "pkv_paged_attention_prefill");
 }

@@ -77,6 +77,6 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, hipStream_t 
 // Returns hipErrorNotSupported when no MFMA variant covers the shape.
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_valu(const AttnArgs& a, hipStream_t stream);
-bool prefill_mfma_supported(int dtype, int head_dim);
+bool prefill_mfma_supported(int dtype, int head_dim, float scale);
 
 }  // namespace pkv

@@ -6,10 +6,10 @@
 // visible keys of the sequence owning row t, kv head h / (H / Hkv).
 //
 // How:
-//  * a workgroup (4 waves) owns one sequence, one kv head, a group of HW query heads of
-//    that kv head and 32*RB consecutive query rows, with HW * RB = 8 column blocks of
-//    (one head, 32 rows); each wave computes two column blocks, so the K/V tiles it
-//    reads from LDS feed 64 query columns;
+//  * a workgroup (8 waves, two per SIMD) owns one sequence, one kv head, a group of HW
+//    query heads of that kv head and 32*RB consecutive query rows, with HW * RB = 8
+//    column blocks of (one head, 32 rows), one per wave.  Two waves per SIMD let the
+//    hardware overlap one wave's MFMA with the other's softmax and LDS traffic;
 //  * keys are visited in tiles of 64.  K and V rows are gathered through the block table
 //    (page ids staged in LDS) with 16-byte loads into registers one tile ahead, then
 //    written to LDS: K row-major, V transposed (dims x tokens); both XOR-swizzled so the
@@ -29,7 +29,7 @@ namespace pkv {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;          // waves per workgroup: 2 per SIMD
 constexpr int kBN = 64;            // keys per tile
 constexpr int kTableChunk = 1024;  // page ids staged in LDS at a time
 constexpr float kLazy = 8.0f;
@@ -94,16 +94,16 @@ __device__ __forceinline__ int vt_pos(int t) {
   return (t & ~15) | (swapped << 2) | (t & 3);
 }
 
-template <typename T, int D>
-__global__ void __launch_bounds__(kThreads)
+template <typename T, int D, int NW>
+__global__ void __launch_bounds__(NW * 64)
 prefill_mfma_kernel(const PrefillParams p) {
+  constexpr int NT = NW * 64;         // threads
+  constexpr int NCB = 8 / NW;         // column blocks per wave
   using L = Lds<D>;
   constexpr int NC = L::NC;
   constexpr int KS = D / 16;          // k-steps of the QK^T product
   constexpr int DB = D / 32;          // 32-dim blocks of O^T
-  constexpr int KROWS = kThreads / NC;           // K rows loaded per pass
-  constexpr int KLOADS = kBN / KROWS;            // K vectors per thread
-  constexpr int TG = D / 32;                     // tokens per thread for V (2 or 4)
+  constexpr int TG = kBN * (D / 8) / NT;         // tokens per thread (1, 2 or 4)
   __shared__ __align__(16) uint8_t s_k[L::KBYTES];
   __shared__ __align__(16) uint8_t s_v[L::VBYTES];
   __shared__ int32_t s_tbl[kTableChunk];
@@ -137,11 +137,11 @@ prefill_mfma_kernel(const PrefillParams p) {
   const int ctx = Ls - qn;
 
   // ---- this wave's two column blocks ------------------------------------------------
-  int head[2], rbase[2], vis[2];
-  bool hvalid[2];
+  int head[NCB], rbase[NCB], vis[NCB];
+  bool hvalid[NCB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int cb = wv * 2 + j;
+  for (int j = 0; j < NCB; ++j) {
+    const int cb = wv * NCB + j;
     const int hw_i = cb % p.hw;
     const int rb_i = cb / p.hw;
     const int hin = hgrp * p.hw + hw_i;          // head index inside the kv group
@@ -151,21 +151,25 @@ prefill_mfma_kernel(const PrefillParams p) {
     const int row = min(rbase[j] + lc, qn - 1);  // rows past the chunk repeat the last one
     vis[j] = visible_end(p.mask, ctx + row, Ls, p.span);
   }
-  int wmax = max(vis[0], vis[1]), wmin = min(vis[0], vis[1]);
+  // smallest visible end over the wave's rows: tiles below it need no mask.  Tiles that
+  // no row of the wave sees are still computed: their probabilities are exactly 0
+  // (every row saw key 0 in the first tile, so the running max is finite), and the
+  // accumulators stay free of branch copies.
+  int wmin = vis[0];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    wmax = max(wmax, __shfl_xor(wmax, off, 64));
-    wmin = min(wmin, __shfl_xor(wmin, off, 64));
-  }
+  for (int j = 1; j < NCB; ++j) wmin = min(wmin, vis[j]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) wmin = min(wmin, __shfl_xor(wmin, off, 64));
+  wmin = __builtin_amdgcn_readfirstlane(wmin);
   // keys the whole workgroup needs: the last row of its tile sees the most
   const int last_row = min(row0 + wg_rows, qn) - 1;
   const int kv_end = visible_end(p.mask, ctx + last_row, Ls, p.span);
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[row lc][dims ks*16+hl*8..+8]
   using S = typename T::storage;
-  u32x4_t qf[2][KS];
+  u32x4_t qf[NCB][KS];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NCB; ++j) {
     const int row = min(rbase[j] + lc, qn - 1);
     const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
         reinterpret_cast<const S*>(p.query) + ((int64_t)(q0 + row) * p.H + head[j]) * D);
@@ -177,37 +181,40 @@ prefill_mfma_kernel(const PrefillParams p) {
   const int32_t* table = p.block_tables + (int64_t)s * p.mb;
   const int last_page = (kv_end - 1) >> p.block_shift;
   int tbl_base = 0;
-  for (int i = tid; i < kTableChunk; i += kThreads) s_tbl[i] = table[min(i, last_page)];
+  for (int i = tid; i < kTableChunk; i += NT) s_tbl[i] = table[min(i, last_page)];
   __syncthreads();
 
   // ---- K / V tile loads into registers (clamped to the last key: finite data) -------
-  const int64_t row_elems = (int64_t)p.Hkv * D;
-  const int64_t head_off = (int64_t)kvh * D;
+  // Thread (token group vg, 8-dim chunk vc) loads K and V of the TG tokens vg*TG.. for
+  // dims vc*8..+8: one block-id lookup serves both tensors, 16 lanes read one 256-byte
+  // row segment, and V arrives ready for its transposed store.
+  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
+  const uint32_t head_bytes = (uint32_t)kvh * D * 2;
+  const uint64_t blk_bytes = (uint64_t)p.block_stride * 2;
   const int bmask = (1 << p.block_shift) - 1;
-  const int kc_ld = tid % NC;
-  const int kr_ld = tid / NC;
-  const int vc_ld = tid % NC;               // 8-dim chunk for V
-  const int vg_ld = tid / NC;               // token group of TG tokens for V
-  u32x4_t kreg[KLOADS], vreg[TG];
+  const int vc_ld = tid % NC;               // 8-dim chunk
+  const int vg_ld = tid / NC;               // token group of TG tokens
+  u32x4_t kreg[TG], vreg[TG];
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.kc);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.vc);
 
   // keys past kv_end (seen by no row of this workgroup) re-read key kv_end-1: finite
   // data whose page id is inside the staged window
-  auto row_ptr = [&](const void* base, int tok) -> const u32x4_t* {
-    const int pos = min(tok, kv_end - 1);
-    const int64_t blk = s_tbl[(pos >> p.block_shift) - tbl_base];
-    return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const S*>(base) + blk * p.block_stride +
-                                            (int64_t)(pos & bmask) * row_elems + head_off);
-  };
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) kreg[i] = row_ptr(p.kc, k0 + kr_ld + i * KROWS)[kc_ld];
-#pragma unroll
-    for (int i = 0; i < TG; ++i) vreg[i] = row_ptr(p.vc, k0 + vg_ld * TG + i)[vc_ld];
+    for (int i = 0; i < TG; ++i) {
+      const int pos = min(k0 + vg_ld * TG + i, kv_end - 1);
+      const uint32_t blk = (uint32_t)s_tbl[(pos >> p.block_shift) - tbl_base];
+      const uint64_t off = (uint64_t)blk * blk_bytes +
+                           ((uint32_t)(pos & bmask) * row_bytes + head_bytes + vc_ld * 16u);
+      kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
+      vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+    }
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i)
-      *reinterpret_cast<u32x4_t*>(s_k + L::k_off(kr_ld + i * KROWS, kc_ld)) = kreg[i];
+    for (int i = 0; i < TG; ++i)
+      *reinterpret_cast<u32x4_t*>(s_k + L::k_off(vg_ld * TG + i, vc_ld)) = kreg[i];
     // transpose TG tokens x 8 dims into 8 dims x TG tokens
     const int pos = vt_pos(vg_ld * TG);
 #pragma unroll
@@ -220,17 +227,19 @@ prefill_mfma_kernel(const PrefillParams p) {
         const uint32_t lo = el(0) | (el(1) << 16);
         const uint32_t hi2 = el(2) | (el(3) << 16);
         *reinterpret_cast<u32x2_t*>(s_v + L::v_off(vrow, pos)) = (u32x2_t){lo, hi2};
-      } else {
+      } else if constexpr (TG == 2) {
         *reinterpret_cast<uint32_t*>(s_v + L::v_off(vrow, pos)) = el(0) | (el(1) << 16);
+      } else {
+        *reinterpret_cast<uint16_t*>(s_v + L::v_off(vrow, pos)) = (uint16_t)el(0);
       }
     }
   };
 
   // ---- accumulators --------------------------------------------------------------------
-  f32x16_t oacc[2][DB];
-  float m[2], lsum[2];
+  f32x16_t oacc[NCB][DB];
+  float m[NCB], lsum[NCB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NCB; ++j) {
     m[j] = -INFINITY;
     lsum[j] = 0.f;
 #pragma unroll
@@ -249,55 +258,55 @@ prefill_mfma_kernel(const PrefillParams p) {
         // all waves have stored their previous loads; the window is only read by loads
         __syncthreads();
         tbl_base = k1 >> p.block_shift;
-        for (int i = tid; i < kTableChunk; i += kThreads)
+        for (int i = tid; i < kTableChunk; i += NT)
           s_tbl[i] = table[min(tbl_base + i, last_page)];
         __syncthreads();
       }
       load_tile(k1);
     }
-    if (k0 < wmax) {
+    {  // every wave computes every tile of the workgroup (see the note on wmin)
       // ---- S^T = K Q^T for the wave's two column blocks ------------------------------
-      f32x16_t sacc[2][2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) sacc[j][tb] = (f32x16_t){};
+      f32x16_t sacc[NCB][2];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           const u32x4_t a = *reinterpret_cast<const u32x4_t*>(s_k + L::k_off(tb * 32 + lc, ks * 2 + hl));
 #pragma unroll
-          for (int j = 0; j < 2; ++j) sacc[j][tb] = Mfma<T>::run(a, qf[j][ks], sacc[j][tb]);
+          for (int j = 0; j < NCB; ++j)
+            sacc[j][tb] = Mfma<T>::run(a, qf[j][ks], ks == 0 ? (f32x16_t){} : sacc[j][tb]);
         }
       }
       // ---- online softmax (lane = one query row of each column block) ---------------
-      const bool need_mask = k0 + kBN > wmin;
-      float x[2][2][16];
-      bool grow = false;
-      float tmax[2];
+      // keys a row cannot see get -inf (only tiles that cross some row's visible end)
+      if (k0 + kBN > wmin) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NCB; ++j)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int tok = k0 + tb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+              if (tok >= vis[j]) sacc[j][tb][i] = -INFINITY;
+            }
+      }
+      // row max on raw scores (scale > 0 on this path), scaled to log2 units
+      bool grow = false;
+      float tmax[NCB];
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) {
         float mx = -INFINITY;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float v = sacc[j][tb][i] * c;
-            if (need_mask) {
-              const int tok = k0 + tb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-              v = tok < vis[j] ? v : -INFINITY;
-            }
-            x[j][tb][i] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[j][tb][i], sacc[j][tb][i + 1]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
         tmax[j] = mx;
         grow |= mx > m[j] + kLazy;
       }
       if (__builtin_expect(__any(grow), 0)) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NCB; ++j) {
           const float mn = fmaxf(m[j], tmax[j]);
           const float alpha = (m[j] == -INFINITY) ? 0.f : fast_exp2(m[j] - mn);
           lsum[j] *= alpha;
@@ -307,9 +316,9 @@ prefill_mfma_kernel(const PrefillParams p) {
         }
       }
       // probabilities -> packed B fragments of O^T = V^T P^T
-      u32x4_t pf[2][4];
+      u32x4_t pf[NCB][4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NCB; ++j) {
         float ls = 0.f;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
@@ -318,7 +327,7 @@ prefill_mfma_kernel(const PrefillParams p) {
             float pr[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              pr[e] = fast_exp2(x[j][tb][h2 * 8 + e] - m[j]);
+              pr[e] = fast_exp2(__builtin_fmaf(sacc[j][tb][h2 * 8 + e], c, -m[j]));
               ls += pr[e];
             }
             pf[j][tb * 2 + h2] = (u32x4_t){pack2(T{}, pr[0], pr[1]), pack2(T{}, pr[2], pr[3]),
@@ -334,7 +343,7 @@ prefill_mfma_kernel(const PrefillParams p) {
           const u32x4_t a =
               *reinterpret_cast<const u32x4_t*>(s_v + L::v_off(db * 32 + lc, ks * 16 + hl * 8));
 #pragma unroll
-          for (int j = 0; j < 2; ++j) oacc[j][db] = Mfma<T>::run(a, pf[j][ks], oacc[j][db]);
+          for (int j = 0; j < NCB; ++j) oacc[j][db] = Mfma<T>::run(a, pf[j][ks], oacc[j][db]);
         }
       }
     }
@@ -343,7 +352,7 @@ prefill_mfma_kernel(const PrefillParams p) {
 
   // ---- normalise and write O (lane: one row, 4 runs of 4 dims per 32-dim block) -------
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NCB; ++j) {
     const float lt = lsum[j] + __shfl_xor(lsum[j], 32, 64);
     const int row = rbase[j] + lc;
     if (!hvalid[j] || row >= qn) continue;
@@ -370,12 +379,13 @@ int log2_exact(int x) {
 
 }  // namespace
 
-bool prefill_mfma_supported(int dtype, int head_dim) {
-  return (dtype == kBF16 || dtype == kF16) && (head_dim == 64 || head_dim == 128);
+bool prefill_mfma_supported(int dtype, int head_dim, float scale) {
+  // the row max is taken on raw scores, which needs a positive scale
+  return (dtype == kBF16 || dtype == kF16) && (head_dim == 64 || head_dim == 128) && scale > 0.f;
 }
 
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
-  if (!prefill_mfma_supported(a.dtype, a.head_dim)) return hipErrorNotSupported;
+  if (!prefill_mfma_supported(a.dtype, a.head_dim, a.scale)) return hipErrorNotSupported;
   if (a.num_tokens == 0 || a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
   PrefillParams p{};
   p.out = a.out;
@@ -408,14 +418,14 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
   const int grid = ((p.nblocks + 7) / 8) * 8;
   if (a.dtype == kBF16) {
     if (a.head_dim == 128)
-      hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 128>), dim3(grid), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 128, kWaves>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
     else
-      hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 64>), dim3(grid), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 64, kWaves>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
   } else {
     if (a.head_dim == 128)
-      hipLaunchKernelGGL((prefill_mfma_kernel<F16, 128>), dim3(grid), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((prefill_mfma_kernel<F16, 128, kWaves>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
     else
-      hipLaunchKernelGGL((prefill_mfma_kernel<F16, 64>), dim3(grid), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((prefill_mfma_kernel<F16, 64, kWaves>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
   }
   return hipGetLastError();
 }
