@@ -122,7 +122,7 @@ def run_decode_step_bench(w, steps, warmup):
     nk, nv, ns = d.key[ni].contiguous(), d.value[ni].contiguous(), d.slots[ni].contiguous()
     out = torch.empty_like(d.query)
     wsb = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, w.max_seq_len)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
 
     def step(tw=None, ts=None):
         e0 = ts.start() if ts else None
@@ -163,7 +163,7 @@ def run_attention_bench(w, kind, steps, warmup, flush=False):
     out = torch.empty_like(d.query)
     if kind == "decode":
         wsb = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, w.max_seq_len)
-        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
         call = lambda: B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens,
                                                 w.scale, w.max_seq_len, ws if wsb else None)
     else:

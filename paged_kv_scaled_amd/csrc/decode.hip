@@ -41,7 +41,8 @@ constexpr int kDecodeThreads = 256;
 constexpr int kWavesPerBlock = kDecodeThreads / kWave;
 constexpr float kLazyRescale = 8.0f;   // log2 units
 constexpr int kStreamMaxSeqs = 1024;   // stream mode scans seq_lens in every wave
-constexpr int kStreamWaves = 4096;     // waves of the stream grid (all head groups)
+constexpr int kStreamWaves = 2048;     // waves of the stream grid (all head groups): one round
+                                       // at two waves per SIMD on 256 CUs
 constexpr int kStreamMinRange = 64;    // shortest range, keys
 
 template <typename T, int D>
@@ -513,6 +514,7 @@ __device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, i
   auto slot_of = [&](int j) -> int64_t {
     return (int64_t)h * slots_per_head + (j == 0 ? slot0 : slot1 + (int64_t)(j - 1) * slot_step);
   };
+  // the (max, sum) pairs are read by all lanes at once, 64 partials per pass
   float M = -INFINITY;
   for (int j = lane; j < n; j += kWave) M = fmaxf(M, p.ws_ml[slot_of(j) * 2]);
 #pragma unroll
@@ -521,18 +523,30 @@ __device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, i
 #pragma unroll
   for (int i = 0; i < DPL; ++i) num[i] = 0.f;
   float den = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const int64_t sl = slot_of(j);
-    const float mj = p.ws_ml[sl * 2];
-    const float w = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
-    den += w * p.ws_ml[sl * 2 + 1];
-    const float* acc = p.ws_acc + sl * D;
+  for (int j0 = 0; j0 < n; j0 += kWave) {
+    const int jl = j0 + lane;
+    float w = 0.f;
+    if (jl < n) {
+      const int64_t sl = slot_of(jl);
+      const float mj = p.ws_ml[sl * 2];
+      w = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
+      den += w * p.ws_ml[sl * 2 + 1];
+    }
+    const int cnt = min(kWave, n - j0);
+    // the accumulator rows are independent loads: four in flight per lane
+#pragma unroll 4
+    for (int k = 0; k < cnt; ++k) {
+      const float wk = __shfl(w, k, kWave);
+      const float* acc = p.ws_acc + slot_of(j0 + k) * D;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      const int d = lane + i * kWave;
-      if (d < D) num[i] += w * acc[d];
+      for (int i = 0; i < DPL; ++i) {
+        const int d = lane + i * kWave;
+        if (d < D) num[i] += wk * acc[d];
+      }
     }
   }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) den += shfl_xor_f(den, off);
   store_row<T, D>(p, sh, lane, num, den > 0.f ? 1.f / den : 0.f);
 }
 
@@ -571,16 +585,21 @@ decode_merge_stream_kernel(const DecodeParams p) {
     store_row<T, D>(p, sh, lane, zero, 0.f);
     return;
   }
-  const int64_t total = stream_total(p, lane);
-  const int64_t R = stream_range_len(total, p.nranges);
-  // start of sequence s on the concatenated axis
-  int64_t P = 0;
-  for (int c0 = 0; c0 < s; c0 += kWave) {
-    int x = (c0 + lane < s) ? p.seq_lens[c0 + lane] : 0;
+  // one pass over the lengths: the batch total and the start P of sequence s
+  int64_t total = 0, P = 0;
+  for (int c0 = 0; c0 < p.S; c0 += kWave) {
+    const int x = (c0 + lane < p.S) ? p.seq_lens[c0 + lane] : 0;
+    int before = (c0 + lane < s) ? x : 0;
+    int all = x;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
-    P += x;
+    for (int off = 1; off < kWave; off <<= 1) {
+      all += __shfl_xor(all, off, kWave);
+      before += __shfl_xor(before, off, kWave);
+    }
+    total += all;
+    P += before;
   }
+  const int64_t R = stream_range_len(total, p.nranges);
   const int64_t r0 = P / R, r1 = (P + L - 1) / R;
   if (r0 == r1) return;
   const int64_t slot0 = r0 * 2 + ((r0 * R < P) ? 1 : 0);

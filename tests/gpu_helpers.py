@@ -81,7 +81,7 @@ class Dev:
         out = out if out is not None else torch.empty_like(self.query)
         ws_bytes = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
                                            w.max_seq_len)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
         B.paged_attention_decode(out, self.query, self.kc, self.vc, self.tables, self.seq_lens,
                                  w.scale, w.max_seq_len, ws if ws_bytes else None)
         return out

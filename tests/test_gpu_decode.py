@@ -129,3 +129,38 @@ def test_decode_rejects_small_workspace(gpu):
     assert e.value.code == B.PKV_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert torch.all(out == 3.0)
+
+
+def test_decode_shared_workspace_back_to_back(gpu):
+    """Decode batches of different shape on one workspace, one after another: nothing a
+    call leaves in the workspace changes the next call's result."""
+    w1 = wl.decode_batch(seed=15, num_seqs=12, lo=300, hi=4096)
+    w2 = wl.decode_batch(seed=16, num_seqs=5, lo=1000, hi=6000)
+    need = max(B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                       w.block_size, w.max_seq_len) for w in (w1, w2))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")   # garbage, not zeros
+    for w in (w1, w2, w1):
+        d = Dev(w)
+        d.write_all()
+        out = torch.empty_like(d.query)
+        B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens, w.scale,
+                                 w.max_seq_len, ws)
+        torch.cuda.synchronize()
+        want, _ = ref.workload_attention(w)
+        compare(as_f64(out), want, w.dtype, w.name)
+
+
+def test_decode_all_empty_batch_with_long_hint(gpu):
+    """seq_lens all 0 with a long max_seq_len hint (the long-context work split): zeros."""
+    lens = np.zeros(6, np.int32)
+    w = wl.build("all_empty", 24, "bf16", lens, lens, 8, 2, 128, 16, wl.MASK_NONE, decode=True,
+                 max_blocks_per_seq=512)
+    q = wl.round_to_storage(np.random.default_rng(4).standard_normal((6, 8, 128)).astype(np.float32), "bf16")
+    w.query = q
+    d = Dev(w)
+    out = torch.full_like(d.query, 5.0)
+    need = B.decode_workspace_size(6, 8, 2, 128, 16, 8192)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens, w.scale, 8192, ws)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
