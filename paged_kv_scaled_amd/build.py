@@ -29,8 +29,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
 
 # Per-file code-generation options.  The MFMA prefill kernel keeps its accumulators in
 # VGPRs (VGPR-form MFMA): with the default AGPR form the compiler copies the output
-# accumulator between register files on every key tile.
-EXTRA = {"prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# accumulator between register files on every key tile.  It also runs with the IEEE mode
+# bit off and NaN-free inputs assumed: in IEEE mode every fmax operand that comes out of an
+# MFMA is first canonicalised (one extra VALU op per score), and NaN keys or queries give
+# undefined results either way.
+EXTRA = {"prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -399,10 +399,11 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 }
 
 // Total keys of the batch, and the range length every stream kernel derives from it.
-__device__ __forceinline__ int64_t stream_total(const DecodeParams& p, int lane) {
+// len0: this lane's entry of the first 64 lengths (0 past the batch), loaded once.
+__device__ __forceinline__ int64_t stream_total(const DecodeParams& p, int lane, int len0) {
   int64_t total = 0;
   for (int c0 = 0; c0 < p.S; c0 += kWave) {
-    int x = (c0 + lane < p.S) ? p.seq_lens[c0 + lane] : 0;
+    int x = c0 == 0 ? len0 : ((c0 + lane < p.S) ? p.seq_lens[c0 + lane] : 0);
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
     total += x;
@@ -417,13 +418,13 @@ __device__ __forceinline__ int64_t stream_range_len(int64_t total, int nranges) 
 
 // First sequence whose keys reach past position x of the concatenated key axis, and the
 // position where that sequence starts.
-__device__ __forceinline__ void stream_locate(const DecodeParams& p, int64_t x, int lane, int& s0,
-                                              int64_t& start0) {
+__device__ __forceinline__ void stream_locate(const DecodeParams& p, int64_t x, int lane, int len0,
+                                              int& s0, int64_t& start0) {
   int count = 0;
   int64_t carry = 0, before = 0;
   for (int c0 = 0; c0 < p.S; c0 += kWave) {
     const bool in = c0 + lane < p.S;
-    const int Ls = in ? p.seq_lens[c0 + lane] : 0;
+    const int Ls = c0 == 0 ? len0 : (in ? p.seq_lens[c0 + lane] : 0);
     const int64_t incl = carry + wave_inclusive_scan(Ls, lane);
     const bool done = in && incl <= x;                 // sequence ends at or before x
     count += __popcll(__ballot(done));
@@ -451,7 +452,8 @@ decode_stream_kernel(const DecodeParams p) {
   const int HG = p.Hkv * p.groups_per_kv;
   const int hg = (int)(wave % HG);
   const int r = (int)(wave / HG);
-  const int64_t total = stream_total(p, lane);
+  const int len0 = lane < p.S ? p.seq_lens[lane] : 0;
+  const int64_t total = stream_total(p, lane, len0);
   const int64_t R = stream_range_len(total, p.nranges);
   const int64_t lo = (int64_t)r * R;
   const int64_t hi = min(total, lo + R);
@@ -461,7 +463,7 @@ decode_stream_kernel(const DecodeParams p) {
   const int nh = min(HPW, p.g - sub * HPW);
   int s;
   int64_t P;
-  stream_locate(p, lo, lane, s, P);
+  stream_locate(p, lo, lane, len0, s, P);
   bool first = true;
   for (; s < p.S && P < hi; ++s) {
     const int L = p.seq_lens[s];
@@ -504,53 +506,62 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int64_t sh, int
   }
 }
 
-// Combine the partials of one head: slots `first + j * stride`, j < n.
+// Combine the n partials (acc, m, l) of one head with the log-sum-exp rule: slot0 for
+// partial 0, slot1 + (j - 1) * slot_step for partial j > 0.  The partials are taken in
+// batches of kMergeBatch whose (m, l) pairs and accumulator rows are all loaded before any
+// is used; the running max moves between batches with a rescale of the sums.
+constexpr int kMergeBatch = 8;
+
 template <typename T, int D>
 __device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, int h,
                                             int64_t slots_per_head, int n, int lane,
                                             int64_t slot0, int64_t slot1, int64_t slot_step) {
   constexpr int DPL = (D + kWave - 1) / kWave;
-  // slot of partial j: j == 0 -> slot0, else slot1 + (j - 1) * slot_step
   auto slot_of = [&](int j) -> int64_t {
     return (int64_t)h * slots_per_head + (j == 0 ? slot0 : slot1 + (int64_t)(j - 1) * slot_step);
   };
-  // the (max, sum) pairs are read by all lanes at once, 64 partials per pass
-  float M = -INFINITY;
-  for (int j = lane; j < n; j += kWave) M = fmaxf(M, p.ws_ml[slot_of(j) * 2]);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) M = fmaxf(M, shfl_xor_f(M, off));
-  float num[DPL];
+  float M = -INFINITY, den = 0.f, num[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) num[i] = 0.f;
-  float den = 0.f;
-  for (int j0 = 0; j0 < n; j0 += kWave) {
-    const int jl = j0 + lane;
-    float w = 0.f;
-    if (jl < n) {
-      const int64_t sl = slot_of(jl);
-      const float mj = p.ws_ml[sl * 2];
-      w = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
-      den += w * p.ws_ml[sl * 2 + 1];
-    }
-    const int cnt = min(kWave, n - j0);
-    // the accumulator rows are independent loads: four in flight per lane
-#pragma unroll 4
-    for (int k = 0; k < cnt; ++k) {
-      const float wk = __shfl(w, k, kWave);
-      const float* acc = p.ws_acc + slot_of(j0 + k) * D;
+  for (int j0 = 0; j0 < n; j0 += kMergeBatch) {
+    const int cnt = min(kMergeBatch, n - j0);
+    // lane k < cnt: (m, l) of partial j0 + k; every lane: its dims of each row (rows past
+    // cnt re-read the last one and get weight 0)
+    const int64_t my = slot_of(j0 + min(lane, cnt - 1));
+    float mj = p.ws_ml[my * 2], lj = p.ws_ml[my * 2 + 1];
+    float acc[kMergeBatch][DPL];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float* row = p.ws_acc + slot_of(j0 + min(k, cnt - 1)) * D;
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
         const int d = lane + i * kWave;
-        if (d < D) num[i] += wk * acc[d];
+        acc[k][i] = d < D ? row[d] : 0.f;
       }
     }
+    if (lane >= cnt) mj = -INFINITY;
+    float bm = mj;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) bm = fmaxf(bm, shfl_xor_f(bm, off));
+    const float Mn = fmaxf(M, bm);
+    const float alpha = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+    const float w = (mj == -INFINITY) ? 0.f : fast_exp2(mj - Mn);
+    den = den * alpha + w * lj;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) num[i] *= alpha;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float wk = __shfl(w, k, kWave);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) num[i] += wk * acc[k][i];
+    }
+    M = Mn;
   }
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) den += shfl_xor_f(den, off);
   store_row<T, D>(p, sh, lane, num, den > 0.f ? 1.f / den : 0.f);
 }
 
-// Split mode: one wave per (sequence, head) with more than one split.
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_merge_split_kernel(const DecodeParams p) {

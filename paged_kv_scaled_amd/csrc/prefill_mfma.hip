@@ -21,7 +21,8 @@
 //  * the probabilities stay where the S^T accumulator put them and are used directly as
 //    the B operand of O^T = V^T P^T: the V^T tile stores each 16-token group in the
 //    token order that accumulator layout implies;
-//  * tiles that a wave's rows cannot see are skipped; fully visible tiles skip the mask.
+//  * every wave computes every key tile of its workgroup (tiles past a row's visible end
+//    get probability 0); fully visible tiles skip the mask.
 #include "common.h"
 #include "kernels.h"
 
@@ -63,6 +64,11 @@ template <> struct Mfma<F16> {
   }
 };
 
+// (1, 1) in the storage type, for row sums by dot2
+template <typename T> __device__ __forceinline__ uint32_t kOnes2();
+template <> __device__ __forceinline__ uint32_t kOnes2<BF16>() { return 0x3F803F80u; }
+template <> __device__ __forceinline__ uint32_t kOnes2<F16>() { return 0x3C003C00u; }
+
 __device__ __forceinline__ int visible_end(int mask, int a, int L, int span) {
   if (mask == 1) return min(L, a + 1);
   if (mask == 2) return min(L, (a / span + 1) * span);
@@ -94,11 +100,12 @@ __device__ __forceinline__ int vt_pos(int t) {
   return (t & ~15) | (swapped << 2) | (t & 3);
 }
 
-template <typename T, int D, int NW>
-__global__ void __launch_bounds__(NW * 64)
+// kWaves waves per workgroup, one 32-column block each.
+template <typename T, int D>
+__global__ void __launch_bounds__(kWaves * 64)
 prefill_mfma_kernel(const PrefillParams p) {
-  constexpr int NT = NW * 64;         // threads
-  constexpr int NCB = 8 / NW;         // column blocks per wave
+  constexpr int NT = kWaves * 64;     // threads
+  constexpr int NCB = 1;              // column blocks per wave
   using L = Lds<D>;
   constexpr int NC = L::NC;
   constexpr int KS = D / 16;          // k-steps of the QK^T product
@@ -136,7 +143,7 @@ prefill_mfma_kernel(const PrefillParams p) {
   const int Ls = p.seq_lens[s];
   const int ctx = Ls - qn;
 
-  // ---- this wave's two column blocks ------------------------------------------------
+  // ---- this wave's column block -------------------------------------------------------
   int head[NCB], rbase[NCB], vis[NCB];
   bool hvalid[NCB];
 #pragma unroll
@@ -265,7 +272,7 @@ prefill_mfma_kernel(const PrefillParams p) {
       load_tile(k1);
     }
     {  // every wave computes every tile of the workgroup (see the note on wmin)
-      // ---- S^T = K Q^T for the wave's two column blocks ------------------------------
+      // ---- S^T = K Q^T for the wave's column block ------------------------------------
       f32x16_t sacc[NCB][2];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -281,14 +288,16 @@ prefill_mfma_kernel(const PrefillParams p) {
       // keys a row cannot see get -inf (only tiles that cross some row's visible end)
       if (k0 + kBN > wmin) {
 #pragma unroll
-        for (int j = 0; j < NCB; ++j)
+        for (int j = 0; j < NCB; ++j) {
+          // element i of token block tb holds key k0 + tb*32 + (i/4)*8 + hl*4 + i%4;
+          // compare its compile-time part against a per-lane threshold
+          const int thr = vis[j] - k0 - hl * 4;
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int tok = k0 + tb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-              if (tok >= vis[j]) sacc[j][tb][i] = -INFINITY;
-            }
+            for (int i = 0; i < 16; ++i)
+              if (tb * 32 + (i >> 2) * 8 + (i & 3) >= thr) sacc[j][tb][i] = -INFINITY;
+        }
       }
       // row max on raw scores (scale > 0 on this path), scaled to log2 units
       bool grow = false;
@@ -319,21 +328,23 @@ prefill_mfma_kernel(const PrefillParams p) {
       u32x4_t pf[NCB][4];
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
-        float ls = 0.f;
+        // the row sum uses the rounded pairs the P.V product uses (dot2 against ones)
+        float ls = lsum[j];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             float pr[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < 8; ++e)
               pr[e] = fast_exp2(__builtin_fmaf(sacc[j][tb][h2 * 8 + e], c, -m[j]));
-              ls += pr[e];
-            }
-            pf[j][tb * 2 + h2] = (u32x4_t){pack2(T{}, pr[0], pr[1]), pack2(T{}, pr[2], pr[3]),
-                                           pack2(T{}, pr[4], pr[5]), pack2(T{}, pr[6], pr[7])};
+            const u32x4_t q4 = (u32x4_t){pack2(T{}, pr[0], pr[1]), pack2(T{}, pr[2], pr[3]),
+                                         pack2(T{}, pr[4], pr[5]), pack2(T{}, pr[6], pr[7])};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) ls = dot2(T{}, q4[w], kOnes2<T>(), ls);
+            pf[j][tb * 2 + h2] = q4;
           }
-        lsum[j] += ls;
+        lsum[j] = ls;
       }
       // ---- O^T += V^T P^T --------------------------------------------------------------
 #pragma unroll
@@ -404,28 +415,25 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
   p.block_shift = log2_exact(a.block_size);
   p.mask = a.mask;
   p.span = a.span_len;
+  // kWaves column blocks per workgroup: HW heads of the kv group x RB row blocks
   int hw = 1;
-  while (hw * 2 <= p.g && hw < 8) hw *= 2;
+  while (hw * 2 <= p.g && hw < kWaves) hw *= 2;
   p.hw = hw;
-  p.rb_log2 = log2_exact(8 / hw);
+  p.rb_log2 = log2_exact(kWaves / hw);
   p.head_groups = (p.g + hw - 1) / hw;
-  const int wg_rows = 32 * (8 / hw);
-  p.qtiles = (a.max_q_len + wg_rows - 1) / wg_rows;
+  const int rows = 32 * (kWaves / hw);
+  p.qtiles = (a.max_q_len + rows - 1) / rows;
   const int64_t nb = (int64_t)p.qtiles * p.head_groups * p.Hkv * p.S;
   if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
   p.nblocks = (int)nb;
   p.scale_log2 = a.scale * kLog2e;
-  const int grid = ((p.nblocks + 7) / 8) * 8;
+  const dim3 grid(((p.nblocks + 7) / 8) * 8), block(kWaves * 64);
   if (a.dtype == kBF16) {
-    if (a.head_dim == 128)
-      hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 128, kWaves>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 64, kWaves>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+    if (a.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 128>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 64>), grid, block, 0, stream, p);
   } else {
-    if (a.head_dim == 128)
-      hipLaunchKernelGGL((prefill_mfma_kernel<F16, 128, kWaves>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((prefill_mfma_kernel<F16, 64, kWaves>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+    if (a.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_kernel<F16, 128>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_mfma_kernel<F16, 64>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
