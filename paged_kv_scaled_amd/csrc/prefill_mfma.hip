@@ -46,7 +46,7 @@ struct PrefillParams {
   const int32_t* block_tables;
   int32_t mb, S, H, Hkv, g, block_shift, mask, span;
   int32_t hw, rb_log2, head_groups, qtiles;   // WG tiling
-  int32_t nblocks;                            // total workgroups
+  int32_t ngroups;                            // (sequence, kv head, head group) groups
   float scale_log2;
 };
 
@@ -121,14 +121,19 @@ prefill_mfma_kernel(const PrefillParams p) {
   const int hl = lane >> 5;           // lane half
   const int lc = lane & 31;           // lane column
 
-  // ---- workgroup -> (sequence, kv head, head group, query tile), XCD-grouped --------
-  const int nb = p.nblocks;
+  // ---- workgroup -> (sequence, kv head, head group, query tile) ----------------------
+  // Workgroups go to the 8 XCDs round-robin (XCD = blockIdx % 8).  Group u = (sequence,
+  // kv head, head group) is dealt to XCD u % 8, and all query tiles of a group stay on
+  // its XCD (they read the same keys: one L2 holds them); the groups of one sequence
+  // spread over all XCDs, so a long sequence does not load one XCD only.  Inside a
+  // group the longest query tiles start first.
   const int bid = blockIdx.x;
-  const int per_xcd = (nb + 7) >> 3;
-  const int logical = (bid & 7) * per_xcd + (bid >> 3);
-  if (logical >= nb) return;
-  const int qt_rev = logical % p.qtiles;
-  int rest = logical / p.qtiles;
+  const int xcd = bid & 7;
+  const int slot = bid >> 3;
+  const int grp = (slot / p.qtiles) * 8 + xcd;
+  if (grp >= p.ngroups) return;
+  const int qt_rev = slot % p.qtiles;
+  int rest = grp;
   const int hgrp = rest % p.head_groups;
   rest /= p.head_groups;
   const int kvh = rest % p.Hkv;
@@ -201,13 +206,13 @@ prefill_mfma_kernel(const PrefillParams p) {
   const int bmask = (1 << p.block_shift) - 1;
   const int vc_ld = tid % NC;               // 8-dim chunk
   const int vg_ld = tid / NC;               // token group of TG tokens
-  u32x4_t kreg[TG], vreg[TG];
+  u32x4_t kra[TG], vra[TG], krb[TG], vrb[TG];   // two tiles in flight
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.kc);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.vc);
 
   // keys past kv_end (seen by no row of this workgroup) re-read key kv_end-1: finite
   // data whose page id is inside the staged window
-  auto load_tile = [&](int k0) {
+  auto load_tile = [&](int k0, u32x4_t (&kreg)[TG], u32x4_t (&vreg)[TG]) {
 #pragma unroll
     for (int i = 0; i < TG; ++i) {
       const int pos = min(k0 + vg_ld * TG + i, kv_end - 1);
@@ -218,7 +223,7 @@ prefill_mfma_kernel(const PrefillParams p) {
       vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const u32x4_t (&kreg)[TG], const u32x4_t (&vreg)[TG]) {
 #pragma unroll
     for (int i = 0; i < TG; ++i)
       *reinterpret_cast<u32x4_t*>(s_k + L::k_off(vg_ld * TG + i, vc_ld)) = kreg[i];
@@ -254,22 +259,23 @@ prefill_mfma_kernel(const PrefillParams p) {
   }
 
   const float c = p.scale_log2;
-  if (kv_end > 0) load_tile(0);
-  for (int k0 = 0; k0 < kv_end; k0 += kBN) {
-    store_tile();
+  // One key tile: its K/V registers (loaded two tiles earlier) go to LDS, the registers are
+  // refilled with the tile two ahead, then every wave computes on the LDS tile.  Two tiles
+  // in flight cover the gather latency when the keys come from HBM rather than L2.
+  auto tile_step = [&](int k0, u32x4_t (&kreg)[TG], u32x4_t (&vreg)[TG]) {
+    store_tile(kreg, vreg);
     __syncthreads();
-    const int k1 = k0 + kBN;
-    if (k1 < kv_end) {
-      // restage page ids when the next tile leaves the staged window
-      if ((((min(k1 + kBN, kv_end) - 1) >> p.block_shift) - tbl_base) >= kTableChunk) {
-        // all waves have stored their previous loads; the window is only read by loads
-        __syncthreads();
-        tbl_base = k1 >> p.block_shift;
+    const int k2 = k0 + 2 * kBN;
+    if (k2 < kv_end) {
+      // restage page ids when tile k2 leaves the staged window; the loads of the tile
+      // in between already took their page ids
+      if ((((min(k2 + kBN, kv_end) - 1) >> p.block_shift) - tbl_base) >= kTableChunk) {
+        tbl_base = k2 >> p.block_shift;
         for (int i = tid; i < kTableChunk; i += NT)
           s_tbl[i] = table[min(tbl_base + i, last_page)];
         __syncthreads();
       }
-      load_tile(k1);
+      load_tile(k2, kreg, vreg);
     }
     {  // every wave computes every tile of the workgroup (see the note on wmin)
       // ---- S^T = K Q^T for the wave's column block ------------------------------------
@@ -359,7 +365,17 @@ prefill_mfma_kernel(const PrefillParams p) {
       }
     }
     __syncthreads();
+  };
+  if (kv_end > 0) {
+    load_tile(0, kra, vra);
+    if (kBN < kv_end) load_tile(kBN, krb, vrb);
   }
+  int k0 = 0;
+  for (; k0 + kBN < kv_end; k0 += 2 * kBN) {
+    tile_step(k0, kra, vra);
+    tile_step(k0 + kBN, krb, vrb);
+  }
+  if (k0 < kv_end) tile_step(k0, kra, vra);
 
   // ---- normalise and write O (lane: one row, 4 runs of 4 dims per 32-dim block) -------
 #pragma unroll
@@ -423,11 +439,12 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
   p.head_groups = (p.g + hw - 1) / hw;
   const int rows = 32 * (kWaves / hw);
   p.qtiles = (a.max_q_len + rows - 1) / rows;
-  const int64_t nb = (int64_t)p.qtiles * p.head_groups * p.Hkv * p.S;
+  const int64_t ng = (int64_t)p.head_groups * p.Hkv * p.S;
+  const int64_t nb = (ng + 7) / 8 * 8 * p.qtiles;     // 8 XCDs x groups per XCD x tiles
   if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
-  p.nblocks = (int)nb;
+  p.ngroups = (int)ng;
   p.scale_log2 = a.scale * kLog2e;
-  const dim3 grid(((p.nblocks + 7) / 8) * 8), block(kWaves * 64);
+  const dim3 grid((unsigned)nb), block(kWaves * 64);
   if (a.dtype == kBF16) {
     if (a.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 128>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 64>), grid, block, 0, stream, p);
