@@ -7,7 +7,7 @@ from oracle import reference as ref
 from paged_kv_scaled_amd import binding as B
 from paged_kv_scaled_amd import workloads as wl
 
-from gpu_helpers import Dev, as_f64, compare
+from gpu_helpers import Dev, as_f64, compare, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -164,3 +164,26 @@ def test_decode_all_empty_batch_with_long_hint(gpu):
     B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens, w.scale, 8192, ws)
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+def test_smallseq_thd_zero_copy_view(gpu):
+    """K/V packed THD [sum s_kv, Hkv, D] used in place as a block_size-1 cache, with
+    block_tables[s][j] = cu_kv[s] + j: no scatter, the same decode kernel."""
+    w = wl.smallseq_varlen(num_seqs=500)
+    key = to_dev(w.key, w.dtype)
+    value = to_dev(w.value, w.dtype)
+    kc = key.view(-1, 1, w.num_kv_heads, w.head_dim)
+    vc = value.view(-1, 1, w.num_kv_heads, w.head_dim)
+    mb = int(w.seq_lens.max())
+    tables = np.zeros((w.num_seqs, mb), np.int32)
+    for s in range(w.num_seqs):
+        tables[s, :w.seq_lens[s]] = w.cu_seq_lens[s] + np.arange(w.seq_lens[s])
+    q = to_dev(w.query, w.dtype)
+    out = torch.empty_like(q)
+    need = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, 1, mb)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    B.paged_attention_decode(out, q, kc, vc, torch.from_numpy(tables).cuda(),
+                             torch.from_numpy(w.seq_lens).cuda(), w.scale, mb, ws if need else None)
+    torch.cuda.synchronize()
+    want, _ = ref.workload_attention(w)
+    compare(as_f64(out), want, w.dtype, "thd_view")

@@ -119,3 +119,35 @@ def test_prefill_rejects_bad_arguments_before_writing(gpu):
     assert e.value.code == B.PKV_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("block_size", [1, 2])
+def test_prefill_table_restage(gpu, block_size):
+    """Sequences of more than 1024 pages: the kernel restages its window of page ids in
+    LDS (every 1024 pages) while tiles are in flight; bf16, D 128 (MFMA path)."""
+    lens = np.array([2600, 1100, 2300], np.int32)
+    ql = np.array([500, 300, 96], np.int32)
+    w = wl.build("restage", 45 + block_size, "bf16", lens, ql, 8, 2, 128, block_size, wl.MASK_CAUSAL)
+    _run(w)
+
+
+def test_prefill_block_size_256(gpu):
+    """The largest block size: every tile lies inside one page."""
+    lens = np.array([700, 1500, 300], np.int32)
+    ql = np.array([700, 200, 33], np.int32)
+    w = wl.build("bs256", 47, "bf16", lens, ql, 16, 4, 128, 256, wl.MASK_CAUSAL)
+    _run(w)
+
+
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f16", 64)])
+def test_prefill_single_visible_key_is_exact(gpu, dtype, head_dim):
+    """Causal row 0 of a sequence without cached context sees one key: its output is that
+    key's V row bit for bit (weight 1, sum 1), on the MFMA path."""
+    lens = np.array([150, 77, 260], np.int32)
+    w = wl.build("single_key", 48, dtype, lens, lens, 8, 2, head_dim, 16, wl.MASK_CAUSAL)
+    got, _, _ = _run(w)
+    v = ref.widen(w.value, dtype)
+    for s in range(w.num_seqs):
+        r0 = w.cu_seqlens_q[s]
+        for h in range(w.num_heads):
+            assert np.array_equal(got[r0, h], v[w.cu_seq_lens[s], h // 4]), (s, h)
