@@ -232,7 +232,16 @@ def cpu_baseline(w, budget_s=15.0):
             if time.perf_counter() - t0 >= budget_s:
                 break
     el = time.perf_counter() - t0
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=round(passes * pass_bytes / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                host_cpu=model, host_cores_available=len(os.sched_getaffinity(0)),
                 sample=f"{passes} full passes over the decode batch ({w.num_seqs} sequences, "
                        f"{w.num_heads} heads), fp64 numpy, 1 BLAS thread, {el:.1f} s",
                 seconds=round(el, 2))
@@ -255,6 +264,42 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     del a, b
     torch.cuda.empty_cache()
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def gemm_ceiling(n=8192, reps=5):
+    """Achievable dense bf16 MFMA rate on this GPU: torch.matmul (hipBLASLt) on n x n x n
+    bf16, median of `reps` launches.  Context for the prefill fractions, not a target."""
+    import torch
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(2):
+        torch.matmul(a, b)
+    tm = Timer()
+    for _ in range(reps):
+        e = tm.start()
+        torch.matmul(a, b)
+        tm.stop(e)
+    ms = med(tm.ms())
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+
+
+def device_info():
+    """What the run was measured on: device properties, and the clocks rocm-smi reports
+    (None where the tool is unavailable)."""
+    import subprocess
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "memory_GB": round(pr.total_memory / 1e9, 1)}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        clk = [l.split(":", 2)[-1].strip() for l in r.stdout.splitlines() if "sclk" in l or "mclk" in l]
+        info["clocks"] = clk[:4] or None
+    except Exception:
+        info["clocks"] = None
+    return info
 
 
 def committed_traffic(kernel_file: str, profile: str):
@@ -284,7 +329,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibration-copy", action="store_true",
-                    help="also run a 1 GiB device copy (reference kernel for counter passes)")
+                    help="kept for old command lines: the 1 GiB device copy (the reference kernel "
+                         "of the counter passes) now always runs")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured copy and GEMM ceilings")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -351,7 +399,12 @@ def main():
         del wk
         torch.cuda.empty_cache()
 
-    copy_gbs = copy_calibration() if args.calibration_copy else None
+    copy_gbs = copy_calibration()
+    gemm_tf = None if args.no_ceilings else gemm_ceiling()
+    roofline["frac_of_measured_copy_ceiling"] = round(achieved / copy_gbs, 4) if copy_gbs else None
+    for name, e in result_wl.items():
+        if e.get("unit") == "TFLOP/s" and gemm_tf:
+            e["frac_of_measured_gemm_ceiling"] = round(e["value"] / gemm_tf, 4)
 
     cpu = None
     if not args.no_cpu:
@@ -382,8 +435,10 @@ def main():
         "workloads": result_wl,
         "step_us_event_median": round(med(r["step_ms"]) * 1e3, 2),
     }
-    if copy_gbs is not None:
-        line["copy_ceiling_GBps"] = copy_gbs
+    line["ceilings"] = {"copy_GBps": copy_gbs, "copy_note": "1 GiB device copy, read + write bytes",
+                        "bf16_gemm_TFLOPs": gemm_tf, "gemm_note": "torch.matmul 8192^3 bf16 (hipBLASLt)",
+                        "hbm_spec_GBps": HBM_PEAK_GBS, "bf16_spec_TFLOPs": BF16_PEAK_TFLOPS}
+    line["device"] = device_info()
     print(json.dumps(line), flush=True)
 
 

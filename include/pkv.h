@@ -43,7 +43,8 @@
  *   accumulators; probabilities are rounded to the input type for the
  *   probability-times-V products; output rounded to nearest even.
  *
- * Device-content preconditions (not checked, undefined behaviour if violated):
+ * Device-content preconditions (not checked by default, undefined behaviour if
+ * violated; pkv_set_device_checks(1) checks all but slot uniqueness on the GPU):
  *   slots in [0, num_blocks*block_size) or negative, unique within one call;
  *   block_tables entries in [0, num_blocks) for the blocks a sequence uses;
  *   seq_lens[s] <= max_blocks_per_seq*block_size and <= max_seq_len;
@@ -180,6 +181,38 @@ int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_
                                 int32_t block_size, float scale, pkv_mask_mode mask,
                                 int32_t span_len, int32_t max_q_len, int32_t max_seq_len,
                                 pkv_dtype dtype, void* stream);
+
+/* ---- device-side precondition checks -------------------------------------------
+ * The preconditions on device memory above cannot be seen by the host without a
+ * copy, which the calls never make.  With checks on, each call first runs a
+ * check kernel on its stream that ORs one bit per violated precondition into a
+ * per-device error word, and every kernel of the library returns at once while
+ * that word is non-zero, so a violating call (and every later call on that
+ * device) writes nothing and reads no memory outside its arguments' true
+ * extents.  The word stays set until pkv_check_device_error reads it.
+ * (Spyre paged-attention PR: no host syncs in the forward, hence the checks run
+ * on the device; CSA2 Vanilla golden PR: a failed call writes nothing.)
+ * Duplicate slots within one kv_cache_write call are not detected. */
+typedef enum {
+  PKV_CHECK_SLOT_RANGE = 1,  /* a slot >= num_blocks * block_size                    */
+  PKV_CHECK_SEQ_LEN = 2,     /* seq_lens[s] < 0, > max_seq_len, or > max_blocks*B;   */
+                             /* for the gather: cu_seq_lens not non-decreasing from 0 */
+                             /* or not ending at total_tokens                        */
+  PKV_CHECK_TABLE = 4,       /* a used block_tables entry outside [0, num_blocks)    */
+  PKV_CHECK_CU_Q = 8         /* cu_seqlens_q: not from 0, decreasing, not ending at  */
+                             /* num_tokens, or q_s > min(seq_lens[s], max_q_len)     */
+} pkv_check_bits;
+
+/* Turn the device-side checks on (enable != 0) or off for every later call in
+ * this process.  Checks cost one small kernel per call.  Returns PKV_OK. */
+int pkv_set_device_checks(int enable);
+
+/* Wait for `stream`, read and clear the error word of the current device.
+ * Returns PKV_OK when no check failed since the last read, else
+ * PKV_ERR_INVALID_ARG with the violated checks named in pkv_last_error() and
+ * the pkv_check_bits in *bits (when bits is not NULL); PKV_ERR_LAUNCH if the
+ * HIP runtime fails.  This call synchronises: it is for tests and debugging. */
+int pkv_check_device_error(void* stream, uint32_t* bits);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until the
  * next pkv_* call on the same thread. */

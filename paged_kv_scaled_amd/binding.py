@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpkv.so")
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_LAUNCH = 0, -1, -2, -3, -4
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
 PKV_MASK_NONE, PKV_MASK_CAUSAL, PKV_MASK_BLOCK_CAUSAL = 0, 1, 2
+PKV_CHECK_SLOT_RANGE, PKV_CHECK_SEQ_LEN, PKV_CHECK_TABLE, PKV_CHECK_CU_Q = 1, 2, 4, 8
 
 # Every symbol include/pkv.h declares, with its ctypes signature.
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -33,6 +34,8 @@ SIGNATURES = {
                                                    _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                                    ctypes.c_int, _I32, _I32, _I32, ctypes.c_int,
                                                    _P]),
+    "pkv_set_device_checks": (ctypes.c_int, [ctypes.c_int]),
+    "pkv_check_device_error": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32)]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_int, []),
 }
@@ -159,3 +162,21 @@ def paged_attention_prefill(out, query, cu_seqlens_q, seq_lens, key_cache, value
                                            T, H, hkv, D, nb, bs, float(scale), int(mask),
                                            int(span_len), int(max_q_len), int(max_seq_len),
                                            _dtype_code(query), _stream()))
+
+
+def set_device_checks(enable: bool):
+    """Device-side precondition checks on (or off) for every later call in this process."""
+    _check(load().pkv_set_device_checks(1 if enable else 0))
+
+
+def check_device_error():
+    """Wait for the current stream, read and clear the device error word.
+    Returns (bits, message): bits is 0 and message "" when no check failed."""
+    lib = load()
+    bits = ctypes.c_uint32(0)
+    rc = lib.pkv_check_device_error(_stream(), ctypes.byref(bits))
+    if rc == PKV_OK:
+        return 0, ""
+    if rc != PKV_ERR_INVALID_ARG:
+        raise PkvError(rc, lib.pkv_last_error().decode())
+    return int(bits.value), lib.pkv_last_error().decode()

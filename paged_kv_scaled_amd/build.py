@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-SOURCES = ["api.cpp", "scatter.hip", "decode.hip", "prefill_valu.hip", "prefill_mfma.hip"]
+SOURCES = ["api.cpp", "scatter.hip", "decode.hip", "prefill_valu.hip", "prefill_mfma.hip", "checks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,6 +1,7 @@
 // C ABI of libpkv: host-side validation, then kernel launches on the caller's stream.
 // Every check runs before anything is enqueued, and a rejected call touches no memory
 // (CSA2 Vanilla golden PR, "Description": rejected before anything is written).
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -63,6 +64,20 @@ int launched(hipError_t e, const char* what) {
   return PKV_OK;
 }
 
+std::atomic<int> g_device_checks{0};
+
+// With device checks on: the device error word that every kernel of the call takes as
+// its guard (null when checks are off).  The call's check kernel is enqueued by the
+// caller of this function, before the kernels it guards.
+int guard_word(const uint32_t** guard, const char* what) {
+  *guard = nullptr;
+  if (!g_device_checks.load(std::memory_order_relaxed)) return PKV_OK;
+  *guard = pkv::check_guard();
+  if (*guard == nullptr)
+    return fail(PKV_ERR_LAUNCH, "%s: the device error word of the current device is unavailable", what);
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -70,6 +85,34 @@ extern "C" {
 int pkv_version(void) { return (1 << 16) | 0; }
 
 const char* pkv_last_error(void) { return g_err; }
+
+int pkv_set_device_checks(int enable) {
+  clear_error();
+  g_device_checks.store(enable != 0 ? 1 : 0, std::memory_order_relaxed);
+  return PKV_OK;
+}
+
+int pkv_check_device_error(void* stream, uint32_t* bits) {
+  clear_error();
+  uint32_t v = 0;
+  const hipError_t e = pkv::take_check_word((hipStream_t)stream, &v);
+  if (e != hipSuccess)
+    return fail(PKV_ERR_LAUNCH, "pkv_check_device_error: %s", hipGetErrorString(e));
+  if (bits) *bits = v;
+  if (v == 0) return PKV_OK;
+  char list[256] = "";
+  const struct { uint32_t bit; const char* name; } names[] = {
+      {PKV_CHECK_SLOT_RANGE, "slot_mapping entry >= num_blocks*block_size"},
+      {PKV_CHECK_SEQ_LEN, "sequence length outside [0, min(max_seq_len, max_blocks_per_seq*block_size)]"},
+      {PKV_CHECK_TABLE, "block_tables entry outside [0, num_blocks)"},
+      {PKV_CHECK_CU_Q, "cu_seqlens_q inconsistent"}};
+  for (const auto& n : names) {
+    if (!(v & n.bit)) continue;
+    if (list[0]) strncat(list, "; ", sizeof(list) - strlen(list) - 1);
+    strncat(list, n.name, sizeof(list) - strlen(list) - 1);
+  }
+  return fail(PKV_ERR_INVALID_ARG, "device checks failed (bits 0x%x): %s", v, list);
+}
 
 int pkv_kv_cache_write(const void* key, const void* value, int64_t kv_token_stride,
                        const int64_t* slot_mapping, int32_t num_tokens, void* key_cache,
@@ -92,6 +135,12 @@ int pkv_kv_cache_write(const void* key, const void* value, int64_t kv_token_stri
   pkv::ScatterArgs a{key, value, kv_token_stride, slot_mapping, num_tokens, key_cache,
                      value_cache, cache_block_stride, num_blocks, block_size, num_kv_heads,
                      head_dim, (int)dtype};
+  if ((rc = guard_word(&a.guard, "pkv_kv_cache_write")) != PKV_OK) return rc;
+  if (a.guard != nullptr &&
+      (rc = launched(pkv::launch_check_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size,
+                                             (hipStream_t)stream),
+                     "pkv_kv_cache_write (device checks)")) != PKV_OK)
+    return rc;
   return launched(pkv::launch_kv_scatter(a, (hipStream_t)stream), "pkv_kv_cache_write");
 }
 
@@ -118,6 +167,14 @@ int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_le
   pkv::GatherArgs a{key_out, value_out, cu_seq_lens, key_cache, value_cache, cache_block_stride,
                     block_tables, max_blocks_per_seq, num_seqs, total_tokens, num_blocks,
                     block_size, num_kv_heads, head_dim, max_seq_len, (int)dtype};
+  if ((rc = guard_word(&a.guard, "pkv_kv_cache_gather")) != PKV_OK) return rc;
+  if (a.guard != nullptr) {
+    pkv::CheckSeqArgs c{nullptr, cu_seq_lens, nullptr, block_tables, num_seqs, max_blocks_per_seq,
+                        num_blocks, block_size, max_seq_len, 0, 0, total_tokens};
+    if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream),
+                       "pkv_kv_cache_gather (device checks)")) != PKV_OK)
+      return rc;
+  }
   return launched(pkv::launch_kv_gather(a, (hipStream_t)stream), "pkv_kv_cache_gather");
 }
 
@@ -181,6 +238,14 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
   a.max_q_len = 1;
   a.dtype = (int)dtype;
   a.workspace = workspace;
+  if ((rc = guard_word(&a.guard, "pkv_paged_attention_decode")) != PKV_OK) return rc;
+  if (a.guard != nullptr) {
+    pkv::CheckSeqArgs c{seq_lens, nullptr, nullptr, block_tables, num_seqs, max_blocks_per_seq,
+                        num_blocks, block_size, max_seq_len, 1, 0, 0};
+    if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream),
+                       "pkv_paged_attention_decode (device checks)")) != PKV_OK)
+      return rc;
+  }
   return launched(pkv::launch_decode(a, plan, (hipStream_t)stream), "pkv_paged_attention_decode");
 }
 
@@ -244,6 +309,14 @@ int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_
   a.max_q_len = max_q_len;
   a.max_seq_len = max_seq_len;
   a.dtype = (int)dtype;
+  if ((rc = guard_word(&a.guard, "pkv_paged_attention_prefill")) != PKV_OK) return rc;
+  if (a.guard != nullptr) {
+    pkv::CheckSeqArgs c{seq_lens, nullptr, cu_seqlens_q, block_tables, num_seqs, max_blocks_per_seq,
+                        num_blocks, block_size, max_seq_len, max_q_len, num_tokens, 0};
+    if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream),
+                       "pkv_paged_attention_prefill (device checks)")) != PKV_OK)
+      return rc;
+  }
   if (pkv::prefill_mfma_supported((int)dtype, head_dim, scale))
     return launched(pkv::launch_prefill_mfma(a, (hipStream_t)stream), "pkv_paged_attention_prefill");
   return launched(pkv::launch_prefill_valu(a, (hipStream_t)stream), "pkv_paged_attention_prefill");

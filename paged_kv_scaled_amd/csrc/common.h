@@ -83,4 +83,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// True when a device-side precondition check on this device has failed (the guard is
+// the error word, null when checks are off): every kernel then returns before it
+// reads or writes anything else.
+__device__ __forceinline__ bool guard_tripped(const uint32_t* guard) {
+  return guard != nullptr && *guard != 0u;
+}
+
 }  // namespace pkv

@@ -80,6 +80,7 @@ struct DecodeParams {
   int64_t total_items;      // split mode: S*nsplit*HG; stream mode: HG*nranges
   int32_t mb, S, H, Hkv, g, block_shift, split_len, nsplit, groups_per_kv, nranges;
   float scale_log2;
+  const uint32_t* guard;    // device error word when device checks are on, else null
 };
 
 template <typename T, int D>
@@ -356,6 +357,7 @@ __device__ __forceinline__ void write_partial(const DecodeParams& p, int64_t slo
 template <typename T, int D, int HPW, int NSTEP>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_split_kernel(const DecodeParams p) {
+  if (guard_tripped(p.guard)) return;
   using C = DecodeShape<T, D>;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = lane / C::LPT, c = lane % C::LPT;
@@ -444,6 +446,7 @@ __device__ __forceinline__ void stream_locate(const DecodeParams& p, int64_t x, 
 template <typename T, int D, int HPW, int NSTEP>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_stream_kernel(const DecodeParams p) {
+  if (guard_tripped(p.guard)) return;
   using C = DecodeShape<T, D>;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = lane / C::LPT, c = lane % C::LPT;
@@ -565,6 +568,7 @@ __device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, i
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_merge_split_kernel(const DecodeParams p) {
+  if (guard_tripped(p.guard)) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t sh = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
   if (sh >= (int64_t)p.S * p.H) return;
@@ -583,6 +587,7 @@ decode_merge_split_kernel(const DecodeParams p) {
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_merge_stream_kernel(const DecodeParams p) {
+  if (guard_tripped(p.guard)) return;
   constexpr int DPL = (D + kWave - 1) / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t sh = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -735,6 +740,7 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& pl, hipStream_t st
   dp.groups_per_kv = pl.groups_per_kv;
   dp.nranges = pl.num_ranges;
   dp.scale_log2 = a.scale * kLog2e;
+  dp.guard = a.guard;
   const size_t slots = pl.workspace_bytes / ((size_t)(a.head_dim + 2) * sizeof(float));
   dp.ws_acc = pl.workspace_bytes ? reinterpret_cast<float*>(a.workspace) : nullptr;
   dp.ws_ml = pl.workspace_bytes ? dp.ws_acc + slots * a.head_dim : nullptr;

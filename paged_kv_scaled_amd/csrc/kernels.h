@@ -23,6 +23,7 @@ struct ScatterArgs {
   int64_t block_stride;        // elements
   int32_t num_blocks, block_size, num_kv_heads, head_dim;
   int dtype;
+  const uint32_t* guard = nullptr;   // device error word when device checks are on
 };
 
 struct GatherArgs {
@@ -36,6 +37,7 @@ struct GatherArgs {
   int32_t max_blocks_per_seq, num_seqs, total_tokens, num_blocks, block_size, num_kv_heads,
       head_dim, max_seq_len;
   int dtype;
+  const uint32_t* guard = nullptr;
 };
 
 struct AttnArgs {
@@ -54,7 +56,27 @@ struct AttnArgs {
   int32_t span_len, max_q_len, max_seq_len;
   int dtype;
   void* workspace;               // decode only
+  const uint32_t* guard;         // device error word when device checks are on, else null
 };
+
+// What the sequence check kernel reads: lengths from seq_lens (attention) or from
+// cu_seq_lens (gather); cu_seqlens_q only for prefill.
+struct CheckSeqArgs {
+  const int32_t* seq_lens;
+  const int32_t* cu_seq_lens;
+  const int32_t* cu_seqlens_q;
+  const int32_t* block_tables;
+  int32_t num_seqs, max_blocks_per_seq, num_blocks, block_size, max_seq_len, max_q_len;
+  int64_t num_tokens, total_tokens;
+};
+
+// Device-side precondition checks: the device address of this device's error word
+// (null if the runtime cannot give it), the two check kernels, and a synchronising
+// read-and-clear of the word.
+const uint32_t* check_guard();
+hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t num_slots, hipStream_t stream);
+hipError_t launch_check_seqs(const CheckSeqArgs& a, hipStream_t stream);
+hipError_t take_check_word(hipStream_t stream, uint32_t* bits);
 
 // Decode split plan: a pure function of the sizes, shared by the workspace query
 // and the launch so that both agree.

@@ -48,6 +48,7 @@ struct PrefillParams {
   int32_t hw, rb_log2, head_groups, qtiles;   // WG tiling
   int32_t ngroups;                            // (sequence, kv head, head group) groups
   float scale_log2;
+  const uint32_t* guard;                      // device error word when checks are on
 };
 
 template <typename T> struct Mfma;
@@ -104,6 +105,7 @@ __device__ __forceinline__ int vt_pos(int t) {
 template <typename T, int D>
 __global__ void __launch_bounds__(kWaves * 64)
 prefill_mfma_kernel(const PrefillParams p) {
+  if (guard_tripped(p.guard)) return;
   constexpr int NT = kWaves * 64;     // threads
   constexpr int NCB = 1;              // column blocks per wave
   using L = Lds<D>;
@@ -444,6 +446,7 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
   if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
   p.ngroups = (int)ng;
   p.scale_log2 = a.scale * kLog2e;
+  p.guard = a.guard;
   const dim3 grid((unsigned)nb), block(kWaves * 64);
   if (a.dtype == kBF16) {
     if (a.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 128>), grid, block, 0, stream, p);

@@ -58,6 +58,7 @@ __device__ __forceinline__ int visible_end(int mask, int a, int L, int span) {
 template <typename T, int DMAX>
 __global__ void __launch_bounds__(kValuThreads)
 prefill_valu_kernel(const AttnArgs p, float scale_log2) {
+  if (guard_tripped(p.guard)) return;
   __shared__ float s_q[kValuWaves][DMAX];
   __shared__ float s_p[kValuWaves][kWave];
   const int lane = threadIdx.x & (kWave - 1);

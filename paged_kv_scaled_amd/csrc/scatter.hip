@@ -32,8 +32,9 @@ __global__ void __launch_bounds__(kScatterThreads)
 kv_scatter_kernel(const char* __restrict__ key, const char* __restrict__ value,
                   int64_t token_stride_b, const int64_t* __restrict__ slots, int32_t num_tokens,
                   char* __restrict__ kc, char* __restrict__ vc, int64_t block_stride_b,
-                  int32_t block_shift, int32_t row_vecs, int64_t num_slots) {
+                  int32_t block_shift, int32_t row_vecs, int64_t num_slots, const uint32_t* guard) {
   using V = typename VecT<VEC>::type;
+  if (guard_tripped(guard)) return;
   const int64_t total = (int64_t)num_tokens * row_vecs;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
   const int32_t bmask = (1 << block_shift) - 1;
@@ -61,8 +62,9 @@ kv_gather_kernel(char* __restrict__ kout, char* __restrict__ vout,
                  const int32_t* __restrict__ cu_seq_lens, const char* __restrict__ kc,
                  const char* __restrict__ vc, int64_t block_stride_b,
                  const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
-                 int32_t block_shift, int32_t row_vecs) {
+                 int32_t block_shift, int32_t row_vecs, const uint32_t* guard) {
   using V = typename VecT<VEC>::type;
+  if (guard_tripped(guard)) return;
   const int s = blockIdx.y;
   const int32_t r0 = cu_seq_lens[s];
   const int32_t L = cu_seq_lens[s + 1] - r0;
@@ -113,7 +115,8 @@ hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream) {
 #define PKV_SCATTER(V)                                                                       \
   hipLaunchKernelGGL(kv_scatter_kernel<V>, dim3(blocks), dim3(kScatterThreads), 0, stream,  \
                      (const char*)a.key, (const char*)a.value, ts_b, a.slots, a.num_tokens,  \
-                     (char*)a.key_cache, (char*)a.value_cache, bs_b, shift, row_vecs, num_slots)
+                     (char*)a.key_cache, (char*)a.value_cache, bs_b, shift, row_vecs, num_slots,  \
+                     a.guard)
   switch (vec) {
     case 16: PKV_SCATTER(16); break;
     case 8: PKV_SCATTER(8); break;
@@ -138,7 +141,7 @@ hipError_t launch_kv_gather(const GatherArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(kv_gather_kernel<V>, grid, dim3(kScatterThreads), 0, stream,              \
                      (char*)a.key_out, (char*)a.value_out, a.cu_seq_lens,                      \
                      (const char*)a.key_cache, (const char*)a.value_cache, bs_b,                \
-                     a.block_tables, a.max_blocks_per_seq, shift, row_vecs)
+                     a.block_tables, a.max_blocks_per_seq, shift, row_vecs, a.guard)
   switch (vec) {
     case 16: PKV_GATHER(16); break;
     case 8: PKV_GATHER(8); break;

@@ -148,3 +148,10 @@ def test_gather_rejections(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         B.load(str(tmp_path / "missing.so"))
+
+
+def test_device_checks_switch(lib):
+    """The switch needs no GPU; reading the error word does (covered by the GPU tests)."""
+    assert lib.pkv_set_device_checks(1) == B.PKV_OK
+    assert lib.pkv_set_device_checks(0) == B.PKV_OK
+    assert B.last_error() == ""

@@ -1,0 +1,160 @@
+"""Device-side precondition checks (pkv_set_device_checks / pkv_check_device_error).
+
+Each invalid input below is backed by allocated memory (tables and caches carry slack
+past what the call is told, the workspace is oversized), so even a check that failed
+to fire could not make a kernel read or write outside an allocation."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import reference as ref
+from paged_kv_scaled_amd import binding as B
+from paged_kv_scaled_amd import workloads as wl
+
+from gpu_helpers import Dev, as_f64, bits_of, compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture
+def checks(gpu):
+    B.set_device_checks(True)
+    B.check_device_error()          # start from a clear word
+    try:
+        yield
+    finally:
+        B.set_device_checks(False)
+        B.check_device_error()
+
+
+def _decode_ws(w, max_seq_len=None, factor=1):
+    need = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                   max_seq_len or w.max_seq_len)
+    return need, torch.zeros(max(need * factor, 1), dtype=torch.uint8, device="cuda")
+
+
+def test_checks_pass_and_change_nothing_on_valid_inputs(checks):
+    """Valid calls with checks on: no bit set, outputs bit-identical to calls without."""
+    w = wl.decode_batch(seed=50, num_seqs=6, lo=100, hi=3000)
+    p = wl.chunked_prefill(seed=51, num_seqs=3, ctx_hi=300, q_hi=200)
+    outs = []
+    for on in (True, False):
+        B.set_device_checks(on)
+        dd, dp = Dev(w), Dev(p)
+        dd.write_all()
+        dp.write_all()
+        od, op = dd.decode(), dp.prefill()
+        kg = torch.empty_like(dp.key)
+        vg = torch.empty_like(dp.value)
+        B.kv_cache_gather(kg, vg, dp.cu_k, dp.kc, dp.vc, dp.tables, p.max_seq_len)
+        torch.cuda.synchronize()
+        outs.append((bits_of(od), bits_of(op), bits_of(kg), bits_of(vg)))
+        if on:
+            assert B.check_device_error() == (0, "")
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    B.set_device_checks(True)
+
+
+def test_checks_flag_slot_out_of_range(checks):
+    w = wl.random_small(3, "bf16", head_dim=64)
+    d = Dev(w)
+    slots = d.slots.clone()
+    slots[-1] = w.num_blocks * w.block_size + 5
+    B.kv_cache_write(d.key, d.value, slots, d.kc, d.vc)
+    bits, msg = B.check_device_error()
+    assert bits == B.PKV_CHECK_SLOT_RANGE and "slot_mapping" in msg
+    assert torch.isnan(d.kc).all() and torch.isnan(d.vc).all()        # nothing written
+    # the word was cleared by the read: a valid call works again
+    B.kv_cache_write(d.key, d.value, d.slots, d.kc, d.vc)
+    assert B.check_device_error() == (0, "")
+    kg, vg = torch.empty_like(d.key), torch.empty_like(d.value)
+    B.kv_cache_gather(kg, vg, d.cu_k, d.kc, d.vc, d.tables, w.max_seq_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(kg), bits_of(d.key)) and np.array_equal(bits_of(vg), bits_of(d.value))
+
+
+def test_checks_flag_table_entry_and_stay_set_until_read(checks):
+    """A block id one past the pool (two slack blocks are allocated behind it): flagged,
+    the output is untouched, and a later valid call is a no-op until the word is read."""
+    w = wl.decode_batch(seed=52, num_seqs=4, lo=200, hi=900)
+    d = Dev(w)
+    d.write_all()
+    shape = (w.num_blocks + 2, w.block_size, w.num_kv_heads, w.head_dim)
+    kbig = torch.zeros(shape, dtype=d.kc.dtype, device="cuda")
+    vbig = torch.zeros(shape, dtype=d.vc.dtype, device="cuda")
+    kbig[:w.num_blocks] = d.kc
+    vbig[:w.num_blocks] = d.vc
+    kc, vc = kbig[:w.num_blocks], vbig[:w.num_blocks]
+    tables = d.tables.clone()
+    tables[2, 1] = w.num_blocks
+    need, ws = _decode_ws(w)
+    out = torch.full_like(d.query, 3.0)
+    B.paged_attention_decode(out, d.query, kc, vc, tables, d.seq_lens, w.scale, w.max_seq_len,
+                             ws if need else None)
+    # a valid call before the read: still guarded, writes nothing
+    out2 = torch.full_like(d.query, 4.0)
+    B.paged_attention_decode(out2, d.query, kc, vc, d.tables, d.seq_lens, w.scale, w.max_seq_len,
+                             ws if need else None)
+    bits, msg = B.check_device_error()
+    assert bits == B.PKV_CHECK_TABLE and "block_tables" in msg
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0) and torch.all(out2 == 4.0)
+    B.paged_attention_decode(out2, d.query, kc, vc, d.tables, d.seq_lens, w.scale, w.max_seq_len,
+                             ws if need else None)
+    assert B.check_device_error() == (0, "")
+    want, _ = ref.workload_attention(w)
+    compare(as_f64(out2), want, w.dtype, "after clear")
+
+
+def test_checks_flag_length_over_hint(checks):
+    """seq_lens[1] = 1000 with max_seq_len = 900 (the table covers 1008 keys; the
+    workspace is 4x the size the hint asks for)."""
+    lens = np.array([300, 1000, 17, 700], np.int32)
+    w = wl.build("over_hint", 53, "bf16", lens, np.ones(4, np.int32), 8, 2, 128, 16, wl.MASK_NONE,
+                 decode=True, max_blocks_per_seq=63)
+    d = Dev(w)
+    d.write_all()
+    need, ws = _decode_ws(w, max_seq_len=900, factor=4)
+    out = torch.full_like(d.query, 2.0)
+    B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens, w.scale, 900,
+                             ws if need else None)
+    bits, msg = B.check_device_error()
+    assert bits == B.PKV_CHECK_SEQ_LEN and "sequence length" in msg
+    assert torch.all(out == 2.0)
+
+
+def test_checks_flag_cu_seqlens_q(checks):
+    """A decreasing cu_seqlens_q (a negative query segment) in prefill."""
+    w = wl.chunked_prefill(seed=54, num_seqs=3, ctx_hi=200, q_lo=20, q_hi=60)
+    d = Dev(w)
+    d.write_all()
+    cu = d.cu_q.clone()
+    cu[1], cu[2] = cu[2], cu[1]
+    out = torch.full_like(d.query, 5.0)
+    B.paged_attention_prefill(out, d.query, cu, d.seq_lens, d.kc, d.vc, d.tables, w.scale, w.mask,
+                              w.span_len, w.max_q_len, w.max_seq_len)
+    bits, msg = B.check_device_error()
+    assert bits & B.PKV_CHECK_CU_Q and "cu_seqlens_q" in msg
+    assert torch.all(out == 5.0)
+
+
+def test_checks_flag_length_over_table_capacity(checks):
+    """The last sequence is 16 keys longer than max_blocks_per_seq * block_size; the
+    table rows sit in a larger buffer, so the row after the last exists."""
+    lens = np.array([100, 200, 256], np.int32)
+    w = wl.build("over_cap", 55, "bf16", lens, lens, 8, 2, 128, 16, wl.MASK_CAUSAL)
+    d = Dev(w)
+    d.write_all()
+    mb = d.tables.shape[1]
+    buf = torch.zeros(d.tables.numel() + 4 * mb, dtype=torch.int32, device="cuda")
+    buf[:d.tables.numel()] = d.tables.flatten()
+    tables = buf[:d.tables.numel()].view(d.tables.shape)
+    seq_lens = d.seq_lens.clone()
+    seq_lens[2] = mb * w.block_size + 16
+    out = torch.full_like(d.query, 6.0)
+    B.paged_attention_prefill(out, d.query, d.cu_q, seq_lens, d.kc, d.vc, tables, w.scale, w.mask,
+                              w.span_len, w.max_q_len, mb * w.block_size)
+    bits, msg = B.check_device_error()
+    assert bits & B.PKV_CHECK_SEQ_LEN
+    assert torch.all(out == 6.0)
