@@ -389,6 +389,103 @@ decode_split_kernel(const DecodeParams p) {
   }
 }
 
+// ---- item mode -------------------------------------------------------------------------
+// Short sequences (each one split and at most kItemPages pages): every group of LPT = 8
+// lanes owns one item (sequence, head group) and walks its keys two per step, so the 8
+// items of a wave run side by side.  Their dependent loads (length, page ids, K/V)
+// overlap, and no cross-lane merge is needed at the end.
+constexpr int kItemPages = 8;   // page ids of an item: one per lane of its group
+constexpr int kItemSteps = 2;   // steps whose loads are issued together
+
+template <typename T, int D>
+__device__ __forceinline__ void load_item_step(Step<T, D>& st, const DecodeParams& p, int32_t pid,
+                                               int64_t head_off, int base, int L, int t, int c) {
+  using C = DecodeShape<T, D>;
+  const int64_t row_elems = (int64_t)p.Hkv * D;
+  const int bmask = (1 << p.block_shift) - 1;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int pos_raw = base + r;
+    st.valid[r] = pos_raw < L;
+    const int pos = min(pos_raw, max(L - 1, 0));          // branch-free: re-read a real key
+    const int64_t blk = __shfl(pid, t * C::LPT + (pos >> p.block_shift), kWave);
+    const int64_t row = blk * p.block_stride + (int64_t)(pos & bmask) * row_elems + head_off;
+    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const typename T::storage*>(p.kc) + row);
+    const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const typename T::storage*>(p.vc) + row);
+#pragma unroll
+    for (int v = 0; v < C::VPL; ++v) {
+      const u32x4_t kk = __builtin_nontemporal_load(kp + v * C::LPT + c);
+      const u32x4_t vv = __builtin_nontemporal_load(vp + v * C::LPT + c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        st.k[r][v * 4 + w] = kk[w];
+        st.v[r][v * 4 + w] = vv[w];
+      }
+    }
+  }
+}
+
+template <typename T, int D, int HPW, int NSTEP>
+__global__ void __launch_bounds__(kDecodeThreads)
+decode_items_kernel(const DecodeParams p) {
+  if (guard_tripped(p.guard)) return;
+  using C = DecodeShape<T, D>;
+  using S = typename T::storage;
+  static_assert(C::LPT == 8 && C::TPR == 8, "item mode needs 8 lanes per row");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = lane / C::LPT, c = lane % C::LPT;
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+  if (wave * C::TPR >= p.total_items) return;            // uniform over the wave
+  const int64_t item_raw = wave * C::TPR + t;
+  const bool live = item_raw < p.total_items;
+  const int64_t item = live ? item_raw : p.total_items - 1;
+  const int HG = p.Hkv * p.groups_per_kv;
+  const int hg = (int)(item % HG);
+  const int s = (int)(item / HG);
+  const int L = p.seq_lens[s];
+  const int kvh = hg / p.groups_per_kv, sub = hg % p.groups_per_kv;
+  const int h0 = kvh * p.g + sub * HPW;
+  const int nh = min(HPW, p.g - sub * HPW);
+  // lane c of the group holds page c of the item; block 0 stands in past the last page
+  const int last_page = L > 0 ? (L - 1) >> p.block_shift : -1;
+  const int32_t pid = c <= last_page ? p.block_tables[(int64_t)s * p.mb + c] : 0;
+  uint32_t q[HPW][C::WPL];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const S*>(p.query) + ((int64_t)s * p.H + h0 + (hh < nh ? hh : 0)) * D);
+#pragma unroll
+    for (int v = 0; v < C::VPL; ++v) {
+      const u32x4_t qq = qp[v * C::LPT + c];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) q[hh][v * 4 + w] = qq[w];
+    }
+  }
+  float m[HPW], l[HPW], acc[HPW][C::EPL];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::EPL; ++e) acc[hh][e] = 0.f;
+  }
+  // the longest item of the wave bounds the steps (uniform loop)
+  int Lw = live ? L : 0;
+#pragma unroll
+  for (int off = C::LPT; off < kWave; off <<= 1) Lw = max(Lw, __shfl_xor(Lw, off, kWave));
+  const int64_t head_off = (int64_t)kvh * D;
+  for (int base = 0; base < Lw; base += 2 * NSTEP) {
+    Step<T, D> st[NSTEP];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) load_item_step<T, D>(st[k], p, pid, head_off, base + 2 * k, L, t, c);
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) compute_step<T, D, HPW>(st[k], q, m, l, acc, p.scale_log2);
+  }
+  if (live) write_output<T, D, HPW>(p, s, h0, nh, c, l, acc);
+}
+
 // ---- stream mode -----------------------------------------------------------------------
 
 __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
@@ -647,6 +744,15 @@ void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t strea
     hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, NS>), dim3(blocks), dim3(kDecodeThreads),
                        0, stream, dp);
     return;
+  }
+  if constexpr (C::LPT == 8 && C::TPR == 8) {
+    if (pl.num_splits == 1 && pl.max_seq_len <= kItemPages << dp.block_shift) {
+      const int64_t waves = (dp.total_items + C::TPR - 1) / C::TPR;
+      const int blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+      hipLaunchKernelGGL((decode_items_kernel<T, D, HPW, kItemSteps>), dim3(blocks),
+                         dim3(kDecodeThreads), 0, stream, dp);
+      return;
+    }
   }
   const int64_t wanted = (dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock;
   const int blocks = (int)(wanted < 8192 ? wanted : 8192);

@@ -187,3 +187,36 @@ def test_smallseq_thd_zero_copy_view(gpu):
     torch.cuda.synchronize()
     want, _ = ref.workload_attention(w)
     compare(as_f64(out), want, w.dtype, "thd_view")
+
+
+@pytest.mark.parametrize("H,Hkv", [(16, 16), (8, 4), (12, 3), (32, 4), (16, 2)])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f16", 64), ("f32", 128)])
+def test_decode_item_mode(gpu, H, Hkv, dtype, head_dim):
+    """Short sequences (at most 8 pages, one split): eight items per wave, one per group
+    of 8 lanes.  Item counts that leave the last wave part-filled, empty sequences, every
+    length from 0 to 8 pages, and 1, 2, 4 and 8 heads per item."""
+    bs = 4
+    lens = np.arange(0, 8 * bs + 1, dtype=np.int32)
+    lens = np.concatenate([lens, np.array([8 * bs, 1, 0, 3, 17], np.int32)])
+    w = wl.build("item_mode", 60 + H, dtype, lens, np.minimum(lens, 1), H, Hkv, head_dim, bs,
+                 wl.MASK_NONE, decode=True)
+    # one query row per sequence, also for the empty ones (decode layout [S, H, D])
+    q = wl.round_to_storage(np.random.default_rng(61).standard_normal((len(lens), H, head_dim))
+                            .astype(np.float32), dtype)
+    w.query = q
+    w.q_lens = np.ones(len(lens), np.int32)
+    w.cu_seqlens_q = np.arange(len(lens) + 1, dtype=np.int32)
+    d = Dev(w)
+    B.kv_cache_write(d.key, d.value, d.slots, d.kc, d.vc)
+    out = d.decode()
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    empty = lens == 0
+    assert np.all(got[empty] == 0)
+    live = np.nonzero(~empty)[0]
+    keys = ref.split_logical(ref.widen(w.key, dtype), w.cu_seq_lens)
+    vals = ref.split_logical(ref.widen(w.value, dtype), w.cu_seq_lens)
+    want, _ = ref.paged_attention(ref.widen(q[live], dtype), [keys[i] for i in live],
+                                  [vals[i] for i in live], np.arange(len(live) + 1, dtype=np.int32),
+                                  lens[live], Hkv, w.scale, wl.MASK_NONE)
+    compare(got[live], want, dtype, f"item_mode H{H} Hkv{Hkv}")
