@@ -286,19 +286,25 @@ def gemm_ceiling(n=8192, reps=5):
 
 
 def device_info():
-    """What the run was measured on: device properties, and the clocks rocm-smi reports
-    (None where the tool is unavailable)."""
-    import subprocess
+    """What the run was measured on: device properties, and the current core and memory
+    clock levels from the driver's sysfs DPM tables (files only: no helper program is
+    started from this GPU process)."""
+    import glob
     import torch
     pr = torch.cuda.get_device_properties(0)
     info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
             "memory_GB": round(pr.total_memory / 1e9, 1)}
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        clk = [l.split(":", 2)[-1].strip() for l in r.stdout.splitlines() if "sclk" in l or "mclk" in l]
-        info["clocks"] = clk[:4] or None
-    except Exception:
-        info["clocks"] = None
+    clocks = {}
+    for kind in ("sclk", "mclk"):
+        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}")):
+            try:
+                cur = [l.strip() for l in open(f) if l.strip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                clocks[kind] = cur[0]
+                break
+    info["clocks"] = clocks or None
     return info
 
 
