@@ -20,6 +20,7 @@ steps; the vllm-omni piecewise block-causal PR for the block-causal mask):
   visible  : key p < L_s and   NONE: always
                                CAUSAL: p <= a (bottom-right aligned)
                                BLOCK_CAUSAL(span): p <= a or p // span == a // span
+                               SPANS(full spans): p <= a or p and a inside one full span
   scores   : z_p = scale * <q, k_p>, q head h reads kv head h // (H / Hkv)
   softmax  : stable: m = max z, w = exp(z - m), out = sum w v / sum w, lse = m + log sum w
   empty row: no visible key -> out = 0, lse = -inf
@@ -34,7 +35,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-MASK_NONE, MASK_CAUSAL, MASK_BLOCK_CAUSAL = 0, 1, 2
+MASK_NONE, MASK_CAUSAL, MASK_BLOCK_CAUSAL, MASK_SPANS = 0, 1, 2, 3
 
 
 # ----------------------------------------------------------------------------------------
@@ -121,12 +122,39 @@ def is_visible(p: int, a: int, seq_len: int, mask: int, span_len: int) -> bool:
     raise ValueError(mask)
 
 
-def visibility_matrix(positions: np.ndarray, seq_len: int, mask: int, span_len: int):
-    """Boolean [len(positions), seq_len] matrix of is_visible, built entry by entry."""
+def full_span_of(pos: int, full_spans) -> Optional[int]:
+    """Index of the full span [start, end) of the list that holds position pos, else None."""
+    for i, (s, e) in enumerate(full_spans):
+        if s <= pos < e:
+            return i
+    return None
+
+
+def span_visible(p: int, a: int, seq_len: int, full_spans) -> bool:
+    """SPANS mask: general span lists (the `full_attn_spans` metadata of the vllm-omni
+    piecewise PR).  Key p is visible to the query at absolute position a when p < L and
+    either p <= a, or p and a lie in the same full (image) span; positions outside every
+    full span form causal text runs.  This is that PR's dense reference,
+    `(q >= kv) or same_image_block`, with the image blocks given by the list."""
+    if p >= seq_len:
+        return False
+    if p <= a:
+        return True
+    i = full_span_of(a, full_spans)
+    return i is not None and i == full_span_of(p, full_spans)
+
+
+def visibility_matrix(positions: np.ndarray, seq_len: int, mask: int, span_len: int,
+                      full_spans=None):
+    """Boolean [len(positions), seq_len] matrix of is_visible (or, for SPANS, of
+    span_visible over this sequence's full spans), built entry by entry."""
     vis = np.zeros((len(positions), seq_len), bool)
     for i, a in enumerate(positions):
         for p in range(seq_len):
-            vis[i, p] = is_visible(p, int(a), seq_len, mask, span_len)
+            if mask == MASK_SPANS:
+                vis[i, p] = span_visible(p, int(a), seq_len, full_spans)
+            else:
+                vis[i, p] = is_visible(p, int(a), seq_len, mask, span_len)
     return vis
 
 
@@ -159,7 +187,8 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray, scale: 
 def paged_attention(query: np.ndarray, keys: Sequence[np.ndarray], values: Sequence[np.ndarray],
                     cu_seqlens_q: np.ndarray, seq_lens: np.ndarray, num_kv_heads: int,
                     scale: float, mask: int, span_len: int = 0,
-                    rows: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None):
+                    rows: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
+                    spans: Optional[Sequence] = None):
     """Attention of a flat (THD) query batch over per-sequence logical K/V.
 
     query [T, H, D] float64; keys[s], values[s] [L_s, Hkv, D] float64.  Sequence s owns
@@ -167,7 +196,8 @@ def paged_attention(query: np.ndarray, keys: Sequence[np.ndarray], values: Seque
     row i of the chunk sits at absolute position a = L_s - q_s + i (chunked prefill;
     decode is the case q_s = 1).  Returns out [T, H, D] and lse [T, H]; with `rows`
     (flat row indices) / `heads` given, only those entries are computed (the rest stay
-    zero / -inf) so that large batches can be sampled.
+    zero / -inf) so that large batches can be sampled.  For the SPANS mask, spans[s]
+    lists the (start, end) full spans of sequence s in absolute positions.
     """
     T, H, D = query.shape
     out = np.zeros((T, H, values[0].shape[-1] if len(values) else D), np.float64)
@@ -184,7 +214,8 @@ def paged_attention(query: np.ndarray, keys: Sequence[np.ndarray], values: Seque
         if not row_ids:
             continue
         positions = np.array([ctx + (r - r0) for r in row_ids], np.int64)
-        vis = visibility_matrix(positions, L, mask, span_len)
+        vis = visibility_matrix(positions, L, mask, span_len,
+                                spans[s] if mask == MASK_SPANS else None)
         for h in head_list:
             kvh = kv_head_of(h, H, num_kv_heads)
             o, l = attend(query[row_ids, h, :], keys[s][:, kvh, :], values[s][:, kvh, :], vis, scale)
@@ -204,7 +235,8 @@ def workload_attention(w, rows=None, heads=None):
     k = split_logical(widen(w.key, w.dtype), w.cu_seq_lens)
     v = split_logical(widen(w.value, w.dtype), w.cu_seq_lens)
     return paged_attention(q, k, v, w.cu_seqlens_q, w.seq_lens, w.num_kv_heads, w.scale,
-                           w.mask, w.span_len, rows=rows, heads=heads)
+                           w.mask, w.span_len, rows=rows, heads=heads,
+                           spans=getattr(w, "spans", None))
 
 
 # ----------------------------------------------------------------------------------------
@@ -230,12 +262,14 @@ def lse_merge(outs: Sequence[np.ndarray], lses: Sequence[np.ndarray]):
 # second formulations and the brute-force twin (used as pins)
 # ----------------------------------------------------------------------------------------
 
-def brute_force(query, keys, values, cu_seqlens_q, seq_lens, num_kv_heads, scale, mask, span_len=0):
+def brute_force(query, keys, values, cu_seqlens_q, seq_lens, num_kv_heads, scale, mask, span_len=0,
+                spans=None):
     """Scalar triple loops with math.exp, no numpy arithmetic: tiny inputs only.
 
     Independent of the helpers above on purpose: the head map, the chunk positions and
     the mask rules are written out again here from the definition, in a different form
-    (the block-causal rule as "key's block no later than the query's block").
+    (the block-causal rule as "key's block no later than the query's block"; the span
+    rule as "a later key is visible only up to the end of the query's full span").
     """
     T, H, D = query.shape
     out = [[[0.0] * D for _ in range(H)] for _ in range(T)]
@@ -252,6 +286,13 @@ def brute_force(query, keys, values, cu_seqlens_q, seq_lens, num_kv_heads, scale
                         continue
                     if mask == MASK_BLOCK_CAUSAL and (p // span_len) > (a // span_len):
                         continue
+                    if mask == MASK_SPANS and p > a:
+                        end = a + 1
+                        for (ss, se) in spans[s]:
+                            if ss <= a < se:
+                                end = se
+                        if p >= end:
+                            continue
                     acc = 0.0
                     for d in range(D):
                         acc += float(query[r, h, d]) * float(keys[s][p, kvh, d])

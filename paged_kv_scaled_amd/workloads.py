@@ -27,8 +27,9 @@ from typing import Optional
 
 import numpy as np
 
-MASK_NONE, MASK_CAUSAL, MASK_BLOCK_CAUSAL = 0, 1, 2
-MASK_NAMES = {MASK_NONE: "none", MASK_CAUSAL: "causal", MASK_BLOCK_CAUSAL: "block_causal"}
+MASK_NONE, MASK_CAUSAL, MASK_BLOCK_CAUSAL, MASK_SPANS = 0, 1, 2, 3
+MASK_NAMES = {MASK_NONE: "none", MASK_CAUSAL: "causal", MASK_BLOCK_CAUSAL: "block_causal",
+              MASK_SPANS: "spans"}
 
 # Storage dtypes: name -> (numpy storage dtype of the raw bits, bytes per element)
 DTYPES = {"f32": (np.uint32, 4), "f16": (np.uint16, 2), "bf16": (np.uint16, 2)}
@@ -79,6 +80,17 @@ class Workload:
     key: np.ndarray               # bits [sum L, Hkv, D] logical keys, sequence-major
     value: np.ndarray             # bits [sum L, Hkv, D]
     decode: bool = False          # one query token per sequence
+    spans: Optional[list] = None  # SPANS mask: per sequence, the (start, end) full spans
+
+    def span_arrays(self):
+        """The span lists flattened for the library: int32 [num_spans, 2] (start, end)
+        pairs, sequence by sequence, and int32 [S+1] offsets into them."""
+        lists = self.spans or [[] for _ in range(self.num_seqs)]
+        flat = [pair for seq in lists for pair in seq]
+        cu = np.zeros(self.num_seqs + 1, np.int32)
+        cu[1:] = np.cumsum([len(x) for x in lists])
+        arr = np.array(flat, np.int32).reshape(-1, 2) if flat else np.zeros((0, 2), np.int32)
+        return arr, cu
 
     @property
     def num_seqs(self) -> int:
@@ -239,12 +251,43 @@ def long_block_causal(seed: int = 4, num_seqs: int = 4, seq_len: int = 8192, dty
                  MASK_BLOCK_CAUSAL, span_len=2048, spare_blocks=spare_blocks, rng=rng)
 
 
+def span_layout(rng: np.random.Generator, seq_len: int, text=(16, 256), image=(256, 1024)):
+    """A text/image layout of one sequence: alternating causal text runs and full image
+    blocks with lengths drawn uniformly from the given ranges, starting with text.
+    Returns the full spans as (start, end) pairs (the text runs are what lies between)."""
+    spans, pos, is_text = [], 0, True
+    while pos < seq_len:
+        lo, hi = text if is_text else image
+        n = int(rng.integers(lo, hi + 1))
+        if not is_text:
+            spans.append((pos, min(pos + n, seq_len)))
+        pos += n
+        is_text = not is_text
+    return spans
+
+
+def mixed_spans(seed: int = 5, num_seqs: int = 4, seq_len: int = 4096, dtype: str = "bf16",
+                num_heads: int = 32, q_len: Optional[int] = None, spare_blocks: int = 1) -> Workload:
+    """General span lists (the next row after the five shapes): per sequence, text runs of
+    U{16..256} tokens (causal) alternating with image blocks of U{256..1024} tokens (full),
+    32 q / 8 kv heads, D 128, B 16.  q_len < seq_len makes it a chunked prefill."""
+    rng = np.random.default_rng(seed)
+    lens = np.full(num_seqs, seq_len, np.int32)                       # draw 1 (fixed)
+    layouts = [span_layout(rng, seq_len) for _ in range(num_seqs)]
+    ql = np.full(num_seqs, q_len or seq_len, np.int32)
+    w = build("mixed_spans", seed, dtype, lens, ql, num_heads, 8, 128, 16, MASK_SPANS,
+              spare_blocks=spare_blocks, rng=rng)
+    w.spans = layouts
+    return w
+
+
 CONFIGS = {
     "tiny_prefill": tiny_prefill,
     "decode_batch": decode_batch,
     "chunked_prefill": chunked_prefill,
     "smallseq_varlen": smallseq_varlen,
     "long_block_causal": long_block_causal,
+    "mixed_spans": mixed_spans,
 }
 
 

@@ -276,6 +276,83 @@ def test_piecewise_golden_two_segment_shapes():
     assert np.max(np.abs(comp - dense)) <= 1e-12
 
 
+def _cover(full, L):
+    """(start, end, kind) list covering [0, L): the text runs between the full spans."""
+    cover, pos = [], 0
+    for (s, e) in full:
+        if pos < s:
+            cover.append((pos, s, "causal"))
+        cover.append((s, e, "full"))
+        pos = e
+    if pos < L:
+        cover.append((pos, L, "causal"))
+    return cover
+
+
+def _spans_one_seq(q, k, v, q_len, full, scale=0.3):
+    L = k.shape[0]
+    return ref.paged_attention(q, [k], [v], np.array([0, q_len], np.int32), np.array([L], np.int32),
+                               k.shape[1], scale, ref.MASK_SPANS, spans=[full])[0]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_spans_equal_piecewise_segments(seed):
+    """vllm-omni piecewise PR: text runs are causal segments attending K[:end] bottom-right
+    aligned, image blocks are full segments attending K[:end] without a mask, one textbook
+    SDPA call per segment; their composition equals the general span rule, for the whole
+    sequence and for a chunk after cached context (the PR's four-segment check against
+    the dense `(q >= kv) or same_image_block` reference, on random layouts)."""
+    rng = np.random.default_rng(31 + seed)
+    L, H, Hkv, D = 41, 4, 2, 8
+    q, k, v = _rand_seq(rng, L, H, Hkv, D)
+    full = wl.span_layout(rng, L, (1, 6), (2, 9))
+    for q_len in (L, 17, 1):
+        ctx = L - q_len
+        o = _spans_one_seq(q[ctx:], k, v, q_len, full)
+        comp = np.zeros_like(o)
+        for (s, e, kv_end, causal) in ref.piecewise_segments(_cover(full, L), L):
+            lo, hi = max(s, ctx), e
+            if lo >= hi:
+                continue
+            m = causal_lower_right(hi - lo, kv_end)._materialize() if causal else None
+            comp[lo - ctx:hi - ctx] = _sdpa(q[lo:hi], k[:kv_end], v[:kv_end], 0.3, attn_mask=m,
+                                            gqa=True)
+        assert np.max(np.abs(o - comp)) <= 1e-12
+
+
+def test_spans_reductions():
+    """Full spans tiling [0, L) in steps of S are BLOCK_CAUSAL(S); no full span is CAUSAL;
+    one full span over the whole sequence is NONE."""
+    rng = np.random.default_rng(32)
+    L = 23
+    q, k, v = _rand_seq(rng, L, 2, 1, 8)
+    for q_len in (L, 9):
+        qq = q[L - q_len:]
+        tiled = [(s, min(s + 5, L)) for s in range(0, L, 5)]
+        assert np.array_equal(_spans_one_seq(qq, k, v, q_len, tiled),
+                              _one_seq(qq, k, v, q_len, ref.MASK_BLOCK_CAUSAL, 5)[0])
+        assert np.array_equal(_spans_one_seq(qq, k, v, q_len, []),
+                              _one_seq(qq, k, v, q_len, ref.MASK_CAUSAL)[0])
+        assert np.array_equal(_spans_one_seq(qq, k, v, q_len, [(0, L)]),
+                              _one_seq(qq, k, v, q_len, ref.MASK_NONE)[0])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_spans_brute_force_agrees(seed):
+    rng = np.random.default_rng(400 + seed)
+    S, H, Hkv, D = 2, 4, 2, 4
+    lens = rng.integers(3, 16, size=S).astype(np.int32)
+    qls = np.array([rng.integers(1, l + 1) for l in lens], np.int32)
+    cu = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+    q = rng.standard_normal((int(cu[-1]), H, D))
+    ks = [rng.standard_normal((int(l), Hkv, D)) for l in lens]
+    vs = [rng.standard_normal((int(l), Hkv, D)) for l in lens]
+    spans = [wl.span_layout(rng, int(l), (1, 4), (1, 6)) for l in lens]
+    o, _ = ref.paged_attention(q, ks, vs, cu, lens, Hkv, 0.35, ref.MASK_SPANS, spans=spans)
+    b = ref.brute_force(q, ks, vs, cu, lens, Hkv, 0.35, ref.MASK_SPANS, spans=spans)
+    assert np.max(np.abs(o - b)) <= 1e-12
+
+
 def test_chunked_prefill_consistency_and_decode_is_last_row():
     """Prefilling in chunks gives the rows of a one-shot causal prefill; decode is its last row."""
     rng = np.random.default_rng(31)
@@ -413,6 +490,20 @@ def test_planted_block_rule_off_by_one_is_caught(monkeypatch):
         return orig(p, a, L, mask, span)
     monkeypatch.setattr(ref, "is_visible", wrong)
     assert _caught(test_block_causal_equals_piecewise_segments)
+
+
+def test_planted_span_end_off_by_one_is_caught(monkeypatch):
+    orig = ref.full_span_of
+
+    def inclusive_end(pos, full_spans):
+        # the span end taken as inclusive: one key past each image block leaks in
+        for i, (s, e) in enumerate(full_spans):
+            if s <= pos <= e:
+                return i
+        return None
+    monkeypatch.setattr(ref, "full_span_of", inclusive_end)
+    assert _caught(test_spans_equal_piecewise_segments, 0)
+    monkeypatch.setattr(ref, "full_span_of", orig)
 
 
 def test_planted_missing_scale_and_unstable_softmax_are_caught(monkeypatch):
