@@ -12,7 +12,8 @@ per step (each K/V row of every sequence read once, Q read, O written, tables an
 lengths, plus the scatter's reads and writes) over the measured step time.
 
 The other workloads (chunked prefill, s_q=1 small-seq varlen, long block-causal
-prefill) are measured with the same library and reported in `workloads`.
+prefill, and prefill with general span lists) are measured with the same library and
+reported in `workloads`.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -64,8 +65,14 @@ def prefill_flops(w) -> float:
             vis = np.full(q, L, np.int64)
         elif w.mask == 1:
             vis = np.minimum(L, a + 1)
-        else:
+        elif w.mask == 2:
             vis = np.minimum(L, (a // w.span_len + 1) * w.span_len)
+        else:                               # span lists: up to the end of a's full span
+            vis = a + 1
+            for (b, e) in w.spans[s]:
+                inside = (a >= b) & (a < e)
+                vis = np.where(inside, e, vis)
+            vis = np.minimum(L, vis)
         tot += int(vis.sum())
     return 4.0 * w.head_dim * w.num_heads * tot
 
@@ -177,9 +184,7 @@ def run_attention_bench(w, kind, steps, warmup, flush=False):
         call = lambda: B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens,
                                                 w.scale, w.max_seq_len, ws if wsb else None)
     else:
-        call = lambda: B.paged_attention_prefill(out, d.query, d.cu_q, d.seq_lens, d.kc, d.vc,
-                                                 d.tables, w.scale, w.mask, w.span_len,
-                                                 w.max_q_len, w.max_seq_len)
+        call = lambda: d.prefill(out)
     buf = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda") if flush else None
     for _ in range(warmup):
         call()
@@ -331,7 +336,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal")
+    ap.add_argument("--workloads",
+                    default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal,mixed_spans")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibration-copy", action="store_true",

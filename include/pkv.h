@@ -182,6 +182,32 @@ int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_
                                 int32_t span_len, int32_t max_q_len, int32_t max_seq_len,
                                 pkv_dtype dtype, void* stream);
 
+/* Prefill with general span lists (vllm-omni piecewise block-causal PR: the
+ * `full_attn_spans` metadata -- image blocks attend bidirectionally, text runs
+ * causally; its dense reference "(q >= kv) or same_image_block").
+ *
+ * Same arguments and layouts as pkv_paged_attention_prefill, except the mask:
+ * the query at absolute position a of sequence s sees key p < seq_lens[s] when
+ * p <= a, or when a lies in a full span [start, end) of s and p < end.  Rows
+ * outside every full span are causal (text).  The full spans of sequence s are
+ * the pairs full_spans[2*i], full_spans[2*i+1] for i in [cu_spans[s],
+ * cu_spans[s+1]), in absolute positions, sorted by start and disjoint (a span
+ * may reach past seq_lens[s]; keys past it do not exist).  full_spans is int32
+ * [num_spans][2], cu_spans int32 [num_seqs+1], both device memory owned by the
+ * caller.  num_spans == 0 is plain CAUSAL (full_spans and cu_spans may then be
+ * NULL).  Errors: as pkv_paged_attention_prefill, plus num_spans < 0 or a NULL
+ * span array with num_spans > 0 -> PKV_ERR_INVALID_ARG. */
+int pkv_paged_attention_prefill_spans(void* out, const void* query, const int32_t* cu_seqlens_q,
+                                      const int32_t* seq_lens, const void* key_cache,
+                                      const void* value_cache, int64_t cache_block_stride,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                      int32_t block_size, float scale, const int32_t* full_spans,
+                                      const int32_t* cu_spans, int32_t num_spans,
+                                      int32_t max_q_len, int32_t max_seq_len, pkv_dtype dtype,
+                                      void* stream);
+
 /* ---- device-side precondition checks -------------------------------------------
  * The preconditions on device memory above cannot be seen by the host without a
  * copy, which the calls never make.  With checks on, each call first runs a
@@ -199,8 +225,11 @@ typedef enum {
                              /* for the gather: cu_seq_lens not non-decreasing from 0 */
                              /* or not ending at total_tokens                        */
   PKV_CHECK_TABLE = 4,       /* a used block_tables entry outside [0, num_blocks)    */
-  PKV_CHECK_CU_Q = 8         /* cu_seqlens_q: not from 0, decreasing, not ending at  */
+  PKV_CHECK_CU_Q = 8,        /* cu_seqlens_q: not from 0, decreasing, not ending at  */
                              /* num_tokens, or q_s > min(seq_lens[s], max_q_len)     */
+  PKV_CHECK_SPANS = 16       /* span lists: cu_spans not from 0 / decreasing / not   */
+                             /* ending at num_spans, or a sequence's spans unsorted, */
+                             /* overlapping, empty or starting below 0               */
 } pkv_check_bits;
 
 /* Turn the device-side checks on (enable != 0) or off for every later call in

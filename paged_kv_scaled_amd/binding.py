@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpkv.so")
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_LAUNCH = 0, -1, -2, -3, -4
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
 PKV_MASK_NONE, PKV_MASK_CAUSAL, PKV_MASK_BLOCK_CAUSAL = 0, 1, 2
-PKV_CHECK_SLOT_RANGE, PKV_CHECK_SEQ_LEN, PKV_CHECK_TABLE, PKV_CHECK_CU_Q = 1, 2, 4, 8
+PKV_CHECK_SLOT_RANGE, PKV_CHECK_SEQ_LEN, PKV_CHECK_TABLE, PKV_CHECK_CU_Q, PKV_CHECK_SPANS = 1, 2, 4, 8, 16
 
 # Every symbol include/pkv.h declares, with its ctypes signature.
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -34,6 +34,10 @@ SIGNATURES = {
                                                    _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                                    ctypes.c_int, _I32, _I32, _I32, ctypes.c_int,
                                                    _P]),
+    "pkv_paged_attention_prefill_spans": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _I32,
+                                                         _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                         _F, _P, _P, _I32, _I32, _I32,
+                                                         ctypes.c_int, _P]),
     "pkv_set_device_checks": (ctypes.c_int, [ctypes.c_int]),
     "pkv_check_device_error": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32)]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -162,6 +166,26 @@ def paged_attention_prefill(out, query, cu_seqlens_q, seq_lens, key_cache, value
                                            T, H, hkv, D, nb, bs, float(scale), int(mask),
                                            int(span_len), int(max_q_len), int(max_seq_len),
                                            _dtype_code(query), _stream()))
+
+
+def paged_attention_prefill_spans(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,
+                                  block_tables, scale: float, full_spans, cu_spans, max_q_len: int,
+                                  max_seq_len: int):
+    """Prefill with general span lists: full_spans int32 [N, 2] (start, end) pairs sequence
+    by sequence, cu_spans int32 [S+1] offsets into them (N = 0: causal)."""
+    lib = load()
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    T, H, D = query.shape
+    S = seq_lens.shape[0]
+    assert D == d and out.shape == query.shape and query.is_contiguous() and out.is_contiguous()
+    n = int(full_spans.shape[0]) if full_spans is not None else 0
+    _check(lib.pkv_paged_attention_prefill_spans(_ptr(out), _ptr(query), _ptr(cu_seqlens_q),
+                                                 _ptr(seq_lens), _ptr(key_cache), _ptr(value_cache),
+                                                 bstride, _ptr(block_tables), block_tables.shape[1],
+                                                 S, T, H, hkv, D, nb, bs, float(scale),
+                                                 _ptr(full_spans if n else None),
+                                                 _ptr(cu_spans if n else None), n, int(max_q_len),
+                                                 int(max_seq_len), _dtype_code(query), _stream()))
 
 
 def set_device_checks(enable: bool):

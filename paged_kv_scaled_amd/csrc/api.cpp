@@ -78,6 +78,76 @@ int guard_word(const uint32_t** guard, const char* what) {
   return PKV_OK;
 }
 
+// Validation and launch shared by the two prefill entry points (mask already checked).
+int prefill_common(void* out, const void* query, const int32_t* cu_seqlens_q,
+                   const int32_t* seq_lens, const void* key_cache, const void* value_cache,
+                   int64_t cache_block_stride, const int32_t* block_tables,
+                   int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_tokens,
+                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                   int32_t block_size, float scale, int mask, int32_t span_len,
+                   const int32_t* full_spans, const int32_t* cu_spans, int32_t num_spans,
+                   int32_t max_q_len, int32_t max_seq_len, pkv_dtype dtype, void* stream,
+                   const char* what) {
+  int rc;
+  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
+  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || max_seq_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs, num_tokens, max_q_len, max_seq_len must be >= 0");
+  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
+                        num_kv_heads, head_dim)) != PKV_OK)
+    return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads)) != PKV_OK) return rc;
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID_ARG, "scale is NaN");
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !query || !cu_seqlens_q || !seq_lens || !block_tables)
+    return fail(PKV_ERR_INVALID_ARG,
+                "out, query, cu_seqlens_q, seq_lens and block_tables must not be NULL");
+  if (max_q_len > max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_q_len (%d) > max_seq_len (%d)", max_q_len, max_seq_len);
+  if (num_tokens > 0 && max_q_len == 0)
+    return fail(PKV_ERR_INVALID_ARG, "max_q_len must be > 0 when num_tokens > 0");
+  if ((int64_t)max_q_len * num_seqs < num_tokens)
+    return fail(PKV_ERR_INVALID_ARG, "num_tokens (%d) > num_seqs*max_q_len (%lld)", num_tokens,
+                (long long)max_q_len * num_seqs);
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
+                (long long)max_blocks_per_seq * block_size, max_seq_len);
+  pkv::AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.seq_lens = seq_lens;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_stride = cache_block_stride;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.scale = scale;
+  a.mask = mask;
+  a.span_len = mask == PKV_MASK_BLOCK_CAUSAL ? span_len : 1;
+  a.full_spans = full_spans;
+  a.cu_spans = cu_spans;
+  a.max_q_len = max_q_len;
+  a.max_seq_len = max_seq_len;
+  a.dtype = (int)dtype;
+  if ((rc = guard_word(&a.guard, what)) != PKV_OK) return rc;
+  if (a.guard != nullptr) {
+    pkv::CheckSeqArgs c{full_spans, cu_spans, num_spans, seq_lens, nullptr, cu_seqlens_q,
+                        block_tables, num_seqs, max_blocks_per_seq, num_blocks, block_size,
+                        max_seq_len, max_q_len, num_tokens, 0};
+    if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream), what)) != PKV_OK) return rc;
+  }
+  if (pkv::prefill_mfma_supported((int)dtype, head_dim, scale))
+    return launched(pkv::launch_prefill_mfma(a, (hipStream_t)stream), what);
+  return launched(pkv::launch_prefill_valu(a, (hipStream_t)stream), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,7 +239,7 @@ int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_le
                     block_size, num_kv_heads, head_dim, max_seq_len, (int)dtype};
   if ((rc = guard_word(&a.guard, "pkv_kv_cache_gather")) != PKV_OK) return rc;
   if (a.guard != nullptr) {
-    pkv::CheckSeqArgs c{nullptr, cu_seq_lens, nullptr, block_tables, num_seqs, max_blocks_per_seq,
+    pkv::CheckSeqArgs c{nullptr, nullptr, 0, nullptr, cu_seq_lens, nullptr, block_tables, num_seqs, max_blocks_per_seq,
                         num_blocks, block_size, max_seq_len, 0, 0, total_tokens};
     if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream),
                        "pkv_kv_cache_gather (device checks)")) != PKV_OK)
@@ -240,7 +310,7 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
   a.workspace = workspace;
   if ((rc = guard_word(&a.guard, "pkv_paged_attention_decode")) != PKV_OK) return rc;
   if (a.guard != nullptr) {
-    pkv::CheckSeqArgs c{seq_lens, nullptr, nullptr, block_tables, num_seqs, max_blocks_per_seq,
+    pkv::CheckSeqArgs c{nullptr, nullptr, 0, seq_lens, nullptr, nullptr, block_tables, num_seqs, max_blocks_per_seq,
                         num_blocks, block_size, max_seq_len, 1, 0, 0};
     if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream),
                        "pkv_paged_attention_decode (device checks)")) != PKV_OK)
@@ -259,67 +329,39 @@ int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_
                                 int32_t span_len, int32_t max_q_len, int32_t max_seq_len,
                                 pkv_dtype dtype, void* stream) {
   clear_error();
-  int rc;
-  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
-  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || max_seq_len < 0)
-    return fail(PKV_ERR_INVALID_ARG, "num_seqs, num_tokens, max_q_len, max_seq_len must be >= 0");
-  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
-                        num_kv_heads, head_dim)) != PKV_OK)
-    return rc;
-  if ((rc = check_heads(num_heads, num_kv_heads)) != PKV_OK) return rc;
   if (mask != PKV_MASK_NONE && mask != PKV_MASK_CAUSAL && mask != PKV_MASK_BLOCK_CAUSAL)
     return fail(PKV_ERR_INVALID_ARG, "unknown mask mode %d", (int)mask);
   if (mask == PKV_MASK_BLOCK_CAUSAL && span_len <= 0)
     return fail(PKV_ERR_INVALID_ARG, "BLOCK_CAUSAL needs span_len > 0 (got %d)", span_len);
-  if (!(scale == scale)) return fail(PKV_ERR_INVALID_ARG, "scale is NaN");
-  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
-  if (!out || !query || !cu_seqlens_q || !seq_lens || !block_tables)
-    return fail(PKV_ERR_INVALID_ARG,
-                "out, query, cu_seqlens_q, seq_lens and block_tables must not be NULL");
-  if (max_q_len > max_seq_len)
-    return fail(PKV_ERR_INVALID_ARG, "max_q_len (%d) > max_seq_len (%d)", max_q_len, max_seq_len);
-  if (num_tokens > 0 && max_q_len == 0)
-    return fail(PKV_ERR_INVALID_ARG, "max_q_len must be > 0 when num_tokens > 0");
-  if ((int64_t)max_q_len * num_seqs < num_tokens)
-    return fail(PKV_ERR_INVALID_ARG, "num_tokens (%d) > num_seqs*max_q_len (%lld)", num_tokens,
-                (long long)max_q_len * num_seqs);
-  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
-    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
-                (long long)max_blocks_per_seq * block_size, max_seq_len);
-  pkv::AttnArgs a{};
-  a.out = out;
-  a.query = query;
-  a.cu_seqlens_q = cu_seqlens_q;
-  a.seq_lens = seq_lens;
-  a.key_cache = key_cache;
-  a.value_cache = value_cache;
-  a.block_stride = cache_block_stride;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_seqs = num_seqs;
-  a.num_tokens = num_tokens;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.num_blocks = num_blocks;
-  a.block_size = block_size;
-  a.scale = scale;
-  a.mask = (int)mask;
-  a.span_len = mask == PKV_MASK_BLOCK_CAUSAL ? span_len : 1;
-  a.max_q_len = max_q_len;
-  a.max_seq_len = max_seq_len;
-  a.dtype = (int)dtype;
-  if ((rc = guard_word(&a.guard, "pkv_paged_attention_prefill")) != PKV_OK) return rc;
-  if (a.guard != nullptr) {
-    pkv::CheckSeqArgs c{seq_lens, nullptr, cu_seqlens_q, block_tables, num_seqs, max_blocks_per_seq,
-                        num_blocks, block_size, max_seq_len, max_q_len, num_tokens, 0};
-    if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream),
-                       "pkv_paged_attention_prefill (device checks)")) != PKV_OK)
-      return rc;
-  }
-  if (pkv::prefill_mfma_supported((int)dtype, head_dim, scale))
-    return launched(pkv::launch_prefill_mfma(a, (hipStream_t)stream), "pkv_paged_attention_prefill");
-  return launched(pkv::launch_prefill_valu(a, (hipStream_t)stream), "pkv_paged_attention_prefill");
+  return prefill_common(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,
+                        cache_block_stride, block_tables, max_blocks_per_seq, num_seqs, num_tokens,
+                        num_heads, num_kv_heads, head_dim, num_blocks, block_size, scale, (int)mask,
+                        span_len, nullptr, nullptr, 0, max_q_len, max_seq_len, dtype, stream,
+                        "pkv_paged_attention_prefill");
+}
+
+int pkv_paged_attention_prefill_spans(void* out, const void* query, const int32_t* cu_seqlens_q,
+                                      const int32_t* seq_lens, const void* key_cache,
+                                      const void* value_cache, int64_t cache_block_stride,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                      int32_t block_size, float scale, const int32_t* full_spans,
+                                      const int32_t* cu_spans, int32_t num_spans,
+                                      int32_t max_q_len, int32_t max_seq_len, pkv_dtype dtype,
+                                      void* stream) {
+  clear_error();
+  if (num_spans < 0) return fail(PKV_ERR_INVALID_ARG, "num_spans must be >= 0 (got %d)", num_spans);
+  if (num_spans > 0 && (!full_spans || !cu_spans))
+    return fail(PKV_ERR_INVALID_ARG, "full_spans and cu_spans must not be NULL when num_spans > 0");
+  // no full span: plain causal prefill
+  const int mask = num_spans > 0 ? pkv::kMaskSpansHost : (int)PKV_MASK_CAUSAL;
+  return prefill_common(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,
+                        cache_block_stride, block_tables, max_blocks_per_seq, num_seqs, num_tokens,
+                        num_heads, num_kv_heads, head_dim, num_blocks, block_size, scale, mask, 1,
+                        num_spans > 0 ? full_spans : nullptr, num_spans > 0 ? cu_spans : nullptr,
+                        num_spans, max_q_len, max_seq_len, dtype, stream,
+                        "pkv_paged_attention_prefill_spans");
 }
 
 }  // extern "C"

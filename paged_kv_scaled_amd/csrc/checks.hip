@@ -61,6 +61,20 @@ check_seqs_kernel(const CheckSeqArgs a, uint32_t* word) {
         (s == a.num_seqs - 1 && q1 != a.num_tokens))
       bits |= PKV_CHECK_CU_Q;
   }
+  if (a.cu_spans != nullptr) {           // prefill with span lists: sorted, disjoint, inside the list
+    const int64_t n0 = a.cu_spans[s], n1 = a.cu_spans[s + 1];
+    bool bad_sp = (s == 0 && n0 != 0) || n1 < n0 || n0 < 0 || n1 > a.num_spans ||
+                  (s == a.num_seqs - 1 && n1 != a.num_spans);
+    if (!bad_sp) {
+      bool b2 = false;
+      for (int64_t i = n0 + lane; i < n1; i += kWave) {
+        const int32_t st = a.full_spans[2 * i], en = a.full_spans[2 * i + 1];
+        b2 |= st < 0 || en <= st || (i > n0 && st < a.full_spans[2 * i - 1]);
+      }
+      bad_sp = __any(b2);
+    }
+    if (bad_sp) bits |= PKV_CHECK_SPANS;
+  }
   if (bits != 0 && lane == 0) atomicOr(word, bits);
 }
 

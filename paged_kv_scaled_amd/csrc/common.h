@@ -83,6 +83,35 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Masks of the prefill kernels (the first three are pkv_mask_mode; SPANS is the span-list
+// entry point).
+constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskBlockCausal = 2, kMaskSpans = 3;
+
+// End of the visible key prefix of the query at absolute position a of a sequence of L
+// keys.  Every mask here sees a prefix [0, end): NONE all keys; CAUSAL p <= a; BLOCK_CAUSAL
+// up to the end of a's span of `span` tokens; SPANS up to the end of the full span
+// holding a, if any (spans[2i], spans[2i+1]) for i in [n0, n1), sorted), else p <= a.
+// The end never decreases with a.
+__device__ __forceinline__ int visible_end(int mask, int a, int L, int span,
+                                           const int32_t* spans = nullptr, int n0 = 0, int n1 = 0) {
+  if (mask == kMaskCausal) return min(L, a + 1);
+  if (mask == kMaskBlockCausal) return min(L, (a / span + 1) * span);
+  if (mask == kMaskSpans) {
+    int e = a + 1;
+    for (int i = n0; i < n1; ++i) {
+      const int s0 = spans[2 * i];
+      if (s0 > a) break;
+      const int s1 = spans[2 * i + 1];
+      if (a < s1) {
+        e = s1;
+        break;
+      }
+    }
+    return min(L, e);
+  }
+  return L;
+}
+
 // True when a device-side precondition check on this device has failed (the guard is
 // the error word, null when checks are off): every kernel then returns before it
 // reads or writes anything else.

@@ -10,6 +10,9 @@ namespace pkv {
 
 enum Dtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
+// The span-list mask (beyond the three pkv_mask_mode values), as the kernels number it.
+constexpr int kMaskSpansHost = 3;
+
 inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
 
 struct ScatterArgs {
@@ -52,8 +55,10 @@ struct AttnArgs {
   int32_t max_blocks_per_seq, num_seqs, num_tokens, num_heads, num_kv_heads, head_dim,
       num_blocks, block_size;
   float scale;
-  int mask;
+  int mask;                      // kMaskNone / kMaskCausal / kMaskBlockCausal / kMaskSpans
   int32_t span_len, max_q_len, max_seq_len;
+  const int32_t* full_spans;     // SPANS: (start, end) pairs, sequence by sequence
+  const int32_t* cu_spans;       // SPANS: [S+1] offsets into full_spans
   int dtype;
   void* workspace;               // decode only
   const uint32_t* guard;         // device error word when device checks are on, else null
@@ -62,6 +67,9 @@ struct AttnArgs {
 // What the sequence check kernel reads: lengths from seq_lens (attention) or from
 // cu_seq_lens (gather); cu_seqlens_q only for prefill.
 struct CheckSeqArgs {
+  const int32_t* full_spans;     // prefill with span lists only
+  const int32_t* cu_spans;
+  int32_t num_spans;
   const int32_t* seq_lens;
   const int32_t* cu_seq_lens;
   const int32_t* cu_seqlens_q;

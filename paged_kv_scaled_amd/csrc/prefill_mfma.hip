@@ -44,6 +44,8 @@ struct PrefillParams {
   const void* vc;
   int64_t block_stride;
   const int32_t* block_tables;
+  const int32_t* full_spans;                  // SPANS mask only
+  const int32_t* cu_spans;
   int32_t mb, S, H, Hkv, g, block_shift, mask, span;
   int32_t hw, rb_log2, head_groups, qtiles;   // WG tiling
   int32_t ngroups;                            // (sequence, kv head, head group) groups
@@ -70,11 +72,6 @@ template <typename T> __device__ __forceinline__ uint32_t kOnes2();
 template <> __device__ __forceinline__ uint32_t kOnes2<BF16>() { return 0x3F803F80u; }
 template <> __device__ __forceinline__ uint32_t kOnes2<F16>() { return 0x3C003C00u; }
 
-__device__ __forceinline__ int visible_end(int mask, int a, int L, int span) {
-  if (mask == 1) return min(L, a + 1);
-  if (mask == 2) return min(L, (a / span + 1) * span);
-  return L;
-}
 
 // LDS layouts.  K: [kBN tokens][D] with 16-byte chunk kc of row r at kc ^ (r & (NC-1)).
 // V^T: [D dims][kBN tokens], chunk (8 tokens) kc of row r at kc ^ vswz(r).
@@ -149,6 +146,7 @@ prefill_mfma_kernel(const PrefillParams p) {
   if (row0 >= qn) return;
   const int Ls = p.seq_lens[s];
   const int ctx = Ls - qn;
+  const int sp0 = p.cu_spans ? p.cu_spans[s] : 0, sp1 = p.cu_spans ? p.cu_spans[s + 1] : 0;
 
   // ---- this wave's column block -------------------------------------------------------
   int head[NCB], rbase[NCB], vis[NCB];
@@ -163,7 +161,7 @@ prefill_mfma_kernel(const PrefillParams p) {
     head[j] = kvh * p.g + (hvalid[j] ? hin : 0);
     rbase[j] = row0 + rb_i * 32;
     const int row = min(rbase[j] + lc, qn - 1);  // rows past the chunk repeat the last one
-    vis[j] = visible_end(p.mask, ctx + row, Ls, p.span);
+    vis[j] = visible_end(p.mask, ctx + row, Ls, p.span, p.full_spans, sp0, sp1);
   }
   // smallest visible end over the wave's rows: tiles below it need no mask.  Tiles that
   // no row of the wave sees are still computed: their probabilities are exactly 0
@@ -177,7 +175,7 @@ prefill_mfma_kernel(const PrefillParams p) {
   wmin = __builtin_amdgcn_readfirstlane(wmin);
   // keys the whole workgroup needs: the last row of its tile sees the most
   const int last_row = min(row0 + wg_rows, qn) - 1;
-  const int kv_end = visible_end(p.mask, ctx + last_row, Ls, p.span);
+  const int kv_end = visible_end(p.mask, ctx + last_row, Ls, p.span, p.full_spans, sp0, sp1);
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[row lc][dims ks*16+hl*8..+8]
   using S = typename T::storage;
@@ -433,6 +431,8 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
   p.block_shift = log2_exact(a.block_size);
   p.mask = a.mask;
   p.span = a.span_len;
+  p.full_spans = a.full_spans;
+  p.cu_spans = a.cu_spans;
   // kWaves column blocks per workgroup: HW heads of the kv group x RB row blocks
   int hw = 1;
   while (hw * 2 <= p.g && hw < kWaves) hw *= 2;

@@ -49,11 +49,6 @@ __device__ __forceinline__ int owner_seq(const int32_t* __restrict__ cu, int S, 
 }
 
 // One past the last key visible to the query at absolute position a.
-__device__ __forceinline__ int visible_end(int mask, int a, int L, int span) {
-  if (mask == 1) return min(L, a + 1);
-  if (mask == 2) return min(L, (a / span + 1) * span);
-  return L;
-}
 
 template <typename T, int DMAX>
 __global__ void __launch_bounds__(kValuThreads)
@@ -73,7 +68,8 @@ prefill_valu_kernel(const AttnArgs p, float scale_log2) {
   const int q0 = p.cu_seqlens_q[s];
   const int qn = p.cu_seqlens_q[s + 1] - q0;
   const int a = L - qn + (t - q0);
-  const int vend = visible_end(p.mask, a, L, p.span_len);
+  const int n0 = p.cu_spans ? p.cu_spans[s] : 0, n1 = p.cu_spans ? p.cu_spans[s + 1] : 0;
+  const int vend = visible_end(p.mask, a, L, p.span_len, p.full_spans, n0, n1);
   const int kvh = h / (p.num_heads / p.num_kv_heads);
   const int bmask = p.block_size - 1;
   int shift = 0;

@@ -267,15 +267,16 @@ def span_layout(rng: np.random.Generator, seq_len: int, text=(16, 256), image=(2
 
 
 def mixed_spans(seed: int = 5, num_seqs: int = 4, seq_len: int = 4096, dtype: str = "bf16",
-                num_heads: int = 32, q_len: Optional[int] = None, spare_blocks: int = 1) -> Workload:
+                num_heads: int = 32, q_len: Optional[int] = None, spare_blocks: int = 1,
+                text=(16, 256), image=(256, 1024), head_dim: int = 128) -> Workload:
     """General span lists (the next row after the five shapes): per sequence, text runs of
     U{16..256} tokens (causal) alternating with image blocks of U{256..1024} tokens (full),
     32 q / 8 kv heads, D 128, B 16.  q_len < seq_len makes it a chunked prefill."""
     rng = np.random.default_rng(seed)
     lens = np.full(num_seqs, seq_len, np.int32)                       # draw 1 (fixed)
-    layouts = [span_layout(rng, seq_len) for _ in range(num_seqs)]
+    layouts = [span_layout(rng, seq_len, text, image) for _ in range(num_seqs)]   # draw 1b
     ql = np.full(num_seqs, q_len or seq_len, np.int32)
-    w = build("mixed_spans", seed, dtype, lens, ql, num_heads, 8, 128, 16, MASK_SPANS,
+    w = build("mixed_spans", seed, dtype, lens, ql, num_heads, 8, head_dim, 16, MASK_SPANS,
               spare_blocks=spare_blocks, rng=rng)
     w.spans = layouts
     return w

@@ -62,6 +62,10 @@ class Dev:
         self.seq_lens = torch.from_numpy(w.seq_lens).cuda()
         self.cu_q = torch.from_numpy(w.cu_seqlens_q).cuda()
         self.cu_k = torch.from_numpy(w.cu_seq_lens).cuda()
+        if w.spans is not None:
+            fs, cs = w.span_arrays()
+            self.full_spans = torch.from_numpy(np.ascontiguousarray(fs)).cuda()
+            self.cu_spans = torch.from_numpy(cs).cuda()
 
     def write_all(self, split_new: bool = True):
         """Scatter every logical row into the cache: the cached context first, then the
@@ -89,9 +93,14 @@ class Dev:
     def prefill(self, out=None):
         w = self.w
         out = out if out is not None else torch.empty_like(self.query)
-        B.paged_attention_prefill(out, self.query, self.cu_q, self.seq_lens, self.kc, self.vc,
-                                  self.tables, w.scale, w.mask, w.span_len, w.max_q_len,
-                                  w.max_seq_len)
+        if w.mask == wl.MASK_SPANS:
+            B.paged_attention_prefill_spans(out, self.query, self.cu_q, self.seq_lens, self.kc,
+                                            self.vc, self.tables, w.scale, self.full_spans,
+                                            self.cu_spans, w.max_q_len, w.max_seq_len)
+        else:
+            B.paged_attention_prefill(out, self.query, self.cu_q, self.seq_lens, self.kc, self.vc,
+                                      self.tables, w.scale, w.mask, w.span_len, w.max_q_len,
+                                      w.max_seq_len)
         return out
 
 

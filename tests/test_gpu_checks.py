@@ -158,3 +158,21 @@ def test_checks_flag_length_over_table_capacity(checks):
     bits, msg = B.check_device_error()
     assert bits & B.PKV_CHECK_SEQ_LEN
     assert torch.all(out == 6.0)
+
+
+def test_checks_flag_unsorted_spans(checks):
+    """Two spans of one sequence swapped (the offsets stay consistent, so every read stays
+    inside the span array)."""
+    w = wl.mixed_spans(seed=74, num_seqs=2, seq_len=300, text=(5, 30), image=(10, 60))
+    d = Dev(w)
+    d.write_all()
+    fs = d.full_spans.clone()
+    n0 = int(w.span_arrays()[1][0]), int(w.span_arrays()[1][1])
+    assert n0[1] - n0[0] >= 2
+    fs[[n0[0], n0[0] + 1]] = fs[[n0[0] + 1, n0[0]]]
+    out = torch.full_like(d.query, 8.0)
+    B.paged_attention_prefill_spans(out, d.query, d.cu_q, d.seq_lens, d.kc, d.vc, d.tables, w.scale,
+                                    fs, d.cu_spans, w.max_q_len, w.max_seq_len)
+    bits, msg = B.check_device_error()
+    assert bits == B.PKV_CHECK_SPANS
+    assert torch.all(out == 8.0)

@@ -151,3 +151,65 @@ def test_prefill_single_visible_key_is_exact(gpu, dtype, head_dim):
         r0 = w.cu_seqlens_q[s]
         for h in range(w.num_heads):
             assert np.array_equal(got[r0, h], v[w.cu_seq_lens[s], h // 4]), (s, h)
+
+
+# ---- general span lists (full image spans among causal text runs) ----------------------
+
+@pytest.mark.parametrize("q_len", [None, 300])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f16", 64), ("f32", 64)])
+def test_prefill_spans(gpu, q_len, dtype, head_dim):
+    """Ragged text runs and image blocks, whole sequences and a chunk after cached context."""
+    w = wl.mixed_spans(seed=70, num_seqs=3, seq_len=700, dtype=dtype, q_len=q_len,
+                       text=(5, 60), image=(20, 200), head_dim=head_dim)
+    _run(w)
+
+
+def test_prefill_spans_full_size_sampled(gpu):
+    """4 x 4096 tokens, 32 q / 8 kv heads: rows at every span edge plus random rows."""
+    w = wl.mixed_spans()
+    rows = set()
+    rng = np.random.default_rng(71)
+    for s in range(w.num_seqs):
+        base = int(w.cu_seqlens_q[s])
+        for (a, b) in w.spans[s]:
+            rows.update(base + x for x in (a - 1, a, b - 1, b) if 0 <= x < 4096)
+        rows.update(base + int(x) for x in rng.integers(0, 4096, 6))
+    _run(w, rows=np.array(sorted(rows)), heads=[0, 5, 17, 31])
+
+
+def test_prefill_spans_tiling_equals_block_causal_and_none_equals_causal(gpu):
+    """Spans tiling the sequence in steps of 48 give BLOCK_CAUSAL(48) bit for bit; an empty
+    span list gives CAUSAL bit for bit."""
+    w = wl.chunked_prefill(seed=72, num_seqs=3, ctx_hi=150, q_lo=30, q_hi=130)
+    d = Dev(w)
+    d.write_all()
+    tiled = [[(s, s + 48) for s in range(0, int(L), 48)] for L in w.seq_lens]
+    flat = torch.tensor([p for seq in tiled for p in seq], dtype=torch.int32, device="cuda")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum([len(t) for t in tiled])]), dtype=torch.int32,
+                      device="cuda")
+    o_sp = torch.empty_like(d.query)
+    B.paged_attention_prefill_spans(o_sp, d.query, d.cu_q, d.seq_lens, d.kc, d.vc, d.tables,
+                                    w.scale, flat, cu, w.max_q_len, w.max_seq_len)
+    o_bc = torch.empty_like(d.query)
+    B.paged_attention_prefill(o_bc, d.query, d.cu_q, d.seq_lens, d.kc, d.vc, d.tables, w.scale,
+                              wl.MASK_BLOCK_CAUSAL, 48, w.max_q_len, w.max_seq_len)
+    o_none = torch.empty_like(d.query)
+    B.paged_attention_prefill_spans(o_none, d.query, d.cu_q, d.seq_lens, d.kc, d.vc, d.tables,
+                                    w.scale, None, None, w.max_q_len, w.max_seq_len)
+    o_c = torch.empty_like(d.query)
+    B.paged_attention_prefill(o_c, d.query, d.cu_q, d.seq_lens, d.kc, d.vc, d.tables, w.scale,
+                              wl.MASK_CAUSAL, 0, w.max_q_len, w.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(o_sp, o_bc) and torch.equal(o_none, o_c)
+
+
+def test_prefill_spans_rejects_bad_arguments(gpu):
+    w = wl.mixed_spans(seed=73, num_seqs=2, seq_len=200, text=(5, 30), image=(10, 60))
+    d = Dev(w)
+    out = torch.full_like(d.query, 7.0)
+    with pytest.raises(B.PkvError) as e:
+        B.paged_attention_prefill_spans(out, d.query, d.cu_q, d.seq_lens, d.kc, d.vc, d.tables,
+                                        w.scale, d.full_spans, None, w.max_q_len, w.max_seq_len)
+    assert e.value.code == B.PKV_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
