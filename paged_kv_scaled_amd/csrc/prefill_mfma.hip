@@ -234,13 +234,18 @@ prefill_mfma_kernel(const PrefillParams p) {
       const int w = d >> 1;
       const bool hi = d & 1;
       auto el = [&](int i) -> uint32_t { return hi ? (vreg[i][w] >> 16) : (vreg[i][w] & 0xFFFFu); };
+      // the same half of two tokens' words, packed by one byte permute: low halves
+      // (bytes 1:0 of each) or high halves (bytes 3:2 of each)
+      auto pair = [&](int i0, int i1) -> uint32_t {
+        return __builtin_amdgcn_perm(vreg[i1][w], vreg[i0][w], hi ? 0x07060302u : 0x05040100u);
+      };
       const int vrow = vc_ld * 8 + d;
       if constexpr (TG == 4) {
-        const uint32_t lo = el(0) | (el(1) << 16);
-        const uint32_t hi2 = el(2) | (el(3) << 16);
+        const uint32_t lo = pair(0, 1);
+        const uint32_t hi2 = pair(2, 3);
         *reinterpret_cast<u32x2_t*>(s_v + L::v_off(vrow, pos)) = (u32x2_t){lo, hi2};
       } else if constexpr (TG == 2) {
-        *reinterpret_cast<uint32_t*>(s_v + L::v_off(vrow, pos)) = el(0) | (el(1) << 16);
+        *reinterpret_cast<uint32_t*>(s_v + L::v_off(vrow, pos)) = pair(0, 1);
       } else {
         *reinterpret_cast<uint16_t*>(s_v + L::v_off(vrow, pos)) = (uint16_t)el(0);
       }
@@ -314,7 +319,8 @@ prefill_mfma_kernel(const PrefillParams p) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[j][tb][i], sacc[j][tb][i + 1]));
+          for (int i = 0; i < 16; i += 2)
+            mx = __builtin_fmaxf(__builtin_fmaxf(mx, sacc[j][tb][i]), sacc[j][tb][i + 1]);   // v_max3
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
         tmax[j] = mx;
         grow |= mx > m[j] + kLazy;
