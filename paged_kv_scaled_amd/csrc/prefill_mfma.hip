@@ -285,16 +285,33 @@ prefill_mfma_kernel(const PrefillParams p) {
     {  // every wave computes every tile of the workgroup (see the note on wmin)
       // ---- S^T = K Q^T for the wave's column block ------------------------------------
       f32x16_t sacc[NCB][2];
+      // K fragments read one k-step ahead of their MFMAs (two register sets)
+      u32x4_t ka[2][2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        ka[0][tb] = *reinterpret_cast<const u32x4_t*>(s_k + L::k_off(tb * 32 + lc, hl));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(s_k + L::k_off(tb * 32 + lc, ks * 2 + hl));
+          for (int tb = 0; tb < 2; ++tb)
+            ka[(ks + 1) & 1][tb] =
+                *reinterpret_cast<const u32x4_t*>(s_k + L::k_off(tb * 32 + lc, (ks + 1) * 2 + hl));
+        }
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int j = 0; j < NCB; ++j)
-            sacc[j][tb] = Mfma<T>::run(a, qf[j][ks], ks == 0 ? (f32x16_t){} : sacc[j][tb]);
-        }
+            sacc[j][tb] = Mfma<T>::run(ka[ks & 1][tb], qf[j][ks], ks == 0 ? (f32x16_t){} : sacc[j][tb]);
       }
+      // keep the read-ahead: the scheduler would otherwise pull each read down to its MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // LDS reads of k-steps 0, 1
+#pragma unroll
+      for (int ks = 0; ks + 2 < KS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NCB, 0);   // MFMAs of k-step ks
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // reads of k-step ks + 2
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NCB, 0);     // the last two k-steps
       // ---- online softmax (lane = one query row of each column block) ---------------
       // keys a row cannot see get -inf (only tiles that cross some row's visible end)
       if (k0 + kBN > wmin) {
