@@ -220,3 +220,19 @@ def test_decode_item_mode(gpu, H, Hkv, dtype, head_dim):
                                   [vals[i] for i in live], np.arange(len(live) + 1, dtype=np.int32),
                                   lens[live], Hkv, w.scale, wl.MASK_NONE)
     compare(got[live], want, dtype, f"item_mode H{H} Hkv{Hkv}")
+
+
+def test_decode_split_mode_with_merge(gpu):
+    """More than 1024 sequences with contexts past one split: split mode (per-sequence
+    splits of 256 keys, partials in the workspace, the split merge kernel); rows of every
+    split count are checked."""
+    rng = np.random.default_rng(81)
+    lens = rng.integers(1, 900, size=1100).astype(np.int32)
+    lens[:4] = [256, 257, 512, 899]
+    w = wl.build("split_mode", 81, "bf16", lens, np.ones(len(lens), np.int32), 8, 2, 128, 16,
+                 wl.MASK_NONE, decode=True)
+    need = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                   w.block_size, w.max_seq_len)
+    assert need > 0                                   # split mode keeps partials
+    rows = np.unique(np.concatenate([np.arange(8), rng.choice(len(lens), 200, replace=False)]))
+    _run(w, rows=rows)

@@ -213,3 +213,13 @@ def test_prefill_spans_rejects_bad_arguments(gpu):
     assert e.value.code == B.PKV_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("H,Hkv", [(32, 2), (48, 2), (6, 1)])
+def test_prefill_wide_gqa(gpu, H, Hkv):
+    """g = 16 and 24 (several head groups per kv head, the last one part-filled for 24)
+    and g = 6 (a group of 8 columns with 2 idle heads)."""
+    w = wl.chunked_prefill(seed=90 + H, num_seqs=3, ctx_hi=200, q_lo=10, q_hi=150)
+    lens = w.seq_lens
+    w = wl.build("wide_gqa", 90 + H, "bf16", lens, w.q_lens, H, Hkv, 128, 16, wl.MASK_CAUSAL)
+    _run(w)
