@@ -55,6 +55,55 @@ def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------
+# FP8 (E4M3) KV cache: quantisation and dequantisation (the FP8 KV-cache row after the five
+# shapes; the pages name FP8 paths but no scale convention, so the convention is a reading:
+# one float scale per tensor, code = E4M3(round(clamp(x * (1/scale)))), value = code * scale)
+# ----------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP 8-bit floating-point E4M3 code: sign, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent 0 holds the subnormals m/8 * 2^-6; no infinities; the codes
+    with all exponent and mantissa bits set are NaN."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_MAGS = np.array([e4m3_value(c) for c in range(0x7F)])   # codes 0x00..0x7E, increasing
+
+
+def quantize_e4m3(x: np.ndarray, inv_scale: np.float32) -> np.ndarray:
+    """uint8 codes of float values x (finite): y = float32(float32(x) * inv_scale) (one
+    rounded product), clamped to [-448, 448], then the nearest E4M3 value, a tie going to
+    the even code; the sign of y (zero included) becomes the sign bit."""
+    y = (np.asarray(x, np.float32) * np.float32(inv_scale)).astype(np.float32)
+    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    a = np.abs(y).astype(np.float64).ravel()
+    hi = np.clip(np.searchsorted(_E4M3_MAGS, a), 0, len(_E4M3_MAGS) - 1)   # first mag >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_MAGS[lo]
+    d_hi = _E4M3_MAGS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(y.ravel()), code | np.uint8(0x80), code).astype(np.uint8)
+    return code.reshape(np.shape(y))
+
+
+def dequantize_e4m3(codes: np.ndarray, scale: float) -> np.ndarray:
+    """float64 values of E4M3 codes times the tensor scale (exact: every code value is a
+    float64 and the product of two such values with <= 24 significant bits is exact)."""
+    table = np.array([e4m3_value(c) for c in range(256)])
+    return table[np.asarray(codes, np.int64)] * float(scale)
+
+
+# ----------------------------------------------------------------------------------------
 # step 1: slot_mapping scatter (raw copy) -- Spyre PR, "Description", step 1
 # ----------------------------------------------------------------------------------------
 
@@ -229,11 +278,22 @@ def split_logical(rows: np.ndarray, cu_seq_lens: np.ndarray):
     return [rows[cu_seq_lens[s]:cu_seq_lens[s + 1]] for s in range(len(cu_seq_lens) - 1)]
 
 
+def workload_kv(w):
+    """Logical K and V rows of a workload as float64: the drawn values, or, for an FP8
+    cache, what the cache holds: the quantised codes times the scales."""
+    k, v = widen(w.key, w.dtype), widen(w.value, w.dtype)
+    if getattr(w, "kv_dtype", None) == "fp8":
+        k = dequantize_e4m3(quantize_e4m3(k, np.float32(1) / np.float32(w.k_scale)), np.float32(w.k_scale))
+        v = dequantize_e4m3(quantize_e4m3(v, np.float32(1) / np.float32(w.v_scale)), np.float32(w.v_scale))
+    return k, v
+
+
 def workload_attention(w, rows=None, heads=None):
     """Oracle output for a generated workload (float64), from its logical K/V."""
     q = widen(w.query, w.dtype)
-    k = split_logical(widen(w.key, w.dtype), w.cu_seq_lens)
-    v = split_logical(widen(w.value, w.dtype), w.cu_seq_lens)
+    kk, vv = workload_kv(w)
+    k = split_logical(kk, w.cu_seq_lens)
+    v = split_logical(vv, w.cu_seq_lens)
     return paged_attention(q, k, v, w.cu_seqlens_q, w.seq_lens, w.num_kv_heads, w.scale,
                            w.mask, w.span_len, rows=rows, heads=heads,
                            spans=getattr(w, "spans", None))

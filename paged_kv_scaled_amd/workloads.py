@@ -81,6 +81,9 @@ class Workload:
     value: np.ndarray             # bits [sum L, Hkv, D]
     decode: bool = False          # one query token per sequence
     spans: Optional[list] = None  # SPANS mask: per sequence, the (start, end) full spans
+    kv_dtype: Optional[str] = None  # "fp8": the cache holds E4M3 codes of key/value
+    k_scale: float = 1.0            # FP8 cache: value = code * scale
+    v_scale: float = 1.0
 
     def span_arrays(self):
         """The span lists flattened for the library: int32 [num_spans, 2] (start, end)
@@ -282,6 +285,20 @@ def mixed_spans(seed: int = 5, num_seqs: int = 4, seq_len: int = 4096, dtype: st
     return w
 
 
+def with_fp8_cache(w: Workload, k_scale: float = 0.0173, v_scale: float = 0.0211) -> Workload:
+    """The same batch over an FP8 (E4M3) cache: kv_cache_write quantises the drawn K/V rows
+    with one scale per tensor (N(0, 1) rows reach about +-5, well inside 448 * scale)."""
+    w.kv_dtype, w.k_scale, w.v_scale = "fp8", float(np.float32(k_scale)), float(np.float32(v_scale))
+    w.name = w.name + "_fp8"
+    return w
+
+
+def decode_batch_fp8(seed: int = 1, **kw) -> Workload:
+    """The decode batch (64 sequences, contexts U[256, 4096], 32 q / 8 kv heads, D 128,
+    B 16) over an FP8 cache."""
+    return with_fp8_cache(decode_batch(seed=seed, **kw))
+
+
 CONFIGS = {
     "tiny_prefill": tiny_prefill,
     "decode_batch": decode_batch,
@@ -289,6 +306,7 @@ CONFIGS = {
     "smallseq_varlen": smallseq_varlen,
     "long_block_causal": long_block_causal,
     "mixed_spans": mixed_spans,
+    "decode_batch_fp8": decode_batch_fp8,
 }
 
 

@@ -520,3 +520,58 @@ def test_planted_missing_scale_and_unstable_softmax_are_caught(monkeypatch):
         return o[:, ::-1].copy(), l
     monkeypatch.setattr(ref, "attend", transposed_v)
     assert _caught(test_full_prefill_equals_sdpa, ref.MASK_NONE)
+
+
+# ----------------------------------------------------------------------------------------
+# FP8 (E4M3) cache quantisation
+# ----------------------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_torch_float8():
+    """Every one of the 256 codes decodes as torch's float8_e4m3fn does (the OCP format)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    t = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = np.array([ref.e4m3_value(c) for c in range(256)])
+    nan = np.isnan(t)
+    assert np.array_equal(nan, np.isnan(mine))
+    assert np.array_equal(t[~nan], mine[~nan])
+    assert ref.e4m3_value(0x7E) == 448.0 and ref.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_e4m3_quantize_matches_torch_on_random_and_tie_values():
+    rng = np.random.default_rng(91)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 40,
+                        rng.standard_normal(2000).astype(np.float32) * 0.01])
+    # every midpoint between neighbouring codes: the ties
+    mags = np.array([ref.e4m3_value(c) for c in range(0x7F)])
+    mids = ((mags[1:] + mags[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, -mids, np.float32([0.0, -0.0, 448.0, -448.0])])
+    mine = ref.quantize_e4m3(x, np.float32(1))
+    t = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, t)
+
+
+def test_e4m3_quantize_round_trip_ties_and_saturation():
+    """Definition checks: each finite code's value maps back to that code; a midpoint goes
+    to the even code; values past 448 saturate; the product with 1/scale is one float32
+    rounding."""
+    vals = np.array([ref.e4m3_value(c) for c in range(0x7F)], np.float32)
+    assert np.array_equal(ref.quantize_e4m3(vals, np.float32(1)), np.arange(0x7F, dtype=np.uint8))
+    assert np.array_equal(ref.quantize_e4m3(-vals[1:], np.float32(1)),
+                          (np.arange(1, 0x7F) | 0x80).astype(np.uint8))
+    mids = ((vals[1:].astype(np.float64) + vals[:-1]) / 2).astype(np.float32)
+    got = ref.quantize_e4m3(mids, np.float32(1)).astype(int)
+    assert np.all(got % 2 == 0) and np.all((got == np.arange(0x7E)) | (got == np.arange(1, 0x7F)))
+    assert list(ref.quantize_e4m3(np.float32([1e6, -1e6, 449.0]), np.float32(1))) == [0x7E, 0xFE, 0x7E]
+    inv = np.float32(1) / np.float32(0.0173)
+    x = np.float32([1.2345, -3.5, 0.01])
+    assert np.array_equal(ref.quantize_e4m3(x, inv), ref.quantize_e4m3((x * inv).astype(np.float32), np.float32(1)))
+
+
+def test_fp8_workload_oracle_uses_dequantised_rows():
+    w = wl.with_fp8_cache(wl.random_small(5, "bf16", head_dim=8))
+    k, v = ref.workload_kv(w)
+    kc = ref.quantize_e4m3(ref.widen(w.key, "bf16"), np.float32(1) / np.float32(w.k_scale))
+    assert np.array_equal(k, ref.dequantize_e4m3(kc, w.k_scale))
+    # the quantisation error stays inside half a code step (relative 2^-4) plus the subnormal step
+    kw = ref.widen(w.key, "bf16")
+    assert np.all(np.abs(k - kw) <= np.abs(kw) * 2.0 ** -4 + 2.0 ** -10 * w.k_scale)
