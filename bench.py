@@ -42,16 +42,19 @@ def decode_bytes(w) -> int:
     O out, the block-table entries used and the lengths."""
     import numpy as np
     eb = 2 if w.dtype != "f32" else 4
+    cb = 1 if getattr(w, "kv_dtype", None) == "fp8" else eb      # cache element bytes
     L = w.seq_lens.astype(np.int64)
-    kv = int(L.sum()) * w.num_kv_heads * w.head_dim * eb * 2
+    kv = int(L.sum()) * w.num_kv_heads * w.head_dim * cb * 2
     qo = 2 * w.num_seqs * w.num_heads * w.head_dim * eb
     tables = int(((L + w.block_size - 1) // w.block_size).sum()) * 4
     return kv + qo + tables + w.num_seqs * 4
 
 
 def scatter_bytes(w, rows) -> int:
+    """K and V rows read in the source type and written in the cache type, plus slots."""
     eb = 2 if w.dtype != "f32" else 4
-    return 2 * len(rows) * w.num_kv_heads * w.head_dim * eb * 2 + len(rows) * 8
+    cb = 1 if getattr(w, "kv_dtype", None) == "fp8" else eb
+    return len(rows) * w.num_kv_heads * w.head_dim * (eb + cb) * 2 + len(rows) * 8
 
 
 def prefill_flops(w) -> float:
@@ -181,8 +184,13 @@ def run_attention_bench(w, kind, steps, warmup, flush=False):
     if kind == "decode":
         wsb = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, w.max_seq_len)
         ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
-        call = lambda: B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens,
-                                                w.scale, w.max_seq_len, ws if wsb else None)
+        if d.fp8:
+            call = lambda: B.paged_attention_decode_fp8(out, d.query, d.kc, d.vc, d.tables,
+                                                        d.seq_lens, w.scale, w.k_scale, w.v_scale,
+                                                        w.max_seq_len, ws if wsb else None)
+        else:
+            call = lambda: B.paged_attention_decode(out, d.query, d.kc, d.vc, d.tables, d.seq_lens,
+                                                    w.scale, w.max_seq_len, ws if wsb else None)
     else:
         call = lambda: d.prefill(out)
     buf = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda") if flush else None
@@ -200,7 +208,7 @@ def run_attention_bench(w, kind, steps, warmup, flush=False):
     ts = Timer()
     for _ in range(max(3, steps // 4)):
         e = ts.start()
-        B.kv_cache_write(d.key, d.value, d.slots, d.kc, d.vc)
+        d.write(d.key, d.value, d.slots)
         ts.stop(e)
     return ms, ts.ms()
 
@@ -337,7 +345,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads",
-                    default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal,mixed_spans")
+                    default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal,mixed_spans,"
+                            "decode_batch_fp8")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibration-copy", action="store_true",

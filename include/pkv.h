@@ -19,7 +19,11 @@
  *   leaves a message in pkv_last_error() (CSA2 Vanilla golden PR,
  *   "Description": unsupported modes are rejected before anything is written;
  *   review thread: a retry must not fail on stale state).
- * - Element types: dtype applies to query, key, value, caches and output alike.
+ * - Element types: dtype applies to query, key, value, caches and output alike,
+ *   except in the FP8-cache entry points (*_fp8), whose caches hold E4M3 codes.
+ * - Alignment: the attention calls read rows in 16-byte vectors, so out, query
+ *   and both caches must be 16-byte aligned and cache_block_stride a multiple
+ *   of 16 bytes (INVALID_ARG otherwise).
  * - Cache layout: key_cache and value_cache are each [num_blocks, block_size,
  *   num_kv_heads, head_dim] with the first dimension strided by
  *   cache_block_stride ELEMENTS; inside a block the layout is dense.  A combined
@@ -69,7 +73,10 @@ typedef enum {
   PKV_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch             */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+/* PKV_FP8_E4M3 (one-byte OCP E4M3 codes) names an FP8 cache; only
+ * pkv_kv_cache_gather takes it as its dtype (a raw byte copy).  The FP8 entry
+ * points below take the caches as codes and dtype for the other tensors. */
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
 
 typedef enum { PKV_MASK_NONE = 0, PKV_MASK_CAUSAL = 1, PKV_MASK_BLOCK_CAUSAL = 2 } pkv_mask_mode;
 
@@ -96,6 +103,32 @@ int pkv_kv_cache_write(const void* key, const void* value, int64_t kv_token_stri
                        void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
                        int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                        pkv_dtype dtype, void* stream);
+
+/*
+ * FP8 KV cache (E4M3).  The pages accept FP8 staging of cache rows (CSA2
+ * Vanilla golden PR, "Description") and name FP8 paths (vllm-omni piecewise
+ * block-causal PR, review thread) but give no scale convention; the one here:
+ * one float scale per cache tensor (k_scale for keys, v_scale for values),
+ *   code  = E4M3_RNE(clamp(float32(x * float32(1 / scale)), -448, 448))
+ *   value = e4m3(code) * scale
+ * with OCP E4M3 (bias 7, max 448, 0x7F / 0xFF NaN, no infinities), ties to
+ * even, subnormals kept; a NaN input gives a NaN code.  Attention over such a
+ * cache computes softmax(scale * q . (e4m3(k_code) * k_scale)) . (e4m3(v_code)
+ * * v_scale) with the precision rules above (the widening to bf16 / fp16 is
+ * exact).  Scales must be positive and finite with finite reciprocals.
+ *
+ * pkv_kv_cache_write_fp8 -- pkv_kv_cache_write that quantises: key and value
+ * are dtype (F32, F16 or BF16) rows as in pkv_kv_cache_write; the caches are
+ * byte arrays of the same [num_blocks, block_size, num_kv_heads, head_dim]
+ * layout (cache_block_stride in bytes).  kv_token_stride and
+ * cache_block_stride must be multiples of 4 and the pointers 4-element aligned.
+ * Errors as pkv_kv_cache_write, plus INVALID_ARG for scales or alignment.
+ */
+int pkv_kv_cache_write_fp8(const void* key, const void* value, int64_t kv_token_stride,
+                           const int64_t* slot_mapping, int32_t num_tokens, void* key_cache,
+                           void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           float k_scale, float v_scale, pkv_dtype dtype, void* stream);
 
 /*
  * pkv_kv_cache_gather -- step 2 of the Spyre PR ("gather the relevant KV entries
@@ -153,6 +186,23 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
                                int32_t block_size, float scale, int32_t max_seq_len,
                                void* workspace, size_t workspace_bytes, pkv_dtype dtype,
                                void* stream);
+
+/*
+ * pkv_paged_attention_decode_fp8 -- pkv_paged_attention_decode over FP8 caches
+ * written by pkv_kv_cache_write_fp8 (conventions above).  query and out are
+ * dtype (PKV_BF16 or PKV_F16); the caches are byte arrays with
+ * cache_block_stride in bytes (a multiple of 16).  Same workspace size as
+ * pkv_paged_attention_decode.  Errors as pkv_paged_attention_decode, plus
+ * UNSUPPORTED for a dtype other than BF16 / F16 and INVALID_ARG for scales.
+ */
+int pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, int64_t cache_block_stride,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                   int32_t block_size, float scale, float k_scale, float v_scale,
+                                   int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                                   pkv_dtype dtype, void* stream);
 
 /*
  * pkv_paged_attention_prefill -- prefill and chunked prefill over a flat (THD)

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpkv.so")
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_LAUNCH = 0, -1, -2, -3, -4
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 PKV_MASK_NONE, PKV_MASK_CAUSAL, PKV_MASK_BLOCK_CAUSAL = 0, 1, 2
 PKV_CHECK_SLOT_RANGE, PKV_CHECK_SEQ_LEN, PKV_CHECK_TABLE, PKV_CHECK_CU_Q, PKV_CHECK_SPANS = 1, 2, 4, 8, 16
 
@@ -24,12 +24,17 @@ _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctype
 SIGNATURES = {
     "pkv_kv_cache_write": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _P, _P, _I64, _I32, _I32, _I32,
                                           _I32, ctypes.c_int, _P]),
+    "pkv_kv_cache_write_fp8": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _P, _P, _I64, _I32, _I32,
+                                              _I32, _I32, _F, _F, ctypes.c_int, _P]),
     "pkv_kv_cache_gather": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32, _I32,
                                            _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
     "pkv_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32,
                                                   _I32, _I32, _I32, _I32, _F, _I32, _P, _SZ,
                                                   ctypes.c_int, _P]),
+    "pkv_paged_attention_decode_fp8": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
+                                                      _I32, _I32, _I32, _I32, _I32, _F, _F, _F,
+                                                      _I32, _P, _SZ, ctypes.c_int, _P]),
     "pkv_paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32,
                                                    _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                                    ctypes.c_int, _I32, _I32, _I32, ctypes.c_int,
@@ -86,7 +91,8 @@ def last_error() -> str:
 
 def _dtype_code(t) -> int:
     import torch
-    return {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}[t.dtype]
+    return {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+            torch.uint8: PKV_FP8_E4M3, torch.float8_e4m3fn: PKV_FP8_E4M3}[t.dtype]
 
 
 def _stream():
@@ -119,6 +125,21 @@ def kv_cache_write(key, value, slot_mapping, key_cache, value_cache):
                                   _dtype_code(key), _stream()))
 
 
+def kv_cache_write_fp8(key, value, slot_mapping, key_cache, value_cache, k_scale: float,
+                       v_scale: float):
+    """kv_cache_write into uint8 caches of E4M3 codes (value = code * scale)."""
+    lib = load()
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    T = key.shape[0]
+    assert key.shape == value.shape and key.stride() == value.stride()
+    assert key.stride()[1:] == (d, 1) and key.shape[1:] == (hkv, d)
+    assert key_cache.element_size() == 1
+    _check(lib.pkv_kv_cache_write_fp8(_ptr(key), _ptr(value), key.stride(0), _ptr(slot_mapping),
+                                      T, _ptr(key_cache), _ptr(value_cache), bstride, nb, bs, hkv,
+                                      d, float(k_scale), float(v_scale), _dtype_code(key),
+                                      _stream()))
+
+
 def kv_cache_gather(key_out, value_out, cu_seq_lens, key_cache, value_cache, block_tables,
                     max_seq_len: int):
     lib = load()
@@ -149,6 +170,24 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, seq
                                           block_tables.shape[1], _ptr(seq_lens), S, H, hkv, D, nb,
                                           bs, float(scale), int(max_seq_len), _ptr(workspace),
                                           ws_bytes, _dtype_code(query), _stream()))
+
+
+def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables, seq_lens,
+                               scale: float, k_scale: float, v_scale: float, max_seq_len: int,
+                               workspace=None):
+    """paged_attention_decode over uint8 caches of E4M3 codes; query/out bf16 or fp16."""
+    lib = load()
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    S, H, D = query.shape
+    assert D == d and out.shape == query.shape and query.is_contiguous() and out.is_contiguous()
+    assert key_cache.element_size() == 1
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attention_decode_fp8(_ptr(out), _ptr(query), _ptr(key_cache),
+                                              _ptr(value_cache), bstride, _ptr(block_tables),
+                                              block_tables.shape[1], _ptr(seq_lens), S, H, hkv, D,
+                                              nb, bs, float(scale), float(k_scale), float(v_scale),
+                                              int(max_seq_len), _ptr(workspace), ws_bytes,
+                                              _dtype_code(query), _stream()))
 
 
 def paged_attention_prefill(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,

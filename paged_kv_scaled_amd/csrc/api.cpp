@@ -31,6 +31,29 @@ int check_dtype(int dtype) {
   return PKV_OK;
 }
 
+// FP8 cache scales: finite and positive (their reciprocal must be finite too).
+int check_fp8_scales(float k_scale, float v_scale) {
+  const float lim = 3.0e38f;
+  if (!(k_scale > 0.f && k_scale < lim && 1.f / k_scale < lim) ||
+      !(v_scale > 0.f && v_scale < lim && 1.f / v_scale < lim))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite "
+                "with finite reciprocals (got %g, %g)", (double)k_scale, (double)v_scale);
+  return PKV_OK;
+}
+
+bool aligned(const void* p, unsigned n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
+// The attention kernels read cache rows and query/output rows in 16-byte vectors (8-byte
+// ones for 64-dim FP8 rows): every row start must be 16-byte aligned.
+int check_attn_alignment(const void* out, const void* query, const void* kc, const void* vc,
+                         int64_t cache_block_stride, int elem_bytes) {
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(kc, 16) || !aligned(vc, 16) ||
+      (cache_block_stride * elem_bytes) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "out, query, key_cache and value_cache must be 16-byte "
+                "aligned and cache_block_stride a multiple of 16 bytes");
+  return PKV_OK;
+}
+
 // Geometry shared by every call that reads or writes the cache.
 int check_cache(const void* kc, const void* vc, int64_t block_stride, int32_t num_blocks,
                 int32_t block_size, int32_t num_kv_heads, int32_t head_dim) {
@@ -111,6 +134,9 @@ int prefill_common(void* out, const void* query, const int32_t* cu_seqlens_q,
   if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
     return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
                 (long long)max_blocks_per_seq * block_size, max_seq_len);
+  if ((rc = check_attn_alignment(out, query, key_cache, value_cache, cache_block_stride,
+                                 dtype == PKV_F32 ? 4 : 2)) != PKV_OK)
+    return rc;
   pkv::AttnArgs a{};
   a.out = out;
   a.query = query;
@@ -148,6 +174,72 @@ int prefill_common(void* out, const void* query, const int32_t* cu_seqlens_q,
   return launched(pkv::launch_prefill_valu(a, (hipStream_t)stream), what);
 }
 
+// Validation and launch shared by the two decode entry points (dtype already checked).
+int decode_common(void* out, const void* query, const void* key_cache, const void* value_cache,
+                  int64_t cache_block_stride, const int32_t* block_tables,
+                  int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                  int32_t block_size, float scale, bool kv_fp8, float k_scale, float v_scale,
+                  int32_t max_seq_len, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                  void* stream, const char* what) {
+  int rc;
+  if (num_seqs < 0 || max_seq_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs and max_seq_len must be >= 0");
+  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
+                        num_kv_heads, head_dim)) != PKV_OK)
+    return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads)) != PKV_OK) return rc;
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID_ARG, "scale is NaN");
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !block_tables || !seq_lens)
+    return fail(PKV_ERR_INVALID_ARG, "out, query, block_tables and seq_lens must not be NULL");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
+                (long long)max_blocks_per_seq * block_size, max_seq_len);
+  if ((rc = check_attn_alignment(out, query, key_cache, value_cache, cache_block_stride,
+                                 kv_fp8 ? 1 : (dtype == PKV_F32 ? 4 : 2))) != PKV_OK)
+    return rc;
+  const pkv::DecodePlan plan =
+      pkv::decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len);
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return fail(PKV_ERR_WORKSPACE, "decode workspace of %zu bytes required (got %zu at %p)",
+                plan.workspace_bytes, workspace_bytes, workspace);
+  pkv::AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.seq_lens = seq_lens;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_stride = cache_block_stride;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.scale = scale;
+  a.mask = PKV_MASK_NONE;
+  a.max_seq_len = max_seq_len;
+  a.max_q_len = 1;
+  a.dtype = (int)dtype;
+  a.workspace = workspace;
+  a.kv_fp8 = kv_fp8 ? 1 : 0;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  if ((rc = guard_word(&a.guard, what)) != PKV_OK) return rc;
+  if (a.guard != nullptr) {
+    pkv::CheckSeqArgs c{nullptr, nullptr, 0, seq_lens, nullptr, nullptr, block_tables, num_seqs, max_blocks_per_seq,
+                        num_blocks, block_size, max_seq_len, 1, 0, 0};
+    if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream),
+                       what)) != PKV_OK)
+      return rc;
+  }
+  return launched(pkv::launch_decode(a, plan, (hipStream_t)stream), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -175,7 +267,8 @@ int pkv_check_device_error(void* stream, uint32_t* bits) {
       {PKV_CHECK_SLOT_RANGE, "slot_mapping entry >= num_blocks*block_size"},
       {PKV_CHECK_SEQ_LEN, "sequence length outside [0, min(max_seq_len, max_blocks_per_seq*block_size)]"},
       {PKV_CHECK_TABLE, "block_tables entry outside [0, num_blocks)"},
-      {PKV_CHECK_CU_Q, "cu_seqlens_q inconsistent"}};
+      {PKV_CHECK_CU_Q, "cu_seqlens_q inconsistent"},
+      {PKV_CHECK_SPANS, "span lists inconsistent"}};
   for (const auto& n : names) {
     if (!(v & n.bit)) continue;
     if (list[0]) strncat(list, "; ", sizeof(list) - strlen(list) - 1);
@@ -214,6 +307,45 @@ int pkv_kv_cache_write(const void* key, const void* value, int64_t kv_token_stri
   return launched(pkv::launch_kv_scatter(a, (hipStream_t)stream), "pkv_kv_cache_write");
 }
 
+int pkv_kv_cache_write_fp8(const void* key, const void* value, int64_t kv_token_stride,
+                           const int64_t* slot_mapping, int32_t num_tokens, void* key_cache,
+                           void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           float k_scale, float v_scale, pkv_dtype dtype, void* stream) {
+  clear_error();
+  int rc;
+  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
+  if ((rc = check_fp8_scales(k_scale, v_scale)) != PKV_OK) return rc;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
+                        num_kv_heads, head_dim)) != PKV_OK)
+    return rc;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "key, value and slot_mapping must not be NULL");
+  if (kv_token_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PKV_ERR_INVALID_ARG, "kv_token_stride %lld < num_kv_heads*head_dim = %lld",
+                (long long)kv_token_stride, (long long)num_kv_heads * head_dim);
+  const unsigned eb = dtype == PKV_F32 ? 4u : 2u;
+  if (kv_token_stride % 4 != 0 || !aligned(key, 4 * eb) || !aligned(value, 4 * eb) ||
+      cache_block_stride % 4 != 0 || !aligned(key_cache, 4) || !aligned(value_cache, 4))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_kv_cache_write_fp8: kv_token_stride and "
+                "cache_block_stride must be multiples of 4 and key/value/cache pointers aligned "
+                "to 4 elements");
+  pkv::ScatterArgs a{key, value, kv_token_stride, slot_mapping, num_tokens, key_cache,
+                     value_cache, cache_block_stride, num_blocks, block_size, num_kv_heads,
+                     head_dim, (int)dtype};
+  if ((rc = guard_word(&a.guard, "pkv_kv_cache_write_fp8")) != PKV_OK) return rc;
+  if (a.guard != nullptr &&
+      (rc = launched(pkv::launch_check_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size,
+                                             (hipStream_t)stream),
+                     "pkv_kv_cache_write_fp8 (device checks)")) != PKV_OK)
+    return rc;
+  // the reciprocals are rounded once to fp32 here; the kernel multiplies by them
+  return launched(pkv::launch_kv_scatter_fp8(a, 1.f / k_scale, 1.f / v_scale, (hipStream_t)stream),
+                  "pkv_kv_cache_write_fp8");
+}
+
 int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_lens,
                         const void* key_cache, const void* value_cache,
                         int64_t cache_block_stride, const int32_t* block_tables,
@@ -222,7 +354,7 @@ int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_le
                         int32_t head_dim, int32_t max_seq_len, pkv_dtype dtype, void* stream) {
   clear_error();
   int rc;
-  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
+  if (dtype != PKV_FP8_E4M3 && (rc = check_dtype(dtype)) != PKV_OK) return rc;
   if (num_seqs < 0 || total_tokens < 0 || max_seq_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs, total_tokens and max_seq_len must be >= 0");
   if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
@@ -268,55 +400,30 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
   clear_error();
   int rc;
   if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
-  if (num_seqs < 0 || max_seq_len < 0)
-    return fail(PKV_ERR_INVALID_ARG, "num_seqs and max_seq_len must be >= 0");
-  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
-                        num_kv_heads, head_dim)) != PKV_OK)
-    return rc;
-  if ((rc = check_heads(num_heads, num_kv_heads)) != PKV_OK) return rc;
-  if (!(scale == scale)) return fail(PKV_ERR_INVALID_ARG, "scale is NaN");
-  if (num_seqs == 0) return PKV_OK;
-  if (!out || !query || !block_tables || !seq_lens)
-    return fail(PKV_ERR_INVALID_ARG, "out, query, block_tables and seq_lens must not be NULL");
-  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
-    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
-                (long long)max_blocks_per_seq * block_size, max_seq_len);
-  const pkv::DecodePlan plan =
-      pkv::decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_seq_len);
-  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
-    return fail(PKV_ERR_WORKSPACE, "decode workspace of %zu bytes required (got %zu at %p)",
-                plan.workspace_bytes, workspace_bytes, workspace);
-  pkv::AttnArgs a{};
-  a.out = out;
-  a.query = query;
-  a.seq_lens = seq_lens;
-  a.key_cache = key_cache;
-  a.value_cache = value_cache;
-  a.block_stride = cache_block_stride;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_seqs = num_seqs;
-  a.num_tokens = num_seqs;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.num_blocks = num_blocks;
-  a.block_size = block_size;
-  a.scale = scale;
-  a.mask = PKV_MASK_NONE;
-  a.max_seq_len = max_seq_len;
-  a.max_q_len = 1;
-  a.dtype = (int)dtype;
-  a.workspace = workspace;
-  if ((rc = guard_word(&a.guard, "pkv_paged_attention_decode")) != PKV_OK) return rc;
-  if (a.guard != nullptr) {
-    pkv::CheckSeqArgs c{nullptr, nullptr, 0, seq_lens, nullptr, nullptr, block_tables, num_seqs, max_blocks_per_seq,
-                        num_blocks, block_size, max_seq_len, 1, 0, 0};
-    if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream),
-                       "pkv_paged_attention_decode (device checks)")) != PKV_OK)
-      return rc;
-  }
-  return launched(pkv::launch_decode(a, plan, (hipStream_t)stream), "pkv_paged_attention_decode");
+  return decode_common(out, query, key_cache, value_cache, cache_block_stride, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                       num_blocks, block_size, scale, false, 1.f, 1.f, max_seq_len, workspace,
+                       workspace_bytes, dtype, stream, "pkv_paged_attention_decode");
+}
+
+int pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, int64_t cache_block_stride,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                   int32_t block_size, float scale, float k_scale, float v_scale,
+                                   int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                                   pkv_dtype dtype, void* stream) {
+  clear_error();
+  int rc;
+  if (dtype != PKV_BF16 && dtype != PKV_F16)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_attention_decode_fp8: query dtype %d is not "
+                "PKV_BF16 or PKV_F16", (int)dtype);
+  if ((rc = check_fp8_scales(k_scale, v_scale)) != PKV_OK) return rc;
+  return decode_common(out, query, key_cache, value_cache, cache_block_stride, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                       num_blocks, block_size, scale, true, k_scale, v_scale, max_seq_len,
+                       workspace, workspace_bytes, dtype, stream, "pkv_paged_attention_decode_fp8");
 }
 
 int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_seqlens_q,

@@ -23,6 +23,14 @@ struct BF16 { using storage = uint16_t; static constexpr int bytes = 2; };
 struct F16  { using storage = uint16_t; static constexpr int bytes = 2; };
 struct F32  { using storage = uint32_t; static constexpr int bytes = 4; };
 
+// An FP8 (E4M3) KV cache read with a bf16 / fp16 query: the query, output and arithmetic
+// are those of the base tag; keys and values are widened from their codes on load.
+struct BF16K8 : BF16 {};
+struct F16K8 : F16 {};
+template <typename T> struct KvFp8 { static constexpr bool value = false; };
+template <> struct KvFp8<BF16K8> { static constexpr bool value = true; };
+template <> struct KvFp8<F16K8> { static constexpr bool value = true; };
+
 // ---- scalar conversions ---------------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -59,6 +67,17 @@ __device__ __forceinline__ float dot2(BF16, uint32_t a, uint32_t b, float acc) {
 __device__ __forceinline__ float dot2(F16, uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
                                 acc, false);
+}
+
+// Two E4M3 codes (bytes 0-1, or 2-3 with HI) of a word -> the packed pair of the compute
+// type (exact: every E4M3 value is a bf16 and an fp16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t widen_fp8x2(BF16, uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t widen_fp8x2(F16, uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI));
 }
 
 // ---- cross-lane helpers ---------------------------------------------------------------

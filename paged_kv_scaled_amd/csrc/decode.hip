@@ -57,6 +57,12 @@ struct DecodeShape {
   static constexpr int EPL = VPL * EPV;            // elements per lane per row
   static constexpr int STEP = 2 * TPR;             // keys per step (two rounds)
   static_assert(NV >= 1 && NV % LPT == 0, "head_dim / dtype combination");
+  // 16-byte vector (of the query / output row) that lane column c holds as its v-th:
+  // interleaved over the columns, or, with an FP8 cache, the lane's own contiguous
+  // EPL elements (the elements its one FP8 load covers).
+  static __device__ __forceinline__ int vec(int v, int c) {
+    return KvFp8<T>::value ? c * VPL + v : v * LPT + c;
+  }
 };
 
 // Steps whose loads are issued together: keep the K/V registers of one batch of steps
@@ -79,7 +85,8 @@ struct DecodeParams {
   float* ws_ml;             // [H, slots_per_head, 2]  (max in log2 units, sum)
   int64_t total_items;      // split mode: S*nsplit*HG; stream mode: HG*nranges
   int32_t mb, S, H, Hkv, g, block_shift, split_len, nsplit, groups_per_kv, nranges;
-  float scale_log2;
+  float scale_log2;         // scale * log2(e) (times k_scale for an FP8 cache)
+  float out_scale;          // v_scale for an FP8 cache, else 1
   const uint32_t* guard;    // device error word when device checks are on, else null
 };
 
@@ -103,6 +110,60 @@ __device__ __forceinline__ void table_window_load(TableWindow& tw, const int32_t
   tw.ids = table[min(first_page + lane, last_page)];
 }
 
+// Round r of a step: this lane's part of the K and V rows at element offset `row`.
+template <typename T, int D>
+__device__ __forceinline__ void load_row(Step<T, D>& st, int r, const DecodeParams& p, int64_t row,
+                                         int c) {
+  using C = DecodeShape<T, D>;
+  if constexpr (KvFp8<T>::value) {
+    // EPL codes per lane, one load each for K and V, widened to the compute pairs
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.kc) + row + c * C::EPL;
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.vc) + row + c * C::EPL;
+    constexpr int NW = C::EPL / 4;                  // code words per lane
+    uint32_t kw[NW], vw[NW];
+    if constexpr (NW == 4) {
+      const u32x4_t kk = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb));
+      const u32x4_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kw[i] = kk[i];
+        vw[i] = vv[i];
+      }
+    } else {
+      static_assert(NW == 2, "FP8 rows of 8 or 16 codes per lane");
+      const u32x2_t kk = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(kb));
+      const u32x2_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(vb));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        kw[i] = kk[i];
+        vw[i] = vv[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      st.k[r][2 * i] = widen_fp8x2<false>(T{}, kw[i]);
+      st.k[r][2 * i + 1] = widen_fp8x2<true>(T{}, kw[i]);
+      st.v[r][2 * i] = widen_fp8x2<false>(T{}, vw[i]);
+      st.v[r][2 * i + 1] = widen_fp8x2<true>(T{}, vw[i]);
+    }
+  } else {
+    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const typename T::storage*>(p.kc) + row);
+    const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const typename T::storage*>(p.vc) + row);
+#pragma unroll
+    for (int v = 0; v < C::VPL; ++v) {
+      const u32x4_t kk = __builtin_nontemporal_load(kp + v * C::LPT + c);
+      const u32x4_t vv = __builtin_nontemporal_load(vp + v * C::LPT + c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        st.k[r][v * 4 + w] = kk[w];
+        st.v[r][v * 4 + w] = vv[w];
+      }
+    }
+  }
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void load_step(Step<T, D>& st, const DecodeParams& p,
                                           const TableWindow& tw, int64_t head_off, int base,
@@ -121,20 +182,7 @@ __device__ __forceinline__ void load_step(Step<T, D>& st, const DecodeParams& p,
     const int idx = ((pos >> p.block_shift) - tw.chunk_base) & (kWave - 1);
     const int64_t blk = __shfl(tw.ids, idx, kWave);
     const int64_t row = blk * p.block_stride + (int64_t)(pos & bmask) * row_elems + head_off;
-    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(
-        reinterpret_cast<const typename T::storage*>(p.kc) + row);
-    const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(
-        reinterpret_cast<const typename T::storage*>(p.vc) + row);
-#pragma unroll
-    for (int v = 0; v < C::VPL; ++v) {
-      const u32x4_t kk = __builtin_nontemporal_load(kp + v * C::LPT + c);
-      const u32x4_t vv = __builtin_nontemporal_load(vp + v * C::LPT + c);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        st.k[r][v * 4 + w] = kk[w];
-        st.v[r][v * 4 + w] = vv[w];
-      }
-    }
+    load_row<T, D>(st, r, p, row, c);
   }
 }
 
@@ -240,7 +288,7 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, int s, int
         reinterpret_cast<const S*>(p.query) + ((int64_t)s * p.H + h0 + (hh < nh ? hh : 0)) * D);
 #pragma unroll
     for (int v = 0; v < C::VPL; ++v) {
-      const u32x4_t qq = qp[v * C::LPT + c];
+      const u32x4_t qq = qp[C::vec(v, c)];
 #pragma unroll
       for (int w = 0; w < 4; ++w) q[hh][v * 4 + w] = qq[w];
     }
@@ -304,7 +352,7 @@ __device__ __forceinline__ void write_output(const DecodeParams& p, int s, int h
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     if (hh >= nh) continue;
-    const float inv = l[hh] > 0.f ? 1.f / l[hh] : 0.f;
+    const float inv = l[hh] > 0.f ? p.out_scale / l[hh] : 0.f;
     u32x4_t* op = reinterpret_cast<u32x4_t*>(reinterpret_cast<S*>(p.out) +
                                              ((int64_t)s * p.H + h0 + hh) * D);
 #pragma unroll
@@ -319,7 +367,7 @@ __device__ __forceinline__ void write_output(const DecodeParams& p, int s, int h
           o[w] = __float_as_uint(acc[hh][v * 4 + w] * inv);
         }
       }
-      op[v * C::LPT + c] = o;
+      op[C::vec(v, c)] = o;
     }
   }
 }
@@ -341,8 +389,9 @@ __device__ __forceinline__ void write_partial(const DecodeParams& p, int64_t slo
 #pragma unroll
       for (int q4 = 0; q4 < C::EPV / 4; ++q4) {
         const int e = v * C::EPV + q4 * 4;
-        wp[(v * C::LPT + c) * (C::EPV / 4) + q4] =
-            (f32x4_t){acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]};
+        const float o = p.out_scale;
+        wp[C::vec(v, c) * (C::EPV / 4) + q4] =
+            (f32x4_t){acc[hh][e] * o, acc[hh][e + 1] * o, acc[hh][e + 2] * o, acc[hh][e + 3] * o};
       }
     }
     if (c == 0) {
@@ -410,20 +459,7 @@ __device__ __forceinline__ void load_item_step(Step<T, D>& st, const DecodeParam
     const int pos = min(pos_raw, max(L - 1, 0));          // branch-free: re-read a real key
     const int64_t blk = __shfl(pid, t * C::LPT + (pos >> p.block_shift), kWave);
     const int64_t row = blk * p.block_stride + (int64_t)(pos & bmask) * row_elems + head_off;
-    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(
-        reinterpret_cast<const typename T::storage*>(p.kc) + row);
-    const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(
-        reinterpret_cast<const typename T::storage*>(p.vc) + row);
-#pragma unroll
-    for (int v = 0; v < C::VPL; ++v) {
-      const u32x4_t kk = __builtin_nontemporal_load(kp + v * C::LPT + c);
-      const u32x4_t vv = __builtin_nontemporal_load(vp + v * C::LPT + c);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        st.k[r][v * 4 + w] = kk[w];
-        st.v[r][v * 4 + w] = vv[w];
-      }
-    }
+    load_row<T, D>(st, r, p, row, c);
   }
 }
 
@@ -458,7 +494,7 @@ decode_items_kernel(const DecodeParams p) {
         reinterpret_cast<const S*>(p.query) + ((int64_t)s * p.H + h0 + (hh < nh ? hh : 0)) * D);
 #pragma unroll
     for (int v = 0; v < C::VPL; ++v) {
-      const u32x4_t qq = qp[v * C::LPT + c];
+      const u32x4_t qq = qp[C::vec(v, c)];
 #pragma unroll
       for (int w = 0; w < 4; ++w) q[hh][v * 4 + w] = qq[w];
     }
@@ -845,25 +881,30 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& pl, hipStream_t st
   dp.nsplit = pl.num_splits;
   dp.groups_per_kv = pl.groups_per_kv;
   dp.nranges = pl.num_ranges;
-  dp.scale_log2 = a.scale * kLog2e;
+  dp.scale_log2 = a.scale * (a.kv_fp8 ? a.k_scale : 1.f) * kLog2e;
+  dp.out_scale = a.kv_fp8 ? a.v_scale : 1.f;
   dp.guard = a.guard;
   const size_t slots = pl.workspace_bytes / ((size_t)(a.head_dim + 2) * sizeof(float));
   dp.ws_acc = pl.workspace_bytes ? reinterpret_cast<float*>(a.workspace) : nullptr;
   dp.ws_ml = pl.workspace_bytes ? dp.ws_acc + slots * a.head_dim : nullptr;
   const int64_t groups = (int64_t)a.num_kv_heads * pl.groups_per_kv;
   dp.total_items = pl.stream ? groups * pl.num_ranges : (int64_t)a.num_seqs * pl.num_splits * groups;
-  switch (a.dtype) {
-    case kBF16: launch_all<BF16>(dp, pl, a.head_dim, false, stream); break;
-    case kF16: launch_all<F16>(dp, pl, a.head_dim, false, stream); break;
-    default: launch_all<F32>(dp, pl, a.head_dim, false, stream); break;
-  }
+  auto dispatch = [&](bool merge) {
+    if (a.kv_fp8) {
+      if (a.dtype == kBF16) launch_all<BF16K8>(dp, pl, a.head_dim, merge, stream);
+      else launch_all<F16K8>(dp, pl, a.head_dim, merge, stream);
+      return;
+    }
+    switch (a.dtype) {
+      case kBF16: launch_all<BF16>(dp, pl, a.head_dim, merge, stream); break;
+      case kF16: launch_all<F16>(dp, pl, a.head_dim, merge, stream); break;
+      default: launch_all<F32>(dp, pl, a.head_dim, merge, stream); break;
+    }
+  };
+  dispatch(false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(pl.stream || pl.num_splits > 1)) return e;
-  switch (a.dtype) {
-    case kBF16: launch_all<BF16>(dp, pl, a.head_dim, true, stream); break;
-    case kF16: launch_all<F16>(dp, pl, a.head_dim, true, stream); break;
-    default: launch_all<F32>(dp, pl, a.head_dim, true, stream); break;
-  }
+  dispatch(true);
   return hipGetLastError();
 }
 

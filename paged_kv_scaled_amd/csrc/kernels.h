@@ -8,12 +8,12 @@
 
 namespace pkv {
 
-enum Dtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
+enum Dtype { kF32 = 0, kF16 = 1, kBF16 = 2, kFp8E4M3 = 3 };
 
 // The span-list mask (beyond the three pkv_mask_mode values), as the kernels number it.
 constexpr int kMaskSpansHost = 3;
 
-inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
+inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : (dt == kFp8E4M3 ? 1 : 2); }
 
 struct ScatterArgs {
   const void* key;
@@ -62,6 +62,8 @@ struct AttnArgs {
   int dtype;
   void* workspace;               // decode only
   const uint32_t* guard;         // device error word when device checks are on, else null
+  int kv_fp8;                    // the caches hold E4M3 codes (value = code * scale)
+  float k_scale, v_scale;
 };
 
 // What the sequence check kernel reads: lengths from seq_lens (attention) or from
@@ -102,6 +104,10 @@ DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
                        int block_size, int max_seq_len);
 
 hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream);
+// Quantising scatter into an FP8 (E4M3) cache: a.dtype is the source type, the cache
+// element is one byte; code = E4M3(clamp(x * inv_scale, +-448)).
+hipError_t launch_kv_scatter_fp8(const ScatterArgs& a, float k_inv_scale, float v_inv_scale,
+                                 hipStream_t stream);
 hipError_t launch_kv_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, hipStream_t stream);
 // Returns hipErrorNotSupported when no MFMA variant covers the shape.

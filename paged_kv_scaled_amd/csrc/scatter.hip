@@ -6,7 +6,11 @@
 // blocks into compact per-sequence tensors (the attention kernels fuse this step into
 // their loads; the exported gather exists so tests can check the addressing bit-exactly).
 //
-// Both are raw copies, so they are written on bytes: one lane moves one VEC-byte
+// The FP8 variant of the scatter quantises each element to an E4M3 code on the way (FP8
+// staging of cache rows: CSA2 Vanilla golden PR, "Description"; the pages fix no scale
+// convention, the one used here is stated in pkv.h).
+//
+// Both plain kernels are raw copies, so they are written on bytes: one lane moves one VEC-byte
 // vector of a token row (num_kv_heads * head_dim elements, dense in source and in
 // cache), consecutive lanes take consecutive vectors of the same row, so every wave
 // reads and writes whole contiguous row segments (coalesced, HBM-bound).
@@ -81,6 +85,80 @@ kv_gather_kernel(char* __restrict__ kout, char* __restrict__ vout,
   *reinterpret_cast<V*>(vout + dst) = *reinterpret_cast<const V*>(vc + src);
 }
 
+// ---- quantising scatter into an FP8 (E4M3) cache ---------------------------------------
+// One lane turns N source elements of a row into N code bytes.  code = E4M3 of
+// clamp(x * inv_scale, +-448), the product rounded once to fp32 and the conversion rounding
+// to nearest even (v_cvt_pk_fp8_f32); a NaN stays NaN (the comparisons below pass it through).
+
+__device__ __forceinline__ float src_value(BF16, uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+__device__ __forceinline__ float src_value(F16, uint16_t u) {
+  return (float)__builtin_bit_cast(_Float16, u);
+}
+__device__ __forceinline__ float src_value(F32, uint32_t u) { return __uint_as_float(u); }
+
+__device__ __forceinline__ float clamp_e4m3(float y) {
+  return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
+}
+
+// Two values -> two codes in the low (HI false) or high half of `old`.
+template <bool HI>
+__device__ __forceinline__ uint32_t to_e4m3x2(float a, float b, float inv, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a * inv), clamp_e4m3(b * inv),
+                                                   (int)old, HI);
+}
+
+template <typename S, int N>
+struct alignas(N * sizeof(typename S::storage)) SrcChunk {
+  typename S::storage e[N];
+};
+
+template <int N> struct CodeChunk;
+template <> struct CodeChunk<8> { using type = u32x2_t; };
+template <> struct CodeChunk<4> { using type = uint32_t; };
+
+template <typename S, int N>
+__device__ __forceinline__ typename CodeChunk<N>::type quantize_chunk(const SrcChunk<S, N>& x,
+                                                                     float inv) {
+  uint32_t w[N / 4];
+#pragma unroll
+  for (int j = 0; j < N / 4; ++j) {
+    const float f0 = src_value(S{}, x.e[4 * j]), f1 = src_value(S{}, x.e[4 * j + 1]);
+    const float f2 = src_value(S{}, x.e[4 * j + 2]), f3 = src_value(S{}, x.e[4 * j + 3]);
+    w[j] = to_e4m3x2<true>(f2, f3, inv, to_e4m3x2<false>(f0, f1, inv, 0u));
+  }
+  if constexpr (N == 8) return (u32x2_t){w[0], w[1]};
+  else return w[0];
+}
+
+// Rows hold num_kv_heads * head_dim elements, a multiple of 16, so N in {4, 8} divides them.
+template <typename S, int N>
+__global__ void __launch_bounds__(kScatterThreads)
+kv_scatter_fp8_kernel(const typename S::storage* __restrict__ key,
+                      const typename S::storage* __restrict__ value, int64_t token_stride,
+                      const int64_t* __restrict__ slots, int32_t num_tokens,
+                      uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, int64_t block_stride,
+                      int32_t block_shift, int32_t row_chunks, int64_t num_slots, float k_inv,
+                      float v_inv, const uint32_t* guard) {
+  using C = typename CodeChunk<N>::type;
+  if (guard_tripped(guard)) return;
+  const int64_t total = (int64_t)num_tokens * row_chunks;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  const int32_t bmask = (1 << block_shift) - 1;
+  const int64_t row = (int64_t)row_chunks * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += step) {
+    const int32_t t = (int32_t)(i / row_chunks);
+    const int32_t v = (int32_t)(i - (int64_t)t * row_chunks);
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;   // padding token (negative slot)
+    const int64_t src = (int64_t)t * token_stride + (int64_t)v * N;
+    const int64_t dst = (slot >> block_shift) * block_stride + (slot & bmask) * row + (int64_t)v * N;
+    const SrcChunk<S, N> kx = *reinterpret_cast<const SrcChunk<S, N>*>(key + src);
+    const SrcChunk<S, N> vx = *reinterpret_cast<const SrcChunk<S, N>*>(value + src);
+    *reinterpret_cast<C*>(kc + dst) = quantize_chunk<S, N>(kx, k_inv);
+    *reinterpret_cast<C*>(vc + dst) = quantize_chunk<S, N>(vx, v_inv);
+  }
+}
+
 int log2_exact(int x) {
   int s = 0;
   while ((1 << s) < x) ++s;
@@ -124,6 +202,40 @@ hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream) {
     default: PKV_SCATTER(2); break;
   }
 #undef PKV_SCATTER
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_scatter_fp8(const ScatterArgs& a, float k_inv, float v_inv,
+                                 hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const int eb = dtype_bytes(a.dtype);
+  const int64_t row = (int64_t)a.num_kv_heads * a.head_dim;
+  // 8 elements per lane when every source chunk is 8-element aligned and every code chunk
+  // 8-byte aligned, else 4
+  const uint64_t bits8 = (uint64_t)(a.token_stride * eb) | (uint64_t)(uintptr_t)a.key |
+                         (uint64_t)(uintptr_t)a.value;
+  const uint64_t bits1 = (uint64_t)a.block_stride | (uint64_t)(uintptr_t)a.key_cache |
+                         (uint64_t)(uintptr_t)a.value_cache;
+  const int n = ((bits8 & (uint64_t)(8 * eb - 1)) == 0 && (bits1 & 7u) == 0) ? 8 : 4;
+  if ((bits8 & (uint64_t)(4 * eb - 1)) != 0 || (bits1 & 3u) != 0) return hipErrorInvalidValue;
+  const int32_t row_chunks = (int32_t)(row / n);
+  const int64_t total = (int64_t)a.num_tokens * row_chunks;
+  const int64_t blocks64 = (total + kScatterThreads - 1) / kScatterThreads;
+  const int blocks = (int)(blocks64 < 65536 ? blocks64 : 65536);
+  const int shift = log2_exact(a.block_size);
+  const int64_t num_slots = (int64_t)a.num_blocks * a.block_size;
+#define PKV_SCATTER8(S, N)                                                                     \
+  hipLaunchKernelGGL((kv_scatter_fp8_kernel<S, N>), dim3(blocks), dim3(kScatterThreads), 0,    \
+                     stream, (const S::storage*)a.key, (const S::storage*)a.value,            \
+                     a.token_stride, a.slots, a.num_tokens, (uint8_t*)a.key_cache,             \
+                     (uint8_t*)a.value_cache, a.block_stride, shift, row_chunks, num_slots,    \
+                     k_inv, v_inv, a.guard)
+  switch (a.dtype) {
+    case kBF16: if (n == 8) PKV_SCATTER8(BF16, 8); else PKV_SCATTER8(BF16, 4); break;
+    case kF16: if (n == 8) PKV_SCATTER8(F16, 8); else PKV_SCATTER8(F16, 4); break;
+    default: if (n == 8) PKV_SCATTER8(F32, 8); else PKV_SCATTER8(F32, 4); break;
+  }
+#undef PKV_SCATTER8
   return hipGetLastError();
 }
 

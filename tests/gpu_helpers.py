@@ -39,7 +39,8 @@ class Dev:
 
     def __init__(self, w: wl.Workload, fill: str = "nan", combined: bool = False):
         self.w = w
-        dt = TORCH_DT[w.dtype]
+        self.fp8 = getattr(w, "kv_dtype", None) == "fp8"
+        dt = torch.uint8 if self.fp8 else TORCH_DT[w.dtype]     # FP8 caches hold E4M3 codes
         shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
         if combined:
             # the (num_blocks, 2, block_size, Hkv, D) layout passed as two strided views
@@ -49,8 +50,9 @@ class Dev:
             self.kc = torch.empty(shape, dtype=dt, device="cuda")
             self.vc = torch.empty(shape, dtype=dt, device="cuda")
         if fill == "nan":
-            self.kc.fill_(float("nan"))
-            self.vc.fill_(float("nan"))
+            nan = 0x7F if self.fp8 else float("nan")
+            self.kc.fill_(nan)
+            self.vc.fill_(nan)
         else:
             self.kc.zero_()
             self.vc.zero_()
@@ -76,9 +78,15 @@ class Dev:
                 if rows.size == 0:
                     continue
                 idx = torch.from_numpy(rows).cuda()
-                B.kv_cache_write(self.key[idx], self.value[idx], self.slots[idx], self.kc, self.vc)
+                self.write(self.key[idx], self.value[idx], self.slots[idx])
         else:
-            B.kv_cache_write(self.key, self.value, self.slots, self.kc, self.vc)
+            self.write(self.key, self.value, self.slots)
+
+    def write(self, key, value, slots):
+        if self.fp8:
+            B.kv_cache_write_fp8(key, value, slots, self.kc, self.vc, self.w.k_scale, self.w.v_scale)
+        else:
+            B.kv_cache_write(key, value, slots, self.kc, self.vc)
 
     def decode(self, out=None):
         w = self.w
@@ -86,8 +94,13 @@ class Dev:
         ws_bytes = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
                                            w.max_seq_len)
         ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-        B.paged_attention_decode(out, self.query, self.kc, self.vc, self.tables, self.seq_lens,
-                                 w.scale, w.max_seq_len, ws if ws_bytes else None)
+        if self.fp8:
+            B.paged_attention_decode_fp8(out, self.query, self.kc, self.vc, self.tables,
+                                         self.seq_lens, w.scale, w.k_scale, w.v_scale,
+                                         w.max_seq_len, ws if ws_bytes else None)
+        else:
+            B.paged_attention_decode(out, self.query, self.kc, self.vc, self.tables, self.seq_lens,
+                                     w.scale, w.max_seq_len, ws if ws_bytes else None)
         return out
 
     def prefill(self, out=None):

@@ -24,7 +24,7 @@ def lib():
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -155,3 +155,74 @@ def test_device_checks_switch(lib):
     assert lib.pkv_set_device_checks(1) == B.PKV_OK
     assert lib.pkv_set_device_checks(0) == B.PKV_OK
     assert B.last_error() == ""
+
+
+def _write_fp8(lib, **kw):
+    a = dict(key=FAKE, value=FAKE, stride=1024, slots=FAKE, T=10, kc=FAKE, vc=FAKE,
+             bstride=16 * 1024, nb=4, bs=16, hkv=8, d=128, ks=0.02, vs=0.03, dt=B.PKV_BF16)
+    a.update(kw)
+    return lib.pkv_kv_cache_write_fp8(a["key"], a["value"], a["stride"], a["slots"], a["T"],
+                                      a["kc"], a["vc"], a["bstride"], a["nb"], a["bs"], a["hkv"],
+                                      a["d"], a["ks"], a["vs"], a["dt"], NULL)
+
+
+def test_write_fp8_rejections(lib):
+    assert _write_fp8(lib, ks=0.0) == B.PKV_ERR_INVALID_ARG
+    assert "scale" in B.last_error()
+    assert _write_fp8(lib, vs=-1.0) == B.PKV_ERR_INVALID_ARG
+    assert _write_fp8(lib, ks=float("inf")) == B.PKV_ERR_INVALID_ARG
+    assert _write_fp8(lib, ks=float("nan")) == B.PKV_ERR_INVALID_ARG
+    assert _write_fp8(lib, ks=1e-45) == B.PKV_ERR_INVALID_ARG           # 1/scale overflows
+    assert _write_fp8(lib, dt=B.PKV_FP8_E4M3) == B.PKV_ERR_UNSUPPORTED  # source must be a float
+    assert _write_fp8(lib, stride=1026) == B.PKV_ERR_INVALID_ARG        # not a multiple of 4
+    assert _write_fp8(lib, key=ctypes.c_void_p(0x1002)) == B.PKV_ERR_INVALID_ARG
+    assert "aligned" in B.last_error()
+    assert _write_fp8(lib, kc=ctypes.c_void_p(0x1001)) == B.PKV_ERR_INVALID_ARG
+    assert _write_fp8(lib, key=NULL) == B.PKV_ERR_INVALID_ARG
+    assert _write_fp8(lib, T=0, key=NULL, value=NULL, slots=NULL) == B.PKV_OK
+
+
+def _decode_fp8(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bstride=16 * 8 * 128, bt=FAKE, mb=256, sl=FAKE,
+             S=64, H=32, Hkv=8, D=128, nb=9000, bs=16, scale=0.088, ks=0.02, vs=0.03, maxL=4096,
+             ws=FAKE, wsb=1 << 30, dt=B.PKV_BF16)
+    a.update(kw)
+    return lib.pkv_paged_attention_decode_fp8(a["out"], a["q"], a["kc"], a["vc"], a["bstride"],
+                                              a["bt"], a["mb"], a["sl"], a["S"], a["H"], a["Hkv"],
+                                              a["D"], a["nb"], a["bs"], a["scale"], a["ks"],
+                                              a["vs"], a["maxL"], a["ws"], a["wsb"], a["dt"], NULL)
+
+
+def test_decode_fp8_rejections(lib):
+    assert _decode_fp8(lib, dt=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED
+    assert _decode_fp8(lib, dt=B.PKV_FP8_E4M3) == B.PKV_ERR_UNSUPPORTED
+    assert _decode_fp8(lib, ks=0.0) == B.PKV_ERR_INVALID_ARG
+    assert _decode_fp8(lib, vs=float("inf")) == B.PKV_ERR_INVALID_ARG
+    assert _decode_fp8(lib, bstride=16 * 8 * 128 + 8) == B.PKV_ERR_INVALID_ARG   # 16-byte rows
+    assert "16" in B.last_error()
+    assert _decode_fp8(lib, kc=ctypes.c_void_p(0x1008)) == B.PKV_ERR_INVALID_ARG
+    assert _decode_fp8(lib, wsb=0) == B.PKV_ERR_WORKSPACE
+    assert _decode_fp8(lib, H=30) == B.PKV_ERR_INVALID_ARG
+    assert _decode_fp8(lib, S=0) == B.PKV_OK
+
+
+def test_attention_alignment_rejections(lib):
+    """The attention calls read rows in 16-byte vectors: misaligned pointers or block
+    strides are rejected on the host."""
+    need = lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 4096)
+    assert _decode(lib, q=ctypes.c_void_p(0x1002), wsb=need) == B.PKV_ERR_INVALID_ARG
+    assert _decode(lib, bstride=16 * 8 * 128 + 4, wsb=need) == B.PKV_ERR_INVALID_ARG
+    assert _decode(lib, bstride=16 * 8 * 128 + 2, dt=B.PKV_F32, wsb=need) == B.PKV_ERR_INVALID_ARG
+    assert _prefill(lib, out=ctypes.c_void_p(0x1004)) == B.PKV_ERR_INVALID_ARG
+    assert _prefill(lib, bstride=16 * 8 * 128 + 2) == B.PKV_ERR_INVALID_ARG
+
+
+def test_gather_takes_fp8_codes(lib):
+    """The gather is a byte copy for FP8 caches: PKV_FP8_E4M3 passes the dtype check (and
+    then fails on the NULL output here)."""
+    r = lib.pkv_kv_cache_gather(NULL, FAKE, FAKE, FAKE, FAKE, 16 * 256, FAKE, 4, 2, 10, 8, 16,
+                                2, 128, 40, B.PKV_FP8_E4M3, NULL)
+    assert r == B.PKV_ERR_INVALID_ARG and "NULL" in B.last_error()
+    r = lib.pkv_kv_cache_gather(NULL, FAKE, FAKE, FAKE, FAKE, 16 * 256, FAKE, 4, 2, 10, 8, 16,
+                                2, 128, 40, 9, NULL)
+    assert r == B.PKV_ERR_UNSUPPORTED
