@@ -83,7 +83,8 @@ def prefill_flops(w) -> float:
 def prefill_bytes(w) -> int:
     import numpy as np
     eb = 2 if w.dtype != "f32" else 4
-    kv = int(w.seq_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * eb * 2
+    cb = 1 if getattr(w, "kv_dtype", None) == "fp8" else eb
+    kv = int(w.seq_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * cb * 2
     return kv + 2 * w.num_tokens * w.num_heads * w.head_dim * eb
 
 

@@ -232,6 +232,26 @@ int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_
                                 int32_t span_len, int32_t max_q_len, int32_t max_seq_len,
                                 pkv_dtype dtype, void* stream);
 
+/*
+ * pkv_paged_attention_prefill_fp8 -- pkv_paged_attention_prefill over FP8
+ * caches written by pkv_kv_cache_write_fp8 (conventions above); query and out
+ * are dtype (PKV_BF16 or PKV_F16), the caches byte arrays with
+ * cache_block_stride in bytes (a multiple of 16).  Masks NONE, CAUSAL and
+ * BLOCK_CAUSAL; there is no FP8 form of the span-list call (the quantised path
+ * of the vllm-omni piecewise block-causal PR rejects span metadata).  Errors as
+ * pkv_paged_attention_prefill, plus UNSUPPORTED for a dtype other than BF16 /
+ * F16 and INVALID_ARG for scales.
+ */
+int pkv_paged_attention_prefill_fp8(void* out, const void* query, const int32_t* cu_seqlens_q,
+                                    const int32_t* seq_lens, const void* key_cache,
+                                    const void* value_cache, int64_t cache_block_stride,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                    int32_t block_size, float scale, float k_scale, float v_scale,
+                                    pkv_mask_mode mask, int32_t span_len, int32_t max_q_len,
+                                    int32_t max_seq_len, pkv_dtype dtype, void* stream);
+
 /* Prefill with general span lists (vllm-omni piecewise block-causal PR: the
  * `full_attn_spans` metadata -- image blocks attend bidirectionally, text runs
  * causally; its dense reference "(q >= kv) or same_image_block").

@@ -39,6 +39,10 @@ SIGNATURES = {
                                                    _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                                    ctypes.c_int, _I32, _I32, _I32, ctypes.c_int,
                                                    _P]),
+    "pkv_paged_attention_prefill_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _I32,
+                                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                       _F, _F, _F, ctypes.c_int, _I32, _I32, _I32,
+                                                       ctypes.c_int, _P]),
     "pkv_paged_attention_prefill_spans": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _I32,
                                                          _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                          _F, _P, _P, _I32, _I32, _I32,
@@ -205,6 +209,25 @@ def paged_attention_prefill(out, query, cu_seqlens_q, seq_lens, key_cache, value
                                            T, H, hkv, D, nb, bs, float(scale), int(mask),
                                            int(span_len), int(max_q_len), int(max_seq_len),
                                            _dtype_code(query), _stream()))
+
+
+def paged_attention_prefill_fp8(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,
+                                block_tables, scale: float, k_scale: float, v_scale: float,
+                                mask: int, span_len: int, max_q_len: int, max_seq_len: int):
+    """paged_attention_prefill over uint8 caches of E4M3 codes; query/out bf16 or fp16."""
+    lib = load()
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    T, H, D = query.shape
+    assert D == d and out.shape == query.shape and query.is_contiguous() and out.is_contiguous()
+    assert key_cache.element_size() == 1
+    S = seq_lens.shape[0]
+    _check(lib.pkv_paged_attention_prefill_fp8(_ptr(out), _ptr(query), _ptr(cu_seqlens_q),
+                                               _ptr(seq_lens), _ptr(key_cache), _ptr(value_cache),
+                                               bstride, _ptr(block_tables), block_tables.shape[1],
+                                               S, T, H, hkv, D, nb, bs, float(scale),
+                                               float(k_scale), float(v_scale), int(mask),
+                                               int(span_len), int(max_q_len), int(max_seq_len),
+                                               _dtype_code(query), _stream()))
 
 
 def paged_attention_prefill_spans(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,

@@ -110,7 +110,8 @@ int prefill_common(void* out, const void* query, const int32_t* cu_seqlens_q,
                    int32_t block_size, float scale, int mask, int32_t span_len,
                    const int32_t* full_spans, const int32_t* cu_spans, int32_t num_spans,
                    int32_t max_q_len, int32_t max_seq_len, pkv_dtype dtype, void* stream,
-                   const char* what) {
+                   const char* what, bool kv_fp8 = false, float k_scale = 1.f,
+                   float v_scale = 1.f) {
   int rc;
   if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
   if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || max_seq_len < 0)
@@ -135,9 +136,12 @@ int prefill_common(void* out, const void* query, const int32_t* cu_seqlens_q,
     return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
                 (long long)max_blocks_per_seq * block_size, max_seq_len);
   if ((rc = check_attn_alignment(out, query, key_cache, value_cache, cache_block_stride,
-                                 dtype == PKV_F32 ? 4 : 2)) != PKV_OK)
+                                 kv_fp8 ? 1 : (dtype == PKV_F32 ? 4 : 2))) != PKV_OK)
     return rc;
   pkv::AttnArgs a{};
+  a.kv_fp8 = kv_fp8 ? 1 : 0;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.out = out;
   a.query = query;
   a.cu_seqlens_q = cu_seqlens_q;
@@ -445,6 +449,32 @@ int pkv_paged_attention_prefill(void* out, const void* query, const int32_t* cu_
                         num_heads, num_kv_heads, head_dim, num_blocks, block_size, scale, (int)mask,
                         span_len, nullptr, nullptr, 0, max_q_len, max_seq_len, dtype, stream,
                         "pkv_paged_attention_prefill");
+}
+
+int pkv_paged_attention_prefill_fp8(void* out, const void* query, const int32_t* cu_seqlens_q,
+                                    const int32_t* seq_lens, const void* key_cache,
+                                    const void* value_cache, int64_t cache_block_stride,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                    int32_t block_size, float scale, float k_scale, float v_scale,
+                                    pkv_mask_mode mask, int32_t span_len, int32_t max_q_len,
+                                    int32_t max_seq_len, pkv_dtype dtype, void* stream) {
+  clear_error();
+  int rc;
+  if (dtype != PKV_BF16 && dtype != PKV_F16)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_attention_prefill_fp8: query dtype %d is not "
+                "PKV_BF16 or PKV_F16", (int)dtype);
+  if ((rc = check_fp8_scales(k_scale, v_scale)) != PKV_OK) return rc;
+  if (mask != PKV_MASK_NONE && mask != PKV_MASK_CAUSAL && mask != PKV_MASK_BLOCK_CAUSAL)
+    return fail(PKV_ERR_INVALID_ARG, "unknown mask mode %d", (int)mask);
+  if (mask == PKV_MASK_BLOCK_CAUSAL && span_len <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "BLOCK_CAUSAL needs span_len > 0 (got %d)", span_len);
+  return prefill_common(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,
+                        cache_block_stride, block_tables, max_blocks_per_seq, num_seqs, num_tokens,
+                        num_heads, num_kv_heads, head_dim, num_blocks, block_size, scale, (int)mask,
+                        span_len, nullptr, nullptr, 0, max_q_len, max_seq_len, dtype, stream,
+                        "pkv_paged_attention_prefill_fp8", true, k_scale, v_scale);
 }
 
 int pkv_paged_attention_prefill_spans(void* out, const void* query, const int32_t* cu_seqlens_q,

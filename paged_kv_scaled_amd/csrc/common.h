@@ -30,6 +30,10 @@ struct F16K8 : F16 {};
 template <typename T> struct KvFp8 { static constexpr bool value = false; };
 template <> struct KvFp8<BF16K8> { static constexpr bool value = true; };
 template <> struct KvFp8<F16K8> { static constexpr bool value = true; };
+// The compute tag of a tag (BF16 for BF16K8, F16 for F16K8, else itself).
+template <typename T> struct BaseOf { using type = T; };
+template <> struct BaseOf<BF16K8> { using type = BF16; };
+template <> struct BaseOf<F16K8> { using type = F16; };
 
 // ---- scalar conversions ---------------------------------------------------------------
 

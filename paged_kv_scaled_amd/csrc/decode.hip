@@ -65,12 +65,21 @@ struct DecodeShape {
   }
 };
 
+// 32-bit words of one K (or V) row that a lane holds in flight: the elements themselves,
+// or for an FP8 cache the raw codes (half as many words; widened when used).
+template <typename T, int D>
+constexpr int raw_words() {
+  return KvFp8<T>::value ? DecodeShape<T, D>::WPL / 2 : DecodeShape<T, D>::WPL;
+}
+
 // Steps whose loads are issued together: keep the K/V registers of one batch of steps
-// at about 64 per lane (2 rounds x 2 tensors x WPL words per step).
+// at about 64 per lane (2 rounds x 2 tensors x raw words per step).
 template <typename T, int D, int HPW>
 struct DecodeSteps {
-  static constexpr int words = 4 * DecodeShape<T, D>::WPL;
-  static constexpr int value = (HPW >= 8 || words > 32) ? 1 : (words > 16 || HPW >= 4 ? 2 : 4);
+  static constexpr int words = 4 * raw_words<T, D>();
+  static constexpr int value =
+      KvFp8<T>::value ? (HPW >= 8 ? 1 : 4)
+                      : ((HPW >= 8 || words > 32) ? 1 : (words > 16 || HPW >= 4 ? 2 : 4));
 };
 
 struct DecodeParams {
@@ -92,11 +101,21 @@ struct DecodeParams {
 
 template <typename T, int D>
 struct Step {
-  using C = DecodeShape<T, D>;
-  uint32_t k[2][C::WPL];
-  uint32_t v[2][C::WPL];
+  static constexpr int RW = raw_words<T, D>();
+  uint32_t k[2][RW];
+  uint32_t v[2][RW];
   bool valid[2];
 };
+
+// Word w (a pair of compute-type elements) of a lane's row held as `raw`.
+template <typename T, int RW>
+__device__ __forceinline__ uint32_t row_word(const uint32_t (&raw)[RW], int w) {
+  if constexpr (KvFp8<T>::value) {
+    return (w & 1) ? widen_fp8x2<true>(T{}, raw[w >> 1]) : widen_fp8x2<false>(T{}, raw[w >> 1]);
+  } else {
+    return raw[w];
+  }
+}
 
 // Block ids of 64 consecutive pages, one per lane (lane i: page chunk_base + i).
 struct TableWindow {
@@ -116,7 +135,7 @@ __device__ __forceinline__ void load_row(Step<T, D>& st, int r, const DecodePara
                                          int c) {
   using C = DecodeShape<T, D>;
   if constexpr (KvFp8<T>::value) {
-    // EPL codes per lane, one load each for K and V, widened to the compute pairs
+    // EPL codes per lane, one load each for K and V (widened when used)
     const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.kc) + row + c * C::EPL;
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.vc) + row + c * C::EPL;
     constexpr int NW = C::EPL / 4;                  // code words per lane
@@ -141,10 +160,8 @@ __device__ __forceinline__ void load_row(Step<T, D>& st, int r, const DecodePara
     }
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      st.k[r][2 * i] = widen_fp8x2<false>(T{}, kw[i]);
-      st.k[r][2 * i + 1] = widen_fp8x2<true>(T{}, kw[i]);
-      st.v[r][2 * i] = widen_fp8x2<false>(T{}, vw[i]);
-      st.v[r][2 * i + 1] = widen_fp8x2<true>(T{}, vw[i]);
+      st.k[r][i] = kw[i];
+      st.v[r][i] = vw[i];
     }
   } else {
     const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(
@@ -212,7 +229,7 @@ __device__ __forceinline__ void compute_step(const Step<T, D>& st,
 #pragma unroll
       for (int w = 0; w < C::WPL; ++w) {
         if constexpr (kHalf) {
-          d = dot2(T{}, q[hh][w], st.k[r][w], d);
+          d = dot2(T{}, q[hh][w], row_word<T>(st.k[r], w), d);
         } else {
           d = __builtin_fmaf(__uint_as_float(q[hh][w]), __uint_as_float(st.k[r][w]), d);
         }
@@ -247,7 +264,7 @@ __device__ __forceinline__ void compute_step(const Step<T, D>& st,
     // pair the two rounds: x = (v0.lo, v1.lo), y = (v0.hi, v1.hi) for every word
 #pragma unroll
     for (int w = 0; w < C::WPL; ++w) {
-      const uint32_t a = st.v[0][w], b = st.v[1][w];
+      const uint32_t a = row_word<T>(st.v[0], w), b = row_word<T>(st.v[1], w);
       const uint32_t x = (a & 0xFFFFu) | (b << 16);
       const uint32_t y = (a >> 16) | (b & 0xFFFF0000u);
 #pragma unroll

@@ -22,7 +22,11 @@
 //    the B operand of O^T = V^T P^T: the V^T tile stores each 16-token group in the
 //    token order that accumulator layout implies;
 //  * every wave computes every key tile of its workgroup (tiles past a row's visible end
-//    get probability 0); fully visible tiles skip the mask.
+//    get probability 0); fully visible tiles skip the mask;
+//  * an FP8 (E4M3) cache is read as codes, widened exactly to bf16 / fp16 on the way to
+//    LDS; k_scale is folded into the score scale and v_scale into the final 1/l.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -49,7 +53,8 @@ struct PrefillParams {
   int32_t mb, S, H, Hkv, g, block_shift, mask, span;
   int32_t hw, rb_log2, head_groups, qtiles;   // WG tiling
   int32_t ngroups;                            // (sequence, kv head, head group) groups
-  float scale_log2;
+  float scale_log2;                           // scale * log2(e) (times k_scale for FP8)
+  float out_scale;                            // v_scale for an FP8 cache, else 1
   const uint32_t* guard;                      // device error word when checks are on
 };
 
@@ -103,6 +108,8 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kWaves * 64)
 prefill_mfma_kernel(const PrefillParams p) {
   if (guard_tripped(p.guard)) return;
+  using TB = typename BaseOf<T>::type;          // MFMA / packing type
+  constexpr bool kK8 = KvFp8<T>::value;         // the caches hold E4M3 codes
   constexpr int NT = kWaves * 64;     // threads
   constexpr int NCB = 1;              // column blocks per wave
   using L = Lds<D>;
@@ -199,34 +206,49 @@ prefill_mfma_kernel(const PrefillParams p) {
   // ---- K / V tile loads into registers (clamped to the last key: finite data) -------
   // Thread (token group vg, 8-dim chunk vc) loads K and V of the TG tokens vg*TG.. for
   // dims vc*8..+8: one block-id lookup serves both tensors, 16 lanes read one 256-byte
-  // row segment, and V arrives ready for its transposed store.
-  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
-  const uint32_t head_bytes = (uint32_t)kvh * D * 2;
-  const uint64_t blk_bytes = (uint64_t)p.block_stride * 2;
+  // row segment (128 bytes of FP8 codes), and V arrives ready for its transposed store.
+  // FP8 codes stay packed in flight and are widened (exactly) on the way to LDS.
+  constexpr uint32_t CE = kK8 ? 1 : 2;      // cache element bytes
+  using KR = typename std::conditional<kK8, u32x2_t, u32x4_t>::type;
+  const uint32_t row_bytes = (uint32_t)p.Hkv * D * CE;
+  const uint32_t head_bytes = (uint32_t)kvh * D * CE;
+  const uint64_t blk_bytes = (uint64_t)p.block_stride * CE;
   const int bmask = (1 << p.block_shift) - 1;
   const int vc_ld = tid % NC;               // 8-dim chunk
   const int vg_ld = tid / NC;               // token group of TG tokens
-  u32x4_t kra[TG], vra[TG], krb[TG], vrb[TG];   // two tiles in flight
+  KR kra[TG], vra[TG], krb[TG], vrb[TG];    // two tiles in flight
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.kc);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.vc);
 
   // keys past kv_end (seen by no row of this workgroup) re-read key kv_end-1: finite
   // data whose page id is inside the staged window
-  auto load_tile = [&](int k0, u32x4_t (&kreg)[TG], u32x4_t (&vreg)[TG]) {
+  auto load_tile = [&](int k0, KR (&kreg)[TG], KR (&vreg)[TG]) {
 #pragma unroll
     for (int i = 0; i < TG; ++i) {
       const int pos = min(k0 + vg_ld * TG + i, kv_end - 1);
       const uint32_t blk = (uint32_t)s_tbl[(pos >> p.block_shift) - tbl_base];
       const uint64_t off = (uint64_t)blk * blk_bytes +
-                           ((uint32_t)(pos & bmask) * row_bytes + head_bytes + vc_ld * 16u);
-      kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
-      vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+                           ((uint32_t)(pos & bmask) * row_bytes + head_bytes + vc_ld * 8u * CE);
+      kreg[i] = *reinterpret_cast<const KR*>(kbase + off);
+      vreg[i] = *reinterpret_cast<const KR*>(vbase + off);
     }
   };
-  auto store_tile = [&](const u32x4_t (&kreg)[TG], const u32x4_t (&vreg)[TG]) {
+  // 8 elements of the compute type from what one load brought
+  auto widen8 = [&](const KR& x) -> u32x4_t {
+    if constexpr (kK8) {
+      return (u32x4_t){widen_fp8x2<false>(TB{}, x[0]), widen_fp8x2<true>(TB{}, x[0]),
+                       widen_fp8x2<false>(TB{}, x[1]), widen_fp8x2<true>(TB{}, x[1])};
+    } else {
+      return x;
+    }
+  };
+  auto store_tile = [&](const KR (&kraw)[TG], const KR (&vraw)[TG]) {
+    u32x4_t vreg[TG];
 #pragma unroll
-    for (int i = 0; i < TG; ++i)
-      *reinterpret_cast<u32x4_t*>(s_k + L::k_off(vg_ld * TG + i, vc_ld)) = kreg[i];
+    for (int i = 0; i < TG; ++i) {
+      *reinterpret_cast<u32x4_t*>(s_k + L::k_off(vg_ld * TG + i, vc_ld)) = widen8(kraw[i]);
+      vreg[i] = widen8(vraw[i]);
+    }
     // transpose TG tokens x 8 dims into 8 dims x TG tokens
     const int pos = vt_pos(vg_ld * TG);
 #pragma unroll
@@ -267,7 +289,7 @@ prefill_mfma_kernel(const PrefillParams p) {
   // One key tile: its K/V registers (loaded two tiles earlier) go to LDS, the registers are
   // refilled with the tile two ahead, then every wave computes on the LDS tile.  Two tiles
   // in flight cover the gather latency when the keys come from HBM rather than L2.
-  auto tile_step = [&](int k0, u32x4_t (&kreg)[TG], u32x4_t (&vreg)[TG]) {
+  auto tile_step = [&](int k0, KR (&kreg)[TG], KR (&vreg)[TG]) {
     store_tile(kreg, vreg);
     __syncthreads();
     const int k2 = k0 + 2 * kBN;
@@ -302,7 +324,7 @@ prefill_mfma_kernel(const PrefillParams p) {
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int j = 0; j < NCB; ++j)
-            sacc[j][tb] = Mfma<T>::run(ka[ks & 1][tb], qf[j][ks], ks == 0 ? (f32x16_t){} : sacc[j][tb]);
+            sacc[j][tb] = Mfma<TB>::run(ka[ks & 1][tb], qf[j][ks], ks == 0 ? (f32x16_t){} : sacc[j][tb]);
       }
       // keep the read-ahead: the scheduler would otherwise pull each read down to its MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // LDS reads of k-steps 0, 1
@@ -367,10 +389,10 @@ prefill_mfma_kernel(const PrefillParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
               pr[e] = fast_exp2(__builtin_fmaf(sacc[j][tb][h2 * 8 + e], c, -m[j]));
-            const u32x4_t q4 = (u32x4_t){pack2(T{}, pr[0], pr[1]), pack2(T{}, pr[2], pr[3]),
-                                         pack2(T{}, pr[4], pr[5]), pack2(T{}, pr[6], pr[7])};
+            const u32x4_t q4 = (u32x4_t){pack2(TB{}, pr[0], pr[1]), pack2(TB{}, pr[2], pr[3]),
+                                         pack2(TB{}, pr[4], pr[5]), pack2(TB{}, pr[6], pr[7])};
 #pragma unroll
-            for (int w = 0; w < 4; ++w) ls = dot2(T{}, q4[w], kOnes2<T>(), ls);
+            for (int w = 0; w < 4; ++w) ls = dot2(TB{}, q4[w], kOnes2<TB>(), ls);
             pf[j][tb * 2 + h2] = q4;
           }
         lsum[j] = ls;
@@ -383,7 +405,7 @@ prefill_mfma_kernel(const PrefillParams p) {
           const u32x4_t a =
               *reinterpret_cast<const u32x4_t*>(s_v + L::v_off(db * 32 + lc, ks * 16 + hl * 8));
 #pragma unroll
-          for (int j = 0; j < NCB; ++j) oacc[j][db] = Mfma<T>::run(a, pf[j][ks], oacc[j][db]);
+          for (int j = 0; j < NCB; ++j) oacc[j][db] = Mfma<TB>::run(a, pf[j][ks], oacc[j][db]);
         }
       }
     }
@@ -406,7 +428,7 @@ prefill_mfma_kernel(const PrefillParams p) {
     const float lt = lsum[j] + __shfl_xor(lsum[j], 32, 64);
     const int row = rbase[j] + lc;
     if (!hvalid[j] || row >= qn) continue;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
     S* op = reinterpret_cast<S*>(p.out) + ((int64_t)(q0 + row) * p.H + head[j]) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -415,8 +437,8 @@ prefill_mfma_kernel(const PrefillParams p) {
         const int d0 = db * 32 + g4 * 8 + hl * 4;
         const f32x16_t& o = oacc[j][db];
         *reinterpret_cast<u32x2_t*>(op + d0) =
-            (u32x2_t){pack2(T{}, o[g4 * 4 + 0] * inv, o[g4 * 4 + 1] * inv),
-                      pack2(T{}, o[g4 * 4 + 2] * inv, o[g4 * 4 + 3] * inv)};
+            (u32x2_t){pack2(TB{}, o[g4 * 4 + 0] * inv, o[g4 * 4 + 1] * inv),
+                      pack2(TB{}, o[g4 * 4 + 2] * inv, o[g4 * 4 + 3] * inv)};
       }
   }
 }
@@ -468,16 +490,19 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
   const int64_t nb = (ng + 7) / 8 * 8 * p.qtiles;     // 8 XCDs x groups per XCD x tiles
   if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
   p.ngroups = (int)ng;
-  p.scale_log2 = a.scale * kLog2e;
+  p.scale_log2 = a.scale * (a.kv_fp8 ? a.k_scale : 1.f) * kLog2e;
+  p.out_scale = a.kv_fp8 ? a.v_scale : 1.f;
   p.guard = a.guard;
   const dim3 grid((unsigned)nb), block(kWaves * 64);
-  if (a.dtype == kBF16) {
-    if (a.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 128>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<BF16, 64>), grid, block, 0, stream, p);
+#define PKV_PREFILL(TT)                                                                        \
+  if (a.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_kernel<TT, 128>), grid, block, 0, stream, p); \
+  else hipLaunchKernelGGL((prefill_mfma_kernel<TT, 64>), grid, block, 0, stream, p)
+  if (a.kv_fp8) {
+    if (a.dtype == kBF16) { PKV_PREFILL(BF16K8); } else { PKV_PREFILL(F16K8); }
   } else {
-    if (a.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_kernel<F16, 128>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<F16, 64>), grid, block, 0, stream, p);
+    if (a.dtype == kBF16) { PKV_PREFILL(BF16); } else { PKV_PREFILL(F16); }
   }
+#undef PKV_PREFILL
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Prefill / chunked-prefill attention on the vector ALU, fp32 throughout.
 //
-// Covers what the MFMA kernel does not: fp32 inputs (any head_dim) and head_dim 16.
+// Covers what the MFMA kernel does not: fp32 inputs (any head_dim) and head_dim 16 (also
+// over an FP8 cache, whose codes are widened exactly to fp32).
 // Semantics are those of the MFMA kernel (Spyre paged-attention PR, "Description"
 // steps 2-6 on a flat query batch; bottom-right causal and block-causal masks of the
 // vllm-omni piecewise block-causal PR).  Probabilities stay fp32 here.
@@ -29,6 +30,16 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
   }
 }
 
+// One K or V element: an E4M3 code widened exactly for an FP8 cache, else as load_elem.
+template <typename T>
+__device__ __forceinline__ float load_kv(const void* base, int64_t idx) {
+  if constexpr (KvFp8<T>::value) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)reinterpret_cast<const uint8_t*>(base)[idx], 0);
+  } else {
+    return load_elem<T>(base, idx);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
   if constexpr (T::bytes == 4) {
@@ -52,7 +63,7 @@ __device__ __forceinline__ int owner_seq(const int32_t* __restrict__ cu, int S, 
 
 template <typename T, int DMAX>
 __global__ void __launch_bounds__(kValuThreads)
-prefill_valu_kernel(const AttnArgs p, float scale_log2) {
+prefill_valu_kernel(const AttnArgs p, float scale_log2, float out_scale) {
   if (guard_tripped(p.guard)) return;
   __shared__ float s_q[kValuWaves][DMAX];
   __shared__ float s_p[kValuWaves][kWave];
@@ -94,7 +105,7 @@ prefill_valu_kernel(const AttnArgs p, float scale_log2) {
       const int64_t blk = table[pos >> shift];
       const int64_t row = blk * p.block_stride + (int64_t)(pos & bmask) * row_elems + (int64_t)kvh * D;
       float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot = __builtin_fmaf(s_q[wv][d], load_elem<T>(p.key_cache, row + d), dot);
+      for (int d = 0; d < D; ++d) dot = __builtin_fmaf(s_q[wv][d], load_kv<T>(p.key_cache, row + d), dot);
       z = dot * scale_log2;
     }
     float cmax = z;
@@ -121,12 +132,12 @@ prefill_valu_kernel(const AttnArgs p, float scale_log2) {
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
         const int d = lane + i * kWave;
-        if (d < D) acc[i] = __builtin_fmaf(w, load_elem<T>(p.value_cache, row + d), acc[i]);
+        if (d < D) acc[i] = __builtin_fmaf(w, load_kv<T>(p.value_cache, row + d), acc[i]);
       }
     }
     __builtin_amdgcn_wave_barrier();
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = l > 0.f ? out_scale / l : 0.f;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) {
     const int d = lane + i * kWave;
@@ -138,17 +149,23 @@ template <typename T>
 void launch_valu_t(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.num_tokens * a.num_heads;
   const int blocks = (int)((items + kValuWaves - 1) / kValuWaves);
-  const float sl2 = a.scale * kLog2e;
+  const float sl2 = a.scale * (a.kv_fp8 ? a.k_scale : 1.f) * kLog2e;
+  const float osc = a.kv_fp8 ? a.v_scale : 1.f;
   if (a.head_dim <= 64)
-    hipLaunchKernelGGL((prefill_valu_kernel<T, 64>), dim3(blocks), dim3(kValuThreads), 0, stream, a, sl2);
+    hipLaunchKernelGGL((prefill_valu_kernel<T, 64>), dim3(blocks), dim3(kValuThreads), 0, stream, a, sl2, osc);
   else
-    hipLaunchKernelGGL((prefill_valu_kernel<T, 128>), dim3(blocks), dim3(kValuThreads), 0, stream, a, sl2);
+    hipLaunchKernelGGL((prefill_valu_kernel<T, 128>), dim3(blocks), dim3(kValuThreads), 0, stream, a, sl2, osc);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_valu(const AttnArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0 || a.num_seqs == 0) return hipSuccess;
+  if (a.kv_fp8) {
+    if (a.dtype == kBF16) launch_valu_t<BF16K8>(a, stream);
+    else launch_valu_t<F16K8>(a, stream);
+    return hipGetLastError();
+  }
   switch (a.dtype) {
     case kBF16: launch_valu_t<BF16>(a, stream); break;
     case kF16: launch_valu_t<F16>(a, stream); break;

@@ -299,6 +299,12 @@ def decode_batch_fp8(seed: int = 1, **kw) -> Workload:
     return with_fp8_cache(decode_batch(seed=seed, **kw))
 
 
+def long_block_causal_fp8(seed: int = 4, **kw) -> Workload:
+    """The long block-causal prefill (4 x 8192 tokens, 64 q / 8 kv heads, spans of 2048)
+    over an FP8 cache."""
+    return with_fp8_cache(long_block_causal(seed=seed, **kw))
+
+
 CONFIGS = {
     "tiny_prefill": tiny_prefill,
     "decode_batch": decode_batch,
@@ -307,6 +313,7 @@ CONFIGS = {
     "long_block_causal": long_block_causal,
     "mixed_spans": mixed_spans,
     "decode_batch_fp8": decode_batch_fp8,
+    "long_block_causal_fp8": long_block_causal_fp8,
 }
 
 

@@ -106,7 +106,11 @@ class Dev:
     def prefill(self, out=None):
         w = self.w
         out = out if out is not None else torch.empty_like(self.query)
-        if w.mask == wl.MASK_SPANS:
+        if self.fp8:
+            B.paged_attention_prefill_fp8(out, self.query, self.cu_q, self.seq_lens, self.kc,
+                                          self.vc, self.tables, w.scale, w.k_scale, w.v_scale,
+                                          w.mask, w.span_len, w.max_q_len, w.max_seq_len)
+        elif w.mask == wl.MASK_SPANS:
             B.paged_attention_prefill_spans(out, self.query, self.cu_q, self.seq_lens, self.kc,
                                             self.vc, self.tables, w.scale, self.full_spans,
                                             self.cu_spans, w.max_q_len, w.max_seq_len)

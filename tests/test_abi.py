@@ -226,3 +226,27 @@ def test_gather_takes_fp8_codes(lib):
     r = lib.pkv_kv_cache_gather(NULL, FAKE, FAKE, FAKE, FAKE, 16 * 256, FAKE, 4, 2, 10, 8, 16,
                                 2, 128, 40, 9, NULL)
     assert r == B.PKV_ERR_UNSUPPORTED
+
+
+def _prefill_fp8(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, cu=FAKE, sl=FAKE, kc=FAKE, vc=FAKE, bstride=16 * 8 * 128, bt=FAKE,
+             mb=512, S=4, T=32768, H=64, Hkv=8, D=128, nb=2049, bs=16, scale=0.088, ks=0.02,
+             vs=0.03, mask=B.PKV_MASK_BLOCK_CAUSAL, span=2048, maxq=8192, maxL=8192,
+             dt=B.PKV_BF16)
+    a.update(kw)
+    return lib.pkv_paged_attention_prefill_fp8(a["out"], a["q"], a["cu"], a["sl"], a["kc"],
+                                               a["vc"], a["bstride"], a["bt"], a["mb"], a["S"],
+                                               a["T"], a["H"], a["Hkv"], a["D"], a["nb"], a["bs"],
+                                               a["scale"], a["ks"], a["vs"], a["mask"], a["span"],
+                                               a["maxq"], a["maxL"], a["dt"], NULL)
+
+
+def test_prefill_fp8_rejections(lib):
+    assert _prefill_fp8(lib, dt=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED
+    assert _prefill_fp8(lib, ks=-0.5) == B.PKV_ERR_INVALID_ARG
+    assert _prefill_fp8(lib, vs=0.0) == B.PKV_ERR_INVALID_ARG
+    assert _prefill_fp8(lib, mask=3) == B.PKV_ERR_INVALID_ARG          # no span lists on FP8
+    assert _prefill_fp8(lib, span=0) == B.PKV_ERR_INVALID_ARG
+    assert _prefill_fp8(lib, bstride=16 * 8 * 128 + 8) == B.PKV_ERR_INVALID_ARG
+    assert _prefill_fp8(lib, cu=NULL) == B.PKV_ERR_INVALID_ARG
+    assert _prefill_fp8(lib, T=0) == B.PKV_OK

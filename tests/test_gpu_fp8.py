@@ -153,3 +153,68 @@ def test_fp8_decode_rejects_f32_query(gpu):
         B.paged_attention_decode_fp8(out, d.query, d.kc, d.vc, d.tables, d.seq_lens, w.scale,
                                      w.k_scale, w.v_scale, w.max_seq_len)
     assert e.value.code == B.PKV_ERR_UNSUPPORTED
+
+
+def _prefill(w, rows=None, heads=None):
+    d = Dev(w)
+    d.write_all()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    want, _ = ref.workload_attention(w, rows=rows, heads=heads)
+    if rows is not None:
+        got, want = got[rows], want[rows]
+    if heads is not None:
+        got, want = got[:, heads], want[:, heads]
+    return compare(got, want, w.dtype, w.name)
+
+
+@pytest.mark.parametrize("mask", [wl.MASK_NONE, wl.MASK_CAUSAL, wl.MASK_BLOCK_CAUSAL])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fp8_prefill_chunked_masks(gpu, mask, dtype):
+    """Chunked prefill over an FP8 cache (MFMA kernel, D 128): several tiles, ragged tails."""
+    w = wl.chunked_prefill(seed=50 + mask, num_seqs=4, ctx_hi=300, q_lo=1, q_hi=200, dtype=dtype)
+    w.mask = mask
+    w.span_len = 48
+    _prefill(wl.with_fp8_cache(w))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fp8_prefill_random_shapes(gpu, seed):
+    """head_dim 16 (vector-ALU kernel), 64 and 128 (MFMA), random GQA, lengths and masks."""
+    rng = np.random.default_rng(400 + seed)
+    d = int(rng.choice([16, 64, 128]))
+    dt = str(rng.choice(["bf16", "f16"]))
+    _prefill(wl.with_fp8_cache(wl.random_small(seed, dt, head_dim=d, max_len=70)))
+
+
+def test_fp8_chunked_prefill_scaled(gpu):
+    """The chunked-prefill shape (8 seqs, ctx <= 2048, chunk 32..512, 32q/8kv, D 128)."""
+    _prefill(wl.with_fp8_cache(wl.chunked_prefill()))
+
+
+def test_fp8_long_block_causal_sampled(gpu):
+    """4 x 8192 tokens, 64 q heads, block-causal spans of 2048, FP8 cache: sampled rows."""
+    w = wl.with_fp8_cache(wl.long_block_causal())
+    rows = []
+    for s in range(w.num_seqs):
+        rows += [s * 8192 + p for p in (0, 1, 2047, 2048, 5000, 6144, 8191)]
+    _prefill(w, rows=np.array(rows), heads=[0, 9, 63])
+
+
+def test_fp8_prefill_single_key_rows_are_scaled_codes(gpu):
+    """A causal row that sees only key 0 returns that key's V row: its codes times v_scale,
+    rounded once to the output type."""
+    w = wl.with_fp8_cache(wl.chunked_prefill(seed=55, num_seqs=2, ctx_hi=0, q_lo=40, q_hi=90))
+    d = Dev(w)
+    d.write_all()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    _, vv = ref.workload_kv(w)
+    g = w.num_heads // w.num_kv_heads
+    for s in range(w.num_seqs):
+        r0 = w.cu_seqlens_q[s]
+        want = vv[w.cu_seq_lens[s]][np.arange(w.num_heads) // g]
+        want = ref.widen(wl.round_to_storage(want.astype(np.float32), w.dtype), w.dtype)
+        assert np.array_equal(got[r0], want)
