@@ -78,7 +78,7 @@ template <typename T, int D, int HPW>
 struct DecodeSteps {
   static constexpr int words = 4 * raw_words<T, D>();
   static constexpr int value =
-      KvFp8<T>::value ? (HPW >= 8 ? 1 : 4)
+      KvFp8<T>::value ? (HPW >= 8 ? 1 : 2)
                       : ((HPW >= 8 || words > 32) ? 1 : (words > 16 || HPW >= 4 ? 2 : 4));
 };
 
@@ -260,7 +260,24 @@ __device__ __forceinline__ void compute_step(const Step<T, D>& st,
     for (int r = 0; r < 2; ++r) pr[r][hh] = st.valid[r] ? fast_exp2(sc[r][hh] - m[hh]) : 0.f;
     l[hh] += pr[0][hh] + pr[1][hh];
   }
-  if constexpr (kHalf) {
+  if constexpr (KvFp8<T>::value) {
+    // pair the two rounds on the codes (one byte permute per two pairs), then widen:
+    // raw word i holds elements 4i..4i+3 of a row
+#pragma unroll
+    for (int i = 0; i < Step<T, D>::RW; ++i) {
+      const uint32_t r0 = st.v[0][i], r1 = st.v[1][i];
+      const uint32_t p01 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);   // r0.b0 r1.b0 r0.b1 r1.b1
+      const uint32_t p23 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);   // r0.b2 r1.b2 r0.b3 r1.b3
+      const uint32_t xy[4] = {widen_fp8x2<false>(T{}, p01), widen_fp8x2<true>(T{}, p01),
+                              widen_fp8x2<false>(T{}, p23), widen_fp8x2<true>(T{}, p23)};
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const uint32_t pp = pack2(T{}, pr[0][hh], pr[1][hh]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[hh][4 * i + e] = dot2(T{}, pp, xy[e], acc[hh][4 * i + e]);
+      }
+    }
+  } else if constexpr (kHalf) {
     // pair the two rounds: x = (v0.lo, v1.lo), y = (v0.hi, v1.hi) for every word
 #pragma unroll
     for (int w = 0; w < C::WPL; ++w) {
