@@ -214,6 +214,50 @@ def run_attention_bench(w, kind, steps, warmup, flush=False):
     return ms, ts.ms()
 
 
+def run_mixed_bench(w, steps, warmup):
+    """The mixed batch through paged_attention_mixed (one attention launch plus the split
+    merge) against the same rows as two calls (prefill of the context sequences, then
+    decode of the generation sequences), both per step between event pairs, with the
+    caches flushed from L2 and MALL before each step."""
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import Dev
+    from paged_kv_scaled_amd import binding as B
+
+    d = Dev(w, fill="zero")
+    d.write_all(split_new=False)
+    nc = w.num_ctx_seqs
+    tc = int(w.cu_seqlens_q[nc])
+    ng = w.num_seqs - nc
+    out = torch.empty_like(d.query)
+    mb = B.mixed_workspace_size(ng, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, w.max_seq_len)
+    mws = torch.zeros(max(mb, 1), dtype=torch.uint8, device="cuda")
+    db = B.decode_workspace_size(ng, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, w.max_seq_len)
+    dws = torch.zeros(max(db, 1), dtype=torch.uint8, device="cuda")
+    ctx_q = int(w.q_lens[:nc].max())
+    fused = lambda: d.mixed(out, mws if mb else None)
+
+    def separate():
+        B.paged_attention_prefill(out[:tc], d.query[:tc], d.cu_q[:nc + 1], d.seq_lens[:nc], d.kc, d.vc,
+                                  d.tables[:nc], w.scale, w.mask, w.span_len, ctx_q, w.max_seq_len)
+        B.paged_attention_decode(out[tc:], d.query[tc:], d.kc, d.vc, d.tables[nc:], d.seq_lens[nc:],
+                                 w.scale, w.max_seq_len, dws if db else None)
+
+    buf = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, call in (("fused", fused), ("separate", separate)):
+        for _ in range(warmup):
+            call()
+        tm = Timer()
+        for _ in range(steps):
+            flush_llc(buf)
+            e = tm.start()
+            call()
+            tm.stop(e)
+        res[name] = tm.ms()
+    return res
+
+
 def med(xs):
     xs = sorted(xs)
     return xs[len(xs) // 2]
@@ -347,7 +391,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads",
                     default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal,mixed_spans,"
-                            "decode_batch_fp8")
+                            "decode_batch_fp8,mixed_batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibration-copy", action="store_true",
@@ -398,6 +442,21 @@ def main():
             continue
         log(f"generating {name}")
         wk = wl.CONFIGS[name]()
+        if wk.num_ctx_seqs is not None:
+            rmx = run_mixed_bench(wk, args.steps, args.warmup)
+            fm, sm = med(rmx["fused"]), med(rmx["separate"])
+            nc = wk.num_ctx_seqs
+            entry = {"metric": "mixed step attention us (one call vs two)", "unit": "us",
+                     "launch_us_median": round(fm * 1e3, 2), "launch_us_min": round(min(rmx["fused"]) * 1e3, 2),
+                     "separate_calls_us_median": round(sm * 1e3, 2),
+                     "speedup_vs_separate": round(sm / fm, 3),
+                     "ctx_seqs": nc, "gen_seqs": wk.num_seqs - nc,
+                     "ctx_rows": int(wk.cu_seqlens_q[nc])}
+            log(f"{name}: {entry}")
+            result_wl[name] = entry
+            del wk
+            torch.cuda.empty_cache()
+            continue
         kind = "decode" if wk.decode else "prefill"
         flush = kind == "prefill"
         ms, sc_ms = run_attention_bench(wk, kind, args.steps, args.warmup, flush=flush)

@@ -252,6 +252,50 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* query, const int32_t*
                                     pkv_mask_mode mask, int32_t span_len, int32_t max_q_len,
                                     int32_t max_seq_len, pkv_dtype dtype, void* stream);
 
+/*
+ * Mixed batch -- one step's context rows (prefill / chunked prefill) and
+ * generation rows (single-token decode) in one call and one attention launch
+ * (plus a small merge launch when a generation sequence is cut into several
+ * pieces).  The launch's first blocks are prefill workgroups and the rest
+ * decode waves, so the decode work starts on the CUs the prefill tail frees.
+ * The Spyre paged-attention PR ("Description") sends the prefill and decode
+ * sequences of a step through one attention call; the CSA2 Vanilla golden PR
+ * ("Description") orders a batch context first, generation after, and keeps
+ * query tiles from crossing that boundary.
+ *
+ * Sequences 0 .. num_ctx_seqs-1 are context sequences: query rows
+ * cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 (cu_seqlens_q int32 [num_ctx_seqs+1],
+ * cu_seqlens_q[num_ctx_seqs] == num_ctx_tokens), the mask rules of
+ * pkv_paged_attention_prefill.  Sequences num_ctx_seqs .. num_seqs-1 are
+ * generation sequences with one query row each, row num_ctx_tokens + (s -
+ * num_ctx_seqs), which attends all seq_lens[s] keys (the last row of any mask).
+ * num_tokens - num_ctx_tokens must equal num_seqs - num_ctx_seqs.
+ * out, query      [num_tokens, num_heads, head_dim] dense (THD).
+ * seq_lens        int32 [num_seqs]; block_tables int32 [num_seqs, max_blocks_per_seq].
+ * max_q_len       host hint >= every context chunk length (0 without context rows).
+ * workspace       device buffer of pkv_mixed_workspace_size(num_seqs -
+ *                 num_ctx_seqs, ...) bytes (may be NULL when that is 0).
+ *                 Contents need no initialisation; calls sharing one workspace
+ *                 must be ordered.
+ * bf16/fp16 with head_dim 64 or 128 and scale > 0 run as one launch; other
+ * cases run the vector-ALU prefill and then the decode (same results, two
+ * launches).  Errors: as pkv_paged_attention_prefill and
+ * pkv_paged_attention_decode, plus INVALID_ARG for an inconsistent boundary.
+ */
+size_t pkv_mixed_workspace_size(int32_t num_gen_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_seq_len);
+
+int pkv_paged_attention_mixed(void* out, const void* query, const int32_t* cu_seqlens_q,
+                              const int32_t* seq_lens, const void* key_cache,
+                              const void* value_cache, int64_t cache_block_stride,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              int32_t num_seqs, int32_t num_tokens, int32_t num_ctx_seqs,
+                              int32_t num_ctx_tokens, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                              float scale, pkv_mask_mode mask, int32_t span_len,
+                              int32_t max_q_len, int32_t max_seq_len, void* workspace,
+                              size_t workspace_bytes, pkv_dtype dtype, void* stream);
+
 /* Prefill with general span lists (vllm-omni piecewise block-causal PR: the
  * `full_attn_spans` metadata -- image blocks attend bidirectionally, text runs
  * causally; its dense reference "(q >= kv) or same_image_block").

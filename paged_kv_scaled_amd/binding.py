@@ -43,6 +43,11 @@ SIGNATURES = {
                                                        _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                        _F, _F, _F, ctypes.c_int, _I32, _I32, _I32,
                                                        ctypes.c_int, _P]),
+    "pkv_mixed_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_paged_attention_mixed": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32,
+                                                 _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                 _F, ctypes.c_int, _I32, _I32, _I32, _P, _SZ,
+                                                 ctypes.c_int, _P]),
     "pkv_paged_attention_prefill_spans": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _I32,
                                                          _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                          _F, _P, _P, _I32, _I32, _I32,
@@ -228,6 +233,32 @@ def paged_attention_prefill_fp8(out, query, cu_seqlens_q, seq_lens, key_cache, v
                                                float(k_scale), float(v_scale), int(mask),
                                                int(span_len), int(max_q_len), int(max_seq_len),
                                                _dtype_code(query), _stream()))
+
+
+def mixed_workspace_size(num_gen_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                         block_size: int, max_seq_len: int) -> int:
+    return int(load().pkv_mixed_workspace_size(num_gen_seqs, num_heads, num_kv_heads, head_dim,
+                                                block_size, max_seq_len))
+
+
+def paged_attention_mixed(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,
+                          block_tables, scale: float, mask: int, span_len: int, max_q_len: int,
+                          max_seq_len: int, num_ctx_seqs: int, num_ctx_tokens: int,
+                          workspace=None):
+    """Context sequences first (rows by cu_seqlens_q), then one-row generation sequences."""
+    lib = load()
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    T, H, D = query.shape
+    S = seq_lens.shape[0]
+    assert D == d and out.shape == query.shape and query.is_contiguous() and out.is_contiguous()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attention_mixed(_ptr(out), _ptr(query), _ptr(cu_seqlens_q),
+                                         _ptr(seq_lens), _ptr(key_cache), _ptr(value_cache),
+                                         bstride, _ptr(block_tables), block_tables.shape[1], S, T,
+                                         int(num_ctx_seqs), int(num_ctx_tokens), H, hkv, D, nb,
+                                         bs, float(scale), int(mask), int(span_len),
+                                         int(max_q_len), int(max_seq_len), _ptr(workspace),
+                                         ws_bytes, _dtype_code(query), _stream()))
 
 
 def paged_attention_prefill_spans(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,

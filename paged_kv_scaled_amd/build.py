@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-SOURCES = ["api.cpp", "scatter.hip", "decode.hip", "prefill_valu.hip", "prefill_mfma.hip", "checks.hip"]
+SOURCES = ["api.cpp", "scatter.hip", "decode.hip", "prefill_valu.hip", "prefill_mfma.hip", "mixed.hip",
+           "checks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -27,13 +28,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-# Per-file code-generation options.  The MFMA prefill kernel keeps its accumulators in
+# Per-file code-generation options.  The MFMA prefill kernel (also inside the mixed-batch
+# kernel) keeps its accumulators in
 # VGPRs (VGPR-form MFMA): with the default AGPR form the compiler copies the output
 # accumulator between register files on every key tile.  It also runs with the IEEE mode
 # bit off and NaN-free inputs assumed: in IEEE mode every fmax operand that comes out of an
 # MFMA is first canonicalised (one extra VALU op per score), and NaN keys or queries give
 # undefined results either way.
-EXTRA = {"prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]}
+_MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]
+EXTRA = {"prefill_mfma.hip": _MFMA_FLAGS, "mixed.hip": _MFMA_FLAGS}
 
 
 def _compile(src: str) -> str:

@@ -477,6 +477,139 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* query, const int32_t*
                         "pkv_paged_attention_prefill_fp8", true, k_scale, v_scale);
 }
 
+size_t pkv_mixed_workspace_size(int32_t num_gen_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_seq_len) {
+  if (num_gen_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      !PKV_HEAD_DIM_SUPPORTED(head_dim) || !is_pow2_in(block_size, 1, 256) || max_seq_len < 0)
+    return 0;
+  return pkv::decode_plan(num_gen_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                          max_seq_len, true)
+      .workspace_bytes;
+}
+
+int pkv_paged_attention_mixed(void* out, const void* query, const int32_t* cu_seqlens_q,
+                              const int32_t* seq_lens, const void* key_cache,
+                              const void* value_cache, int64_t cache_block_stride,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              int32_t num_seqs, int32_t num_tokens, int32_t num_ctx_seqs,
+                              int32_t num_ctx_tokens, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                              float scale, pkv_mask_mode mask, int32_t span_len,
+                              int32_t max_q_len, int32_t max_seq_len, void* workspace,
+                              size_t workspace_bytes, pkv_dtype dtype, void* stream) {
+  clear_error();
+  const char* what = "pkv_paged_attention_mixed";
+  int rc;
+  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
+  if (mask != PKV_MASK_NONE && mask != PKV_MASK_CAUSAL && mask != PKV_MASK_BLOCK_CAUSAL)
+    return fail(PKV_ERR_INVALID_ARG, "unknown mask mode %d", (int)mask);
+  if (mask == PKV_MASK_BLOCK_CAUSAL && span_len <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "BLOCK_CAUSAL needs span_len > 0 (got %d)", span_len);
+  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || max_seq_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs, num_tokens, max_q_len, max_seq_len must be >= 0");
+  if (num_ctx_seqs < 0 || num_ctx_seqs > num_seqs || num_ctx_tokens < 0 ||
+      num_ctx_tokens > num_tokens)
+    return fail(PKV_ERR_INVALID_ARG, "need 0 <= num_ctx_seqs <= num_seqs and 0 <= num_ctx_tokens "
+                "<= num_tokens (got %d of %d, %d of %d)", num_ctx_seqs, num_seqs, num_ctx_tokens,
+                num_tokens);
+  const int32_t num_gen = num_seqs - num_ctx_seqs;
+  if (num_tokens - num_ctx_tokens != num_gen)
+    return fail(PKV_ERR_INVALID_ARG, "generation sequences take one query row each: "
+                "num_tokens - num_ctx_tokens (%d) != num_seqs - num_ctx_seqs (%d)",
+                num_tokens - num_ctx_tokens, num_gen);
+  if (num_ctx_seqs == 0 && num_ctx_tokens != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_ctx_tokens must be 0 without context sequences");
+  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
+                        num_kv_heads, head_dim)) != PKV_OK)
+    return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads)) != PKV_OK) return rc;
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID_ARG, "scale is NaN");
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !seq_lens || !block_tables || (num_ctx_seqs > 0 && !cu_seqlens_q))
+    return fail(PKV_ERR_INVALID_ARG,
+                "out, query, seq_lens, block_tables (and cu_seqlens_q with context sequences) "
+                "must not be NULL");
+  if (num_ctx_tokens > 0 && max_q_len == 0)
+    return fail(PKV_ERR_INVALID_ARG, "max_q_len must be > 0 when num_ctx_tokens > 0");
+  if (max_q_len > max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_q_len (%d) > max_seq_len (%d)", max_q_len, max_seq_len);
+  if ((int64_t)max_q_len * num_ctx_seqs < num_ctx_tokens)
+    return fail(PKV_ERR_INVALID_ARG, "num_ctx_tokens (%d) > num_ctx_seqs*max_q_len (%lld)",
+                num_ctx_tokens, (long long)max_q_len * num_ctx_seqs);
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
+                (long long)max_blocks_per_seq * block_size, max_seq_len);
+  if ((rc = check_attn_alignment(out, query, key_cache, value_cache, cache_block_stride,
+                                 dtype == PKV_F32 ? 4 : 2)) != PKV_OK)
+    return rc;
+  const pkv::DecodePlan plan = pkv::decode_plan(num_gen > 0 ? num_gen : 1, num_heads,
+                                                num_kv_heads, head_dim, block_size, max_seq_len,
+                                                true);
+  if (num_gen > 0 && plan.workspace_bytes > 0 &&
+      (!workspace || workspace_bytes < plan.workspace_bytes))
+    return fail(PKV_ERR_WORKSPACE, "mixed-batch workspace of %zu bytes required (got %zu at %p)",
+                plan.workspace_bytes, workspace_bytes, workspace);
+  const size_t eb = dtype == PKV_F32 ? 4 : 2;
+  const size_t row_bytes = (size_t)num_heads * head_dim * eb;
+  pkv::AttnArgs ctx{};
+  ctx.out = out;
+  ctx.query = query;
+  ctx.cu_seqlens_q = cu_seqlens_q;
+  ctx.seq_lens = seq_lens;
+  ctx.key_cache = key_cache;
+  ctx.value_cache = value_cache;
+  ctx.block_stride = cache_block_stride;
+  ctx.block_tables = block_tables;
+  ctx.max_blocks_per_seq = max_blocks_per_seq;
+  ctx.num_seqs = num_ctx_seqs;
+  ctx.num_tokens = num_ctx_tokens;
+  ctx.num_heads = num_heads;
+  ctx.num_kv_heads = num_kv_heads;
+  ctx.head_dim = head_dim;
+  ctx.num_blocks = num_blocks;
+  ctx.block_size = block_size;
+  ctx.scale = scale;
+  ctx.mask = mask;
+  ctx.span_len = mask == PKV_MASK_BLOCK_CAUSAL ? span_len : 1;
+  ctx.max_q_len = max_q_len;
+  ctx.max_seq_len = max_seq_len;
+  ctx.dtype = (int)dtype;
+  pkv::AttnArgs gen = ctx;
+  gen.out = static_cast<char*>(out) + (size_t)num_ctx_tokens * row_bytes;
+  gen.query = static_cast<const char*>(query) + (size_t)num_ctx_tokens * row_bytes;
+  gen.cu_seqlens_q = nullptr;
+  gen.seq_lens = seq_lens + num_ctx_seqs;
+  gen.block_tables = block_tables + (size_t)num_ctx_seqs * max_blocks_per_seq;
+  gen.num_seqs = num_gen;
+  gen.num_tokens = num_gen;
+  gen.mask = PKV_MASK_NONE;
+  gen.max_q_len = 1;
+  gen.workspace = workspace;
+  if ((rc = guard_word(&ctx.guard, what)) != PKV_OK) return rc;
+  gen.guard = ctx.guard;
+  if (ctx.guard != nullptr) {
+    if (num_ctx_seqs > 0) {
+      pkv::CheckSeqArgs c{nullptr, nullptr, 0, seq_lens, nullptr, cu_seqlens_q, block_tables,
+                          num_ctx_seqs, max_blocks_per_seq, num_blocks, block_size, max_seq_len,
+                          max_q_len, num_ctx_tokens, 0};
+      if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream), what)) != PKV_OK) return rc;
+    }
+    if (num_gen > 0) {
+      pkv::CheckSeqArgs c{nullptr, nullptr, 0, gen.seq_lens, nullptr, nullptr, gen.block_tables,
+                          num_gen, max_blocks_per_seq, num_blocks, block_size, max_seq_len, 1, 0, 0};
+      if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream), what)) != PKV_OK) return rc;
+    }
+  }
+  if (pkv::mixed_fused_supported((int)dtype, head_dim, scale, false))
+    return launched(pkv::launch_mixed(ctx, gen, plan, (hipStream_t)stream), what);
+  // fp32 or head_dim 16: the vector-ALU prefill, then split-mode decode (two launches)
+  if (num_ctx_seqs > 0 && num_ctx_tokens > 0 &&
+      (rc = launched(pkv::launch_prefill_valu(ctx, (hipStream_t)stream), what)) != PKV_OK)
+    return rc;
+  if (num_gen > 0) return launched(pkv::launch_decode(gen, plan, (hipStream_t)stream), what);
+  return PKV_OK;
+}
+
 int pkv_paged_attention_prefill_spans(void* out, const void* query, const int32_t* cu_seqlens_q,
                                       const int32_t* seq_lens, const void* key_cache,
                                       const void* value_cache, int64_t cache_block_stride,

@@ -135,6 +135,13 @@ __device__ __forceinline__ int visible_end(int mask, int a, int L, int span,
   return L;
 }
 
+// log2 of a power of two (block sizes, tiling factors).
+inline int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
 // True when a device-side precondition check on this device has failed (the guard is
 // the error word, null when checks are off): every kernel then returns before it
 // reads or writes anything else.

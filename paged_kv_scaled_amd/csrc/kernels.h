@@ -100,8 +100,10 @@ struct DecodePlan {
   int max_seq_len;
   size_t workspace_bytes;
 };
+// mixed: the plan of the decode rows of a mixed batch -- at most 4 heads per wave (they run
+// inside the prefill kernel's register budget).
 DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                       int block_size, int max_seq_len);
+                       int block_size, int max_seq_len, bool mixed = false);
 
 hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream);
 // Quantising scatter into an FP8 (E4M3) cache: a.dtype is the source type, the cache
@@ -114,5 +116,11 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, hipStream_t 
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_valu(const AttnArgs& a, hipStream_t stream);
 bool prefill_mfma_supported(int dtype, int head_dim, float scale);
+// Mixed batch in one launch (plus the split merge): ctx holds the context sequences (THD
+// rows from 0), gen the generation sequences (one row each, pointers already offset);
+// plan from decode_plan(..., mixed = true) for gen.
+bool mixed_fused_supported(int dtype, int head_dim, float scale, bool kv_fp8);
+hipError_t launch_mixed(const AttnArgs& ctx, const AttnArgs& gen, const DecodePlan& plan,
+                        hipStream_t stream);
 
 }  // namespace pkv

@@ -159,12 +159,6 @@ kv_scatter_fp8_kernel(const typename S::storage* __restrict__ key,
   }
 }
 
-int log2_exact(int x) {
-  int s = 0;
-  while ((1 << s) < x) ++s;
-  return s;
-}
-
 // Widest vector that divides every byte offset the kernel forms.
 int pick_vec(int64_t row_b, int64_t a, int64_t b, const void* p0, const void* p1, const void* p2,
              const void* p3) {

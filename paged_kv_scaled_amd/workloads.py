@@ -84,6 +84,8 @@ class Workload:
     kv_dtype: Optional[str] = None  # "fp8": the cache holds E4M3 codes of key/value
     k_scale: float = 1.0            # FP8 cache: value = code * scale
     v_scale: float = 1.0
+    num_ctx_seqs: Optional[int] = None   # mixed batch: context sequences first, then
+                                         # one-row generation sequences
 
     def span_arrays(self):
         """The span lists flattened for the library: int32 [num_spans, 2] (start, end)
@@ -299,6 +301,26 @@ def decode_batch_fp8(seed: int = 1, **kw) -> Workload:
     return with_fp8_cache(decode_batch(seed=seed, **kw))
 
 
+def mixed_batch(seed: int = 6, num_ctx: int = 8, num_gen: int = 64, ctx_hi: int = 2048,
+                q_lo: int = 32, q_hi: int = 512, lo: int = 256, hi: int = 4096,
+                dtype: str = "bf16", num_heads: int = 32, num_kv_heads: int = 8,
+                head_dim: int = 128, block_size: int = 16, mask: int = MASK_CAUSAL,
+                span_len: int = 0) -> Workload:
+    """One serving step: the chunked-prefill shape (8 sequences, context U{0..2048} plus a
+    chunk U{32..512}) followed by the decode-batch shape (64 one-token sequences with
+    contexts U[256, 4096]), 32 q / 8 kv heads, D 128, B 16, causal."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(0, ctx_hi + 1, size=num_ctx).astype(np.int32)     # draw 1
+    ql = rng.integers(q_lo, q_hi + 1, size=num_ctx).astype(np.int32)
+    gl = rng.integers(lo, hi + 1, size=num_gen).astype(np.int32)
+    lens = np.concatenate([ctx + ql, gl])
+    qls = np.concatenate([ql, np.ones(num_gen, np.int32)])
+    w = build("mixed_batch", seed, dtype, lens, qls, num_heads, num_kv_heads, head_dim,
+              block_size, mask, span_len=span_len, rng=rng)
+    w.num_ctx_seqs = num_ctx
+    return w
+
+
 def long_block_causal_fp8(seed: int = 4, **kw) -> Workload:
     """The long block-causal prefill (4 x 8192 tokens, 64 q / 8 kv heads, spans of 2048)
     over an FP8 cache."""
@@ -314,6 +336,7 @@ CONFIGS = {
     "mixed_spans": mixed_spans,
     "decode_batch_fp8": decode_batch_fp8,
     "long_block_causal_fp8": long_block_causal_fp8,
+    "mixed_batch": mixed_batch,
 }
 
 

@@ -103,6 +103,21 @@ class Dev:
                                      w.scale, w.max_seq_len, ws if ws_bytes else None)
         return out
 
+    def mixed(self, out=None, ws=None):
+        """The whole batch through paged_attention_mixed (context sequences first)."""
+        w = self.w
+        nc = w.num_ctx_seqs
+        out = out if out is not None else torch.empty_like(self.query)
+        if ws is None:
+            ws_bytes = B.mixed_workspace_size(w.num_seqs - nc, w.num_heads, w.num_kv_heads,
+                                              w.head_dim, w.block_size, w.max_seq_len)
+            ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+        ctx_q = int(w.q_lens[:nc].max()) if nc else 0
+        B.paged_attention_mixed(out, self.query, self.cu_q[:nc + 1], self.seq_lens, self.kc,
+                                self.vc, self.tables, w.scale, w.mask, w.span_len, ctx_q,
+                                w.max_seq_len, nc, int(w.cu_seqlens_q[nc]), ws)
+        return out
+
     def prefill(self, out=None):
         w = self.w
         out = out if out is not None else torch.empty_like(self.query)
