@@ -24,6 +24,9 @@ steps; the vllm-omni piecewise block-causal PR for the block-causal mask):
   scores   : z_p = scale * <q, k_p>, q head h reads kv head h // (H / Hkv)
   softmax  : stable: m = max z, w = exp(z - m), out = sum w v / sum w, lse = m + log sum w
   empty row: no visible key -> out = 0, lse = -inf
+  small-seq training path (ROCm TransformerEngine small-seq PR): the forward also returns
+  the attention weights P; the backward is the gradient of sum(d_out * out) taken in the
+  pages' steps (grad_V, grad_attn, softmax backward, grad_Q / grad_K)
 
 Parity status of each function is stated in its docstring; every function here
 is pinned by `tests/test_oracle_pins.py` against something other than itself.
@@ -297,6 +300,68 @@ def workload_attention(w, rows=None, heads=None):
     return paged_attention(q, k, v, w.cu_seqlens_q, w.seq_lens, w.num_kv_heads, w.scale,
                            w.mask, w.span_len, rows=rows, heads=heads,
                            spans=getattr(w, "spans", None))
+
+
+# ----------------------------------------------------------------------------------------
+# small-seq training path: attention weights and the backward pass (ROCm TransformerEngine
+# small-seq PR, description: the forward writes the attention weights for s_q = 1 and
+# s_kv <= 16, the backward reads them and computes grad_V, grad_attn, the softmax backward
+# and grad_Q / grad_K).  The backward is the gradient of sum(d_out * out).
+# ----------------------------------------------------------------------------------------
+
+def smallseq_forward(q: np.ndarray, keys: Sequence[np.ndarray], values: Sequence[np.ndarray],
+                     num_kv_heads: int, scale: float, max_kv: Optional[int] = None):
+    """One query row per sequence.  q [S, H, D]; keys[s], values[s] [L_s, Hkv, D].
+
+    Returns out [S, H, D] and the attention weights P [S, H, max_kv]:
+    P[s, h, k] = softmax over k < L_s of scale <q[s, h], K_s[k, h // g]>, zero for
+    k >= L_s (an empty sequence has an all-zero row and a zero output)."""
+    S, H, D = q.shape
+    if max_kv is None:
+        max_kv = max([int(k.shape[0]) for k in keys] + [1])
+    out = np.zeros((S, H, values[0].shape[-1] if len(values) else D), np.float64)
+    P = np.zeros((S, H, max_kv), np.float64)
+    for s in range(S):
+        L = int(keys[s].shape[0])
+        if L == 0:
+            continue
+        for h in range(H):
+            kvh = kv_head_of(h, H, num_kv_heads)
+            z = scale * (keys[s][:, kvh, :] @ q[s, h])
+            w = np.exp(z - z.max())
+            P[s, h, :L] = w / w.sum()
+            out[s, h] = P[s, h, :L] @ values[s][:, kvh, :]
+    return out, P
+
+
+def smallseq_backward(q: np.ndarray, keys: Sequence[np.ndarray], values: Sequence[np.ndarray],
+                      d_out: np.ndarray, num_kv_heads: int, scale: float):
+    """Gradients of sum(d_out * out) for smallseq_forward, in the pages' four steps, from
+    the exact attention weights P (query head h of kv head j = h // g):
+      grad_V      dV[k, j] = sum over h of j of P[h, k] dO[h]
+      grad_attn   dP[h, k] = <dO[h], V[k, j]>
+      softmax bwd dS[h, k] = P[h, k] (dP[h, k] - sum_k' P[h, k'] dP[h, k'])
+      grad_Q      dQ[h]    = scale sum_k dS[h, k] K[k, j]
+      grad_K      dK[k, j] = scale sum over h of j of dS[h, k] q[h]
+    Returns dq [S, H, D] and per-sequence dk[s], dv[s] [L_s, Hkv, D]."""
+    S, H, D = q.shape
+    _, P = smallseq_forward(q, keys, values, num_kv_heads, scale)
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk = [np.zeros(k.shape, np.float64) for k in keys]
+    dv = [np.zeros(v.shape, np.float64) for v in values]
+    for s in range(S):
+        L = int(keys[s].shape[0])
+        if L == 0:
+            continue
+        for h in range(H):
+            kvh = kv_head_of(h, H, num_kv_heads)
+            p = P[s, h, :L]
+            dv[s][:, kvh, :] += np.outer(p, d_out[s, h])                       # grad_V
+            dp = values[s][:, kvh, :] @ d_out[s, h]                            # grad_attn
+            ds = p * (dp - p @ dp)                                             # softmax bwd
+            dq[s, h] = scale * (ds @ keys[s][:, kvh, :])                       # grad_Q
+            dk[s][:, kvh, :] += scale * np.outer(ds, q[s, h])                  # grad_K
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------------------

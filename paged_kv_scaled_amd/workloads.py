@@ -86,6 +86,8 @@ class Workload:
     v_scale: float = 1.0
     num_ctx_seqs: Optional[int] = None   # mixed batch: context sequences first, then
                                          # one-row generation sequences
+    d_out: Optional[np.ndarray] = None   # small-seq backward: gradient of the output
+                                         # [S, H, D], storage bits of `dtype`
 
     def span_arrays(self):
         """The span lists flattened for the library: int32 [num_spans, 2] (start, end)
@@ -247,6 +249,20 @@ def smallseq_varlen(seed: int = 3, num_seqs: int = 30720, dtype: str = "bf16",
                  MASK_NONE, spare_blocks=spare_blocks, decode=True, rng=rng)
 
 
+def smallseq_train(seed: int = 7, num_seqs: int = 30720, dtype: str = "bf16",
+                   num_heads: int = 16, num_kv_heads: int = 16, head_dim: int = 128,
+                   kv_choices=SMALLSEQ_KV) -> Workload:
+    """The small-seq shape for the training path: s_q = 1, s_kv uniform over
+    {2,4,6,8,12,16}, 16 heads (MHA), D 128, B 16, plus the output gradient d_out ~ N(0,1)
+    (drawn after Q, K and V)."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(kv_choices, np.int32)[rng.integers(0, len(kv_choices), size=num_seqs)]
+    w = build("smallseq_train", seed, dtype, lens, np.ones(num_seqs, np.int32), num_heads,
+              num_kv_heads, head_dim, 16, MASK_NONE, decode=True, rng=rng)
+    w.d_out = _draw_values(rng, (num_seqs, num_heads, head_dim), dtype)     # draw 4
+    return w
+
+
 def long_block_causal(seed: int = 4, num_seqs: int = 4, seq_len: int = 8192, dtype: str = "bf16",
                       num_heads: int = 64, spare_blocks: int = 1) -> Workload:
     """4 x 8192 tokens, 64 q heads / 8 kv heads, D 128, B 16, block-causal spans of 2048."""
@@ -337,6 +353,7 @@ CONFIGS = {
     "decode_batch_fp8": decode_batch_fp8,
     "long_block_causal_fp8": long_block_causal_fp8,
     "mixed_batch": mixed_batch,
+    "smallseq_train": smallseq_train,
 }
 
 

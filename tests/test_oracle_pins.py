@@ -575,3 +575,141 @@ def test_fp8_workload_oracle_uses_dequantised_rows():
     # the quantisation error stays inside half a code step (relative 2^-4) plus the subnormal step
     kw = ref.widen(w.key, "bf16")
     assert np.all(np.abs(k - kw) <= np.abs(kw) * 2.0 ** -4 + 2.0 ** -10 * w.k_scale)
+
+
+# ---- small-seq training path: attention weights and backward ---------------------------
+
+def _smallseq_case(seed, S=3, H=4, Hkv=2, D=5, lens=(1, 3, 7)):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((S, H, D))
+    keys = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    values = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    d_out = rng.standard_normal((S, H, D))
+    return q, keys, values, d_out
+
+
+def _loss(q, keys, values, d_out, Hkv, scale):
+    out, _ = ref.smallseq_forward(q, keys, values, Hkv, scale)
+    return float(np.sum(out * d_out))
+
+
+def test_smallseq_forward_matches_paged_attention_decode_rows():
+    """The forward is the decode case of the general oracle (one row per sequence), and
+    its weights are a distribution over the first L_s keys."""
+    q, keys, values, _ = _smallseq_case(11)
+    out, P = ref.smallseq_forward(q, keys, values, 2, 0.37)
+    lens = np.array([k.shape[0] for k in keys], np.int32)
+    cu = np.arange(len(lens) + 1, dtype=np.int32)
+    want, _ = ref.paged_attention(q, keys, values, cu, lens, 2, 0.37, ref.MASK_NONE)
+    assert np.allclose(out, want, rtol=0, atol=1e-13)
+    assert np.allclose(P.sum(-1), 1.0, atol=1e-14)
+    for s, L in enumerate(lens):
+        assert np.all(P[s, :, L:] == 0)
+
+
+def test_smallseq_backward_matches_finite_differences():
+    """Central differences of sum(d_out * out) in every coordinate of q, K and V."""
+    Hkv, scale, eps = 2, 0.41, 1e-6
+    q, keys, values, d_out = _smallseq_case(12)
+    dq, dk, dv = ref.smallseq_backward(q, keys, values, d_out, Hkv, scale)
+
+    def fd(arr, idx, rebuild):
+        a = arr.copy(); a[idx] += eps
+        b = arr.copy(); b[idx] -= eps
+        return (_loss(*rebuild(a), d_out, Hkv, scale) - _loss(*rebuild(b), d_out, Hkv, scale)) / (2 * eps)
+
+    for idx in np.ndindex(q.shape):
+        g = fd(q, idx, lambda a: (a, keys, values))
+        assert abs(g - dq[idx]) < 1e-7 * max(1.0, abs(g)), ("dq", idx, g, dq[idx])
+    for s in range(len(keys)):
+        for idx in np.ndindex(keys[s].shape):
+            def rk(a, s=s):
+                ks = list(keys); ks[s] = a
+                return (q, ks, values)
+            def rv(a, s=s):
+                vs = list(values); vs[s] = a
+                return (q, keys, vs)
+            gk = fd(keys[s], idx, rk)
+            gv = fd(values[s], idx, rv)
+            assert abs(gk - dk[s][idx]) < 1e-7 * max(1.0, abs(gk)), ("dk", s, idx)
+            assert abs(gv - dv[s][idx]) < 1e-7 * max(1.0, abs(gv)), ("dv", s, idx)
+
+
+def test_smallseq_backward_matches_torch_autograd():
+    """torch float64 autograd of softmax attention written with torch ops (GQA by
+    repeat_interleave), on several random batches."""
+    for seed in range(4):
+        rng = np.random.default_rng(100 + seed)
+        H, Hkv, D = 6, 3, 8
+        lens = list(rng.integers(1, 17, size=5))
+        q, keys, values, d_out = _smallseq_case(100 + seed, S=5, H=H, Hkv=Hkv, D=D, lens=lens)
+        dq, dk, dv = ref.smallseq_backward(q, keys, values, d_out, Hkv, 0.3)
+        for s in range(5):
+            tq = torch.tensor(q[s], requires_grad=True)                       # [H, D]
+            tk = torch.tensor(keys[s], requires_grad=True)                    # [L, Hkv, D]
+            tv = torch.tensor(values[s], requires_grad=True)
+            ke = tk.repeat_interleave(H // Hkv, dim=1)                        # [L, H, D]
+            ve = tv.repeat_interleave(H // Hkv, dim=1)
+            z = 0.3 * torch.einsum("hd,lhd->hl", tq, ke)
+            o = torch.einsum("hl,lhd->hd", torch.softmax(z, dim=-1), ve)
+            (o * torch.tensor(d_out[s])).sum().backward()
+            assert np.allclose(tq.grad.numpy(), dq[s], atol=1e-12)
+            assert np.allclose(tk.grad.numpy(), dk[s], atol=1e-12)
+            assert np.allclose(tv.grad.numpy(), dv[s], atol=1e-12)
+
+
+def test_smallseq_backward_closed_forms():
+    """One key: P = 1, so dV = the sum of dO over the group's heads and dQ = dK = 0.
+    Any length: the key gradients of a query sum to zero (the softmax backward removes
+    the mean), so sum_k dK[k] = 0."""
+    q, keys, values, d_out = _smallseq_case(13, lens=(1, 1, 1))
+    dq, dk, dv = ref.smallseq_backward(q, keys, values, d_out, 2, 0.5)
+    assert np.all(dq == 0)
+    for s in range(3):
+        assert np.all(dk[s] == 0)
+        assert np.allclose(dv[s][0], d_out[s].reshape(2, 2, -1).sum(axis=1), atol=1e-15)
+    q, keys, values, d_out = _smallseq_case(14, lens=(16, 5, 9))
+    _, dk, _ = ref.smallseq_backward(q, keys, values, d_out, 2, 0.5)
+    for s in range(3):
+        assert np.allclose(dk[s].sum(axis=0), 0.0, atol=1e-13)
+
+
+def test_smallseq_backward_gqa_equals_mha_with_repeated_kv():
+    """Grouped heads: the same as MHA on repeated K/V with dK, dV summed over the group."""
+    q, keys, values, d_out = _smallseq_case(15, S=2, H=6, Hkv=2, D=4, lens=(5, 12))
+    dq, dk, dv = ref.smallseq_backward(q, keys, values, d_out, 2, 0.7)
+    kr = [np.repeat(k, 3, axis=1) for k in keys]
+    vr = [np.repeat(v, 3, axis=1) for v in values]
+    dq2, dk2, dv2 = ref.smallseq_backward(q, kr, vr, d_out, 6, 0.7)
+    assert np.allclose(dq, dq2, atol=1e-14)
+    for s in range(2):
+        assert np.allclose(dk[s], dk2[s].reshape(dk2[s].shape[0], 2, 3, -1).sum(axis=2), atol=1e-14)
+        assert np.allclose(dv[s], dv2[s].reshape(dv2[s].shape[0], 2, 3, -1).sum(axis=2), atol=1e-14)
+
+
+def test_smallseq_backward_planted_mistake_is_caught():
+    """A softmax backward without the mean term fails the finite-difference pin."""
+    Hkv, scale, eps = 2, 0.41, 1e-6
+    q, keys, values, d_out = _smallseq_case(16)
+    _, P = ref.smallseq_forward(q, keys, values, Hkv, scale)
+    s, h, L = 2, 1, keys[2].shape[0]
+    p = P[s, h, :L]
+    dp = values[s][:, h // 2, :] @ d_out[s, h]
+    wrong = scale * ((p * dp) @ keys[s][:, h // 2, :])       # dS = P dP, mean dropped
+    a = q.copy(); a[s, h, 0] += eps
+    b = q.copy(); b[s, h, 0] -= eps
+    g = (_loss(a, keys, values, d_out, Hkv, scale) - _loss(b, keys, values, d_out, Hkv, scale)) / (2 * eps)
+    assert abs(g - wrong[0]) > 1e-4
+
+
+def test_smallseq_train_workload_feeds_the_oracle():
+    """The training workload's rows, split per sequence, run through the oracle; with one
+    query row per sequence its forward equals the general oracle's decode rows."""
+    w = wl.smallseq_train(num_seqs=40)
+    q = ref.widen(w.query, w.dtype)
+    k = ref.split_logical(ref.widen(w.key, w.dtype), w.cu_seq_lens)
+    v = ref.split_logical(ref.widen(w.value, w.dtype), w.cu_seq_lens)
+    out, P = ref.smallseq_forward(q, k, v, w.num_kv_heads, w.scale, max_kv=16)
+    want, _ = ref.workload_attention(w)
+    assert np.allclose(out, want, atol=1e-13)
+    assert P.shape == (40, 16, 16) and w.d_out.shape == (40, 16, 128)
