@@ -52,6 +52,8 @@
  *   slots in [0, num_blocks*block_size) or negative, unique within one call;
  *   block_tables entries in [0, num_blocks) for the blocks a sequence uses;
  *   seq_lens[s] <= max_blocks_per_seq*block_size and <= max_seq_len;
+ *   cu_seq_lens (gather, small-seq backward) prefix sums from 0 to the total,
+ *   equal to the differences of seq_lens where both are given;
  *   cu_seqlens_q non-decreasing with q_s = cu[s+1]-cu[s] <= min(seq_lens[s], max_q_len);
  *   cu_seqlens_q[num_seqs] == num_tokens.
  */
@@ -295,6 +297,56 @@ int pkv_paged_attention_mixed(void* out, const void* query, const int32_t* cu_se
                               float scale, pkv_mask_mode mask, int32_t span_len,
                               int32_t max_q_len, int32_t max_seq_len, void* workspace,
                               size_t workspace_bytes, pkv_dtype dtype, void* stream);
+
+/*
+ * Small-seq training path (ROCm TransformerEngine small-seq PR, description:
+ * varlen cross attention with one query token per sequence and s_kv <= 16; the
+ * forward writes the attention weights, the backward reads them and computes
+ * grad_V, grad_attn, the softmax backward and grad_Q / grad_K).  Keys and
+ * values come from the paged cache through the block table, as in decode.
+ *
+ * pkv_smallseq_attention_fwd -- out[s, h] = sum_k P[s, h, k] V_s[k, h / g] with
+ *   P[s, h, k] = softmax over k < seq_lens[s] of scale <q[s, h], K_s[k, h / g]>.
+ * out, query      [num_seqs, num_heads, head_dim] dense.
+ * weights         [num_seqs, num_heads, max_seq_len] in dtype: P rounded to
+ *                 nearest even, zero for k >= seq_lens[s] (a sequence with no
+ *                 keys gets a zero row and a zero output).
+ * max_seq_len     1..16, >= every seq_lens[s]; the row length of weights.
+ * dtype           PKV_BF16 or PKV_F16; head_dim 16, 64 or 128.
+ * Errors: INVALID_ARG (null pointers, max_seq_len outside [1, 16], sizes,
+ * alignment), UNSUPPORTED (dtype, head_dim).
+ */
+int pkv_smallseq_attention_fwd(void* out, void* weights, const void* query,
+                               const void* key_cache, const void* value_cache,
+                               int64_t cache_block_stride, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                               float scale, int32_t max_seq_len, pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_smallseq_attention_bwd -- gradients of sum(d_out * out) for the forward
+ * above, from the weights it saved (P as stored, not recomputed):
+ *   dV[k, j] = sum over the heads h of kv head j of P[h, k] dO[h]
+ *   dP[h, k] = <dO[h], V[k, j]>;  dS = P (dP - sum_k P dP)
+ *   dQ[h]    = scale sum_k dS[h, k] K[k, j]
+ *   dK[k, j] = scale sum over the heads h of kv head j of dS[h, k] q[h]
+ * d_query, d_out, query  [num_seqs, num_heads, head_dim].
+ * d_key, d_value  [total_kv, num_kv_heads, head_dim]: key k of sequence s at row
+ *                 cu_seq_lens[s] + k (THD, the layout of the packed K/V inputs).
+ * cu_seq_lens     int32 [num_seqs+1], prefix sums of seq_lens, ending at total_kv.
+ * Scalars and errors as pkv_smallseq_attention_fwd.  Accumulation is fp32;
+ * results are rounded to nearest even.
+ */
+int pkv_smallseq_attention_bwd(void* d_query, void* d_key, void* d_value, const void* d_out,
+                               const void* query, const void* weights, const void* key_cache,
+                               const void* value_cache, int64_t cache_block_stride,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, const int32_t* cu_seq_lens,
+                               int32_t num_seqs, int32_t total_kv, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                               int32_t block_size, float scale, int32_t max_seq_len,
+                               pkv_dtype dtype, void* stream);
 
 /* Prefill with general span lists (vllm-omni piecewise block-causal PR: the
  * `full_attn_spans` metadata -- image blocks attend bidirectionally, text runs

@@ -48,6 +48,12 @@ SIGNATURES = {
                                                  _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                  _F, ctypes.c_int, _I32, _I32, _I32, _P, _SZ,
                                                  ctypes.c_int, _P]),
+    "pkv_smallseq_attention_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
+                                                  _I32, _I32, _I32, _I32, _I32, _F, _I32,
+                                                  ctypes.c_int, _P]),
+    "pkv_smallseq_attention_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _I32,
+                                                  _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                  _I32, _F, _I32, ctypes.c_int, _P]),
     "pkv_paged_attention_prefill_spans": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _I32,
                                                          _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                          _F, _P, _P, _I32, _I32, _I32,
@@ -259,6 +265,38 @@ def paged_attention_mixed(out, query, cu_seqlens_q, seq_lens, key_cache, value_c
                                          bs, float(scale), int(mask), int(span_len),
                                          int(max_q_len), int(max_seq_len), _ptr(workspace),
                                          ws_bytes, _dtype_code(query), _stream()))
+
+
+def smallseq_attention_fwd(out, weights, query, key_cache, value_cache, block_tables, seq_lens,
+                           scale: float, max_seq_len: int):
+    """One query row per sequence (<= 16 keys): out [S, H, D], weights [S, H, max_seq_len]."""
+    lib = load()
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    S, H, D = query.shape
+    assert D == d and out.shape == query.shape and query.is_contiguous() and out.is_contiguous()
+    assert weights.shape == (S, H, max_seq_len) and weights.is_contiguous()
+    _check(lib.pkv_smallseq_attention_fwd(_ptr(out), _ptr(weights), _ptr(query), _ptr(key_cache),
+                                          _ptr(value_cache), bstride, _ptr(block_tables),
+                                          block_tables.shape[1], _ptr(seq_lens), S, H, hkv, D, nb,
+                                          bs, float(scale), int(max_seq_len), _dtype_code(query),
+                                          _stream()))
+
+
+def smallseq_attention_bwd(d_query, d_key, d_value, d_out, query, weights, key_cache,
+                           value_cache, block_tables, seq_lens, cu_seq_lens, scale: float,
+                           max_seq_len: int):
+    """Gradients from the saved weights; d_key/d_value [total_kv, Hkv, D] by cu_seq_lens."""
+    lib = load()
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    S, H, D = query.shape
+    assert d_query.shape == query.shape == d_out.shape and d_key.shape == d_value.shape
+    assert weights.shape == (S, H, max_seq_len)
+    _check(lib.pkv_smallseq_attention_bwd(_ptr(d_query), _ptr(d_key), _ptr(d_value), _ptr(d_out),
+                                          _ptr(query), _ptr(weights), _ptr(key_cache),
+                                          _ptr(value_cache), bstride, _ptr(block_tables),
+                                          block_tables.shape[1], _ptr(seq_lens), _ptr(cu_seq_lens),
+                                          S, d_key.shape[0], H, hkv, D, nb, bs, float(scale),
+                                          int(max_seq_len), _dtype_code(query), _stream()))
 
 
 def paged_attention_prefill_spans(out, query, cu_seqlens_q, seq_lens, key_cache, value_cache,

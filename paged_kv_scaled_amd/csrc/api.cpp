@@ -244,6 +244,53 @@ int decode_common(void* out, const void* query, const void* key_cache, const voi
   return launched(pkv::launch_decode(a, plan, (hipStream_t)stream), what);
 }
 
+// Validation shared by the small-seq forward and backward (dtype already checked).
+int smallseq_common(pkv::SmallArgs& a, const void* query, const void* key_cache,
+                    const void* value_cache, int64_t cache_block_stride,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                    int32_t block_size, float scale, int32_t max_seq_len, pkv_dtype dtype,
+                    const char* what) {
+  int rc;
+  if (dtype != PKV_BF16 && dtype != PKV_F16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: dtype %d is not PKV_BF16 or PKV_F16", what, (int)dtype);
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (max_seq_len < 1 || max_seq_len > 16)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_seq_len must be in [1, 16] (got %d)", what, max_seq_len);
+  if ((rc = check_cache(key_cache, value_cache, cache_block_stride, num_blocks, block_size,
+                        num_kv_heads, head_dim)) != PKV_OK)
+    return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads)) != PKV_OK) return rc;
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID_ARG, "scale is NaN");
+  if (num_seqs == 0) return PKV_OK;
+  if (!query || !seq_lens || !block_tables)
+    return fail(PKV_ERR_INVALID_ARG, "query, seq_lens and block_tables must not be NULL");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < max_seq_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq*block_size (%lld) < max_seq_len (%d)",
+                (long long)max_blocks_per_seq * block_size, max_seq_len);
+  if (!aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+      (cache_block_stride * 2) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "query and the caches must be 16-byte aligned and "
+                "cache_block_stride a multiple of 16 bytes");
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_stride = cache_block_stride;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_seq_len = max_seq_len;
+  a.scale = scale;
+  a.dtype = (int)dtype;
+  return guard_word(&a.guard, what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -608,6 +655,71 @@ int pkv_paged_attention_mixed(void* out, const void* query, const int32_t* cu_se
     return rc;
   if (num_gen > 0) return launched(pkv::launch_decode(gen, plan, (hipStream_t)stream), what);
   return PKV_OK;
+}
+
+int pkv_smallseq_attention_fwd(void* out, void* weights, const void* query,
+                               const void* key_cache, const void* value_cache,
+                               int64_t cache_block_stride, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                               float scale, int32_t max_seq_len, pkv_dtype dtype, void* stream) {
+  clear_error();
+  const char* what = "pkv_smallseq_attention_fwd";
+  pkv::SmallArgs a{};
+  int rc = smallseq_common(a, query, key_cache, value_cache, cache_block_stride, block_tables,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads,
+                           head_dim, num_blocks, block_size, scale, max_seq_len, dtype, what);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  if (!out || !weights)
+    return fail(PKV_ERR_INVALID_ARG, "out and weights must not be NULL");
+  if (!aligned(out, 16) || !aligned(weights, 2))
+    return fail(PKV_ERR_INVALID_ARG, "out must be 16-byte aligned and weights 2-byte aligned");
+  a.out = out;
+  a.weights = weights;
+  if (a.guard != nullptr) {
+    pkv::CheckSeqArgs c{nullptr, nullptr, 0, seq_lens, nullptr, nullptr, block_tables, num_seqs,
+                        max_blocks_per_seq, num_blocks, block_size, max_seq_len, 1, 0, 0};
+    if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream), what)) != PKV_OK) return rc;
+  }
+  return launched(pkv::launch_smallseq(a, false, (hipStream_t)stream), what);
+}
+
+int pkv_smallseq_attention_bwd(void* d_query, void* d_key, void* d_value, const void* d_out,
+                               const void* query, const void* weights, const void* key_cache,
+                               const void* value_cache, int64_t cache_block_stride,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, const int32_t* cu_seq_lens,
+                               int32_t num_seqs, int32_t total_kv, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                               int32_t block_size, float scale, int32_t max_seq_len,
+                               pkv_dtype dtype, void* stream) {
+  clear_error();
+  const char* what = "pkv_smallseq_attention_bwd";
+  pkv::SmallArgs a{};
+  int rc = smallseq_common(a, query, key_cache, value_cache, cache_block_stride, block_tables,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads,
+                           head_dim, num_blocks, block_size, scale, max_seq_len, dtype, what);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  if (total_kv < 0) return fail(PKV_ERR_INVALID_ARG, "total_kv must be >= 0 (got %d)", total_kv);
+  if (!d_query || !d_out || !weights || !cu_seq_lens || (total_kv > 0 && (!d_key || !d_value)))
+    return fail(PKV_ERR_INVALID_ARG,
+                "d_query, d_out, weights, cu_seq_lens (and d_key, d_value) must not be NULL");
+  if (!aligned(d_query, 16) || !aligned(d_out, 16) || !aligned(weights, 2) ||
+      (total_kv > 0 && (!aligned(d_key, 16) || !aligned(d_value, 16))))
+    return fail(PKV_ERR_INVALID_ARG, "gradient rows must be 16-byte aligned, weights 2-byte");
+  a.d_query = d_query;
+  a.d_key = d_key;
+  a.d_value = d_value;
+  a.d_out = d_out;
+  a.weights = const_cast<void*>(weights);
+  a.cu_seq_lens = cu_seq_lens;
+  if (a.guard != nullptr) {
+    pkv::CheckSeqArgs c{nullptr, nullptr, 0, seq_lens, cu_seq_lens, nullptr, block_tables, num_seqs,
+                        max_blocks_per_seq, num_blocks, block_size, max_seq_len, 0, 0, total_kv};
+    if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream), what)) != PKV_OK) return rc;
+  }
+  return launched(pkv::launch_smallseq(a, true, (hipStream_t)stream), what);
 }
 
 int pkv_paged_attention_prefill_spans(void* out, const void* query, const int32_t* cu_seqlens_q,

@@ -41,6 +41,8 @@ check_seqs_kernel(const CheckSeqArgs a, uint32_t* word) {
     const int64_t c0 = a.cu_seq_lens[s], c1 = a.cu_seq_lens[s + 1];
     L = c1 - c0;
     if ((s == 0 && c0 != 0) || (s == a.num_seqs - 1 && c1 != a.total_tokens)) bits |= PKV_CHECK_SEQ_LEN;
+    // both given (small-seq backward): they must agree
+    if (a.seq_lens != nullptr && a.seq_lens[s] != L) bits |= PKV_CHECK_SEQ_LEN;
   } else {
     L = a.seq_lens[s];
   }

@@ -106,6 +106,29 @@ DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
                        int block_size, int max_seq_len, bool mixed = false);
 
 hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream);
+// Small-seq training path (one query row per sequence, at most 16 keys).
+struct SmallArgs {
+  void* out;                     // forward output [S, H, D]
+  void* weights;                 // [S, H, max_seq_len] attention weights, query type
+  const void* query;             // [S, H, D]
+  const void* d_out;             // backward: [S, H, D]
+  void* d_query;                 // backward: [S, H, D]
+  void* d_key;                   // backward: [total_kv, Hkv, D], THD by cu_seq_lens
+  void* d_value;
+  const void* key_cache;
+  const void* value_cache;
+  int64_t block_stride;          // elements
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* cu_seq_lens;    // backward
+  int32_t max_blocks_per_seq, num_seqs, num_heads, num_kv_heads, head_dim, block_size;
+  int32_t max_seq_len;           // <= 16: the weights' row length
+  float scale;
+  int dtype;
+  const uint32_t* guard;
+};
+hipError_t launch_smallseq(const SmallArgs& a, bool backward, hipStream_t stream);
+
 // Quantising scatter into an FP8 (E4M3) cache: a.dtype is the source type, the cache
 // element is one byte; code = E4M3(clamp(x * inv_scale, +-448)).
 hipError_t launch_kv_scatter_fp8(const ScatterArgs& a, float k_inv_scale, float v_inv_scale,

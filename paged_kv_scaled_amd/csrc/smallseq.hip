@@ -1,0 +1,327 @@
+// Small-seq training path: attention with saved weights, and its backward.
+//
+// What is computed (ROCm TransformerEngine small-seq PR, description: varlen cross
+// attention with one query token per sequence and at most 16 keys; the forward writes the
+// attention weights, the backward reads them and computes grad_V, grad_attn, the softmax
+// backward and grad_Q / grad_K).  For sequence s, query head h, kv head j = h / g and keys
+// k < L_s (read from the paged cache through the block table):
+//   forward   P[h, k] = softmax_k(scale <q[h], K[k, j]>),   out[h] = sum_k P[h, k] V[k, j]
+//   backward  dV[k, j] = sum_{h of j} P[h, k] dO[h]                         (grad_V)
+//             dP[h, k] = <dO[h], V[k, j]>                                   (grad_attn)
+//             dS[h, k] = P[h, k] (dP[h, k] - sum_k' P[h, k'] dP[h, k'])     (softmax bwd)
+//             dQ[h]    = scale sum_k dS[h, k] K[k, j]                       (grad_Q)
+//             dK[k, j] = scale sum_{h of j} dS[h, k] q[h]                   (grad_K)
+// The backward takes P from the weights the forward saved (in the query type, as the
+// page's attention-weights buffer is), not from a recomputation.
+//
+// How (MI355X, HBM / latency bound, vector ALU): one wave owns one (sequence, kv head)
+// item.  Lanes = (key t of a round, column c): LPT lanes share a key row, each holding EPL
+// contiguous elements (one or two 16-byte loads), and TPR = 64 / LPT keys make a round;
+// with at most 16 keys an item takes one or two rounds.  K and V of the item stay in
+// registers while the wave walks the g query heads of its kv head, so dK and dV sum over
+// the group in registers and are written once.  Dot products reduce over the LPT lanes of
+// a key with xor shuffles; sums over keys reduce over the key lanes and the rounds.
+#include "common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kSmallThreads = 256;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr int kSmallMaxKv = 16;
+
+template <int D>
+struct SmallShape {
+  static constexpr int LPT = D / 8 < 8 ? D / 8 : 8;     // lanes per key row
+  static constexpr int EPL = D / LPT;                   // elements per lane (8 or 16)
+  static constexpr int TPR = kWave / LPT;               // keys per round
+  static constexpr int NR = (kSmallMaxKv + TPR - 1) / TPR;   // rounds
+  static constexpr int NV = EPL / 8;                    // 16-byte vectors per lane
+};
+
+struct SmallParams {
+  void* out;              // forward: [S, H, D]
+  void* weights;          // [S, H, max_kv], query type
+  const void* query;      // [S, H, D]
+  const void* d_out;      // backward: [S, H, D]
+  void* d_query;          // backward: [S, H, D]
+  void* d_key;            // backward: [total_kv, Hkv, D] (THD rows cu_kv[s] + k)
+  void* d_value;
+  const void* kc;
+  const void* vc;
+  int64_t block_stride;   // elements
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* cu_kv;   // backward only
+  int32_t mb, S, H, Hkv, g, block_shift, max_kv;
+  float scale;
+  const uint32_t* guard;
+};
+
+// The lane's EPL elements of a row of D storage elements starting at `row`, widened.
+template <typename T, int D>
+__device__ __forceinline__ void load_f32(const typename T::storage* base, int64_t row, int c,
+                                         float (&x)[SmallShape<D>::EPL]) {
+  using C = SmallShape<D>;
+  const u32x4_t* p = reinterpret_cast<const u32x4_t*>(base + row + c * C::EPL);
+#pragma unroll
+  for (int v = 0; v < C::NV; ++v) {
+    const u32x4_t w = p[v];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[v * 8 + 2 * i] = lo_of(T{}, w[i]);
+      x[v * 8 + 2 * i + 1] = hi_of(T{}, w[i]);
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void store_row(typename T::storage* base, int64_t row, int c,
+                                          const float (&x)[SmallShape<D>::EPL]) {
+  using C = SmallShape<D>;
+  u32x4_t* p = reinterpret_cast<u32x4_t*>(base + row + c * C::EPL);
+#pragma unroll
+  for (int v = 0; v < C::NV; ++v) {
+    u32x4_t w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack2(T{}, x[v * 8 + 2 * i], x[v * 8 + 2 * i + 1]);
+    p[v] = w;
+  }
+}
+
+// Sum over the LPT lanes of one key row (lanes t*LPT .. t*LPT+LPT-1).
+template <int LPT>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < LPT; off <<= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// Sum / max over the key lanes of a round (lanes with the same column).
+template <int LPT>
+__device__ __forceinline__ float keys_sum(float x) {
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+template <int LPT>
+__device__ __forceinline__ float keys_max(float x) {
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+// K and V rows of the item's keys (key t + r*TPR in round r), widened; keys past L re-read
+// key 0 (finite data, never used).
+template <typename T, int D>
+__device__ __forceinline__ void load_kv(const SmallParams& p, int s, int kvh, int L, int t, int c,
+                                        float (&k)[SmallShape<D>::NR][SmallShape<D>::EPL],
+                                        float (&v)[SmallShape<D>::NR][SmallShape<D>::EPL]) {
+  using C = SmallShape<D>;
+  using S = typename T::storage;
+  const int32_t* table = p.block_tables + (int64_t)s * p.mb;
+  const int bmask = (1 << p.block_shift) - 1;
+  const int64_t row_elems = (int64_t)p.Hkv * D;
+#pragma unroll
+  for (int r = 0; r < C::NR; ++r) {
+    int pos = t + r * C::TPR;
+    pos = pos < L ? pos : 0;
+    const int64_t blk = table[pos >> p.block_shift];
+    const int64_t row = blk * p.block_stride + (int64_t)(pos & bmask) * row_elems + (int64_t)kvh * D;
+    load_f32<T, D>(reinterpret_cast<const S*>(p.kc), row, c, k[r]);
+    load_f32<T, D>(reinterpret_cast<const S*>(p.vc), row, c, v[r]);
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kSmallThreads)
+smallseq_fwd_kernel(const SmallParams p) {
+  if (guard_tripped(p.guard)) return;
+  using C = SmallShape<D>;
+  using S = typename T::storage;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = lane / C::LPT, c = lane % C::LPT;
+  const int64_t item = (int64_t)blockIdx.x * kSmallWaves + threadIdx.x / kWave;
+  if (item >= (int64_t)p.S * p.Hkv) return;
+  const int s = (int)(item / p.Hkv), kvh = (int)(item % p.Hkv);
+  const int L = min(p.seq_lens[s], p.max_kv);
+  float k[C::NR][C::EPL], v[C::NR][C::EPL];
+  if (L > 0) load_kv<T, D>(p, s, kvh, L, t, c, k, v);
+  for (int hi = 0; hi < p.g; ++hi) {
+    const int h = kvh * p.g + hi;
+    const int64_t qrow = ((int64_t)s * p.H + h) * D;
+    float pr[C::NR], o[C::EPL];
+#pragma unroll
+    for (int e = 0; e < C::EPL; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int r = 0; r < C::NR; ++r) pr[r] = 0.f;
+    if (L > 0) {
+      float q[C::EPL];
+      load_f32<T, D>(reinterpret_cast<const S*>(p.query), qrow, c, q);
+      float z[C::NR];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < C::NR; ++r) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < C::EPL; ++e) d = __builtin_fmaf(q[e], k[r][e], d);
+        d = row_sum<C::LPT>(d) * p.scale;
+        z[r] = (t + r * C::TPR < L) ? d : -INFINITY;
+        mx = fmaxf(mx, z[r]);
+      }
+      mx = keys_max<C::LPT>(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < C::NR; ++r) {
+        pr[r] = (t + r * C::TPR < L) ? __expf(z[r] - mx) : 0.f;
+        sum += pr[r];
+      }
+      sum = keys_sum<C::LPT>(sum);
+      const float inv = 1.f / sum;
+#pragma unroll
+      for (int r = 0; r < C::NR; ++r) {
+        pr[r] *= inv;
+#pragma unroll
+        for (int e = 0; e < C::EPL; ++e) o[e] = __builtin_fmaf(pr[r], v[r][e], o[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < C::EPL; ++e) o[e] = keys_sum<C::LPT>(o[e]);
+    }
+    // weights: one lane per key writes P (zero past L, up to max_kv)
+    S* wrow = reinterpret_cast<S*>(p.weights) + ((int64_t)s * p.H + h) * p.max_kv;
+#pragma unroll
+    for (int r = 0; r < C::NR; ++r) {
+      const int key = t + r * C::TPR;
+      if (c == 0 && key < p.max_kv) wrow[key] = (S)(pack2(T{}, pr[r], 0.f) & 0xFFFFu);
+    }
+    if (t == 0) store_row<T, D>(reinterpret_cast<S*>(p.out), qrow, c, o);
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kSmallThreads)
+smallseq_bwd_kernel(const SmallParams p) {
+  if (guard_tripped(p.guard)) return;
+  using C = SmallShape<D>;
+  using S = typename T::storage;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = lane / C::LPT, c = lane % C::LPT;
+  const int64_t item = (int64_t)blockIdx.x * kSmallWaves + threadIdx.x / kWave;
+  if (item >= (int64_t)p.S * p.Hkv) return;
+  const int s = (int)(item / p.Hkv), kvh = (int)(item % p.Hkv);
+  const int L = min(p.seq_lens[s], p.max_kv);
+  float k[C::NR][C::EPL], v[C::NR][C::EPL], dk[C::NR][C::EPL], dv[C::NR][C::EPL];
+#pragma unroll
+  for (int r = 0; r < C::NR; ++r)
+#pragma unroll
+    for (int e = 0; e < C::EPL; ++e) dk[r][e] = dv[r][e] = 0.f;
+  if (L > 0) load_kv<T, D>(p, s, kvh, L, t, c, k, v);
+  for (int hi = 0; hi < p.g; ++hi) {
+    const int h = kvh * p.g + hi;
+    const int64_t qrow = ((int64_t)s * p.H + h) * D;
+    float dq[C::EPL];
+#pragma unroll
+    for (int e = 0; e < C::EPL; ++e) dq[e] = 0.f;
+    if (L > 0) {
+      float q[C::EPL], go[C::EPL];
+      load_f32<T, D>(reinterpret_cast<const S*>(p.query), qrow, c, q);
+      load_f32<T, D>(reinterpret_cast<const S*>(p.d_out), qrow, c, go);
+      const S* wrow = reinterpret_cast<const S*>(p.weights) + ((int64_t)s * p.H + h) * p.max_kv;
+      float pr[C::NR], dp[C::NR];
+      float dsum = 0.f;
+#pragma unroll
+      for (int r = 0; r < C::NR; ++r) {
+        const int key = t + r * C::TPR;
+        const bool in = key < L;
+        pr[r] = in ? lo_of(T{}, (uint32_t)wrow[key]) : 0.f;
+        // grad_V
+#pragma unroll
+        for (int e = 0; e < C::EPL; ++e) dv[r][e] = __builtin_fmaf(pr[r], go[e], dv[r][e]);
+        // grad_attn
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < C::EPL; ++e) d = __builtin_fmaf(go[e], v[r][e], d);
+        dp[r] = row_sum<C::LPT>(d);
+        dsum = __builtin_fmaf(pr[r], dp[r], dsum);
+      }
+      dsum = keys_sum<C::LPT>(dsum);
+#pragma unroll
+      for (int r = 0; r < C::NR; ++r) {
+        // softmax backward, then grad_K (this lane's key) and grad_Q (summed over keys)
+        const float ds = pr[r] * (dp[r] - dsum) * p.scale;
+#pragma unroll
+        for (int e = 0; e < C::EPL; ++e) {
+          dk[r][e] = __builtin_fmaf(ds, q[e], dk[r][e]);
+          dq[e] = __builtin_fmaf(ds, k[r][e], dq[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < C::EPL; ++e) dq[e] = keys_sum<C::LPT>(dq[e]);
+    }
+    if (t == 0) store_row<T, D>(reinterpret_cast<S*>(p.d_query), qrow, c, dq);
+  }
+  // dK, dV rows of the item's keys, THD at cu_kv[s] + key
+  const int64_t base = p.cu_kv[s];
+#pragma unroll
+  for (int r = 0; r < C::NR; ++r) {
+    const int key = t + r * C::TPR;
+    if (key < L) {
+      const int64_t row = ((base + key) * p.Hkv + kvh) * D;
+      store_row<T, D>(reinterpret_cast<S*>(p.d_key), row, c, dk[r]);
+      store_row<T, D>(reinterpret_cast<S*>(p.d_value), row, c, dv[r]);
+    }
+  }
+}
+
+template <typename T>
+void launch_small(const SmallParams& p, int d, bool backward, hipStream_t stream) {
+  const int64_t items = (int64_t)p.S * p.Hkv;
+  const dim3 grid((unsigned)((items + kSmallWaves - 1) / kSmallWaves)), block(kSmallThreads);
+#define PKV_SMALL(DD)                                                                        \
+  if (backward) hipLaunchKernelGGL((smallseq_bwd_kernel<T, DD>), grid, block, 0, stream, p); \
+  else hipLaunchKernelGGL((smallseq_fwd_kernel<T, DD>), grid, block, 0, stream, p)
+  switch (d) {
+    case 16: PKV_SMALL(16); break;
+    case 64: PKV_SMALL(64); break;
+    default: PKV_SMALL(128); break;
+  }
+#undef PKV_SMALL
+}
+
+}  // namespace
+
+hipError_t launch_smallseq(const SmallArgs& a, bool backward, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  if ((int64_t)a.num_seqs * a.num_kv_heads > (int64_t)0x7FFFFFFF / kSmallWaves * kSmallWaves)
+    return hipErrorInvalidValue;
+  SmallParams p{};
+  p.out = a.out;
+  p.weights = a.weights;
+  p.query = a.query;
+  p.d_out = a.d_out;
+  p.d_query = a.d_query;
+  p.d_key = a.d_key;
+  p.d_value = a.d_value;
+  p.kc = a.key_cache;
+  p.vc = a.value_cache;
+  p.block_stride = a.block_stride;
+  p.block_tables = a.block_tables;
+  p.seq_lens = a.seq_lens;
+  p.cu_kv = a.cu_seq_lens;
+  p.mb = a.max_blocks_per_seq;
+  p.S = a.num_seqs;
+  p.H = a.num_heads;
+  p.Hkv = a.num_kv_heads;
+  p.g = a.num_heads / a.num_kv_heads;
+  p.block_shift = log2_exact(a.block_size);
+  p.max_kv = a.max_seq_len;
+  p.scale = a.scale;
+  p.guard = a.guard;
+  if (a.dtype == kBF16) launch_small<BF16>(p, a.head_dim, backward, stream);
+  else launch_small<F16>(p, a.head_dim, backward, stream);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

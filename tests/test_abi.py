@@ -250,3 +250,27 @@ def test_prefill_fp8_rejections(lib):
     assert _prefill_fp8(lib, bstride=16 * 8 * 128 + 8) == B.PKV_ERR_INVALID_ARG
     assert _prefill_fp8(lib, cu=NULL) == B.PKV_ERR_INVALID_ARG
     assert _prefill_fp8(lib, T=0) == B.PKV_OK
+
+
+def test_smallseq_rejections(lib):
+    def fwd(**kw):
+        a = dict(out=FAKE, w=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bstride=16 * 16 * 128, bt=FAKE, mb=1,
+                 sl=FAKE, S=30720, H=16, Hkv=16, D=128, nb=30721, bs=16, scale=0.088, maxL=16,
+                 dt=B.PKV_BF16)
+        a.update(kw)
+        return lib.pkv_smallseq_attention_fwd(a["out"], a["w"], a["q"], a["kc"], a["vc"],
+                                              a["bstride"], a["bt"], a["mb"], a["sl"], a["S"],
+                                              a["H"], a["Hkv"], a["D"], a["nb"], a["bs"],
+                                              a["scale"], a["maxL"], a["dt"], NULL)
+    assert fwd(maxL=17) == B.PKV_ERR_INVALID_ARG
+    assert "16" in B.last_error()
+    assert fwd(maxL=0) == B.PKV_ERR_INVALID_ARG
+    assert fwd(dt=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED
+    assert fwd(D=80, bstride=16 * 16 * 80) == B.PKV_ERR_UNSUPPORTED
+    assert fwd(w=NULL) == B.PKV_ERR_INVALID_ARG
+    assert fwd(H=12, Hkv=8) == B.PKV_ERR_INVALID_ARG
+    assert fwd(S=0) == B.PKV_OK
+    r = lib.pkv_smallseq_attention_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       16 * 16 * 128, FAKE, 1, FAKE, NULL, 4, 40, 16, 16, 128,
+                                       5, 16, 0.088, 16, B.PKV_BF16, NULL)
+    assert r == B.PKV_ERR_INVALID_ARG and "cu_seq_lens" in B.last_error()
