@@ -258,6 +258,50 @@ def run_mixed_bench(w, steps, warmup):
     return res
 
 
+def smallseq_train_bytes(w, max_kv=16):
+    """Algorithmic bytes of the small-seq forward (K, V, Q in; O and the weights out) and
+    backward (K, V, Q, dO and the weights in; dQ, dK, dV out), plus lengths and tables."""
+    import numpy as np
+    eb = 2
+    kv = int(w.seq_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * eb
+    qrow = w.num_seqs * w.num_heads * w.head_dim * eb
+    wts = w.num_seqs * w.num_heads * max_kv * eb
+    meta = w.num_seqs * 4 * 2
+    return 2 * kv + 2 * qrow + wts + meta, 2 * kv + 3 * qrow + wts + 2 * kv + meta + w.num_seqs * 4
+
+
+def run_train_bench(w, steps, warmup, max_kv=16):
+    """Per-launch event timing of the small-seq forward and backward (cache written untimed)."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import Dev
+    from paged_kv_scaled_amd import binding as B
+
+    d = Dev(w, fill="zero")
+    d.write_all(split_new=False)
+    dt = d.query.dtype
+    out = torch.empty_like(d.query)
+    weights = torch.empty((w.num_seqs, w.num_heads, max_kv), dtype=dt, device="cuda")
+    d_out = torch.from_numpy(w.d_out.view(np.int16)).cuda().view(dt)
+    dq, dk, dv = torch.empty_like(d.query), torch.empty_like(d.key), torch.empty_like(d.value)
+    fwd = lambda: B.smallseq_attention_fwd(out, weights, d.query, d.kc, d.vc, d.tables, d.seq_lens,
+                                           w.scale, max_kv)
+    bwd = lambda: B.smallseq_attention_bwd(dq, dk, dv, d_out, d.query, weights, d.kc, d.vc, d.tables,
+                                           d.seq_lens, d.cu_k, w.scale, max_kv)
+    res = {}
+    for name, call in (("fwd", fwd), ("bwd", bwd)):
+        for _ in range(warmup):
+            call()
+        tm = Timer()
+        for _ in range(steps):
+            e = tm.start()
+            call()
+            tm.stop(e)
+        res[name] = tm.ms()
+    return res
+
+
 def med(xs):
     xs = sorted(xs)
     return xs[len(xs) // 2]
@@ -391,7 +435,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads",
                     default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal,mixed_spans,"
-                            "decode_batch_fp8,mixed_batch")
+                            "decode_batch_fp8,mixed_batch,smallseq_train")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibration-copy", action="store_true",
@@ -442,6 +486,22 @@ def main():
             continue
         log(f"generating {name}")
         wk = wl.CONFIGS[name]()
+        if wk.d_out is not None:
+            rt = run_train_bench(wk, args.steps, args.warmup)
+            fb, bb = smallseq_train_bytes(wk)
+            fm, bm = med(rt["fwd"]), med(rt["bwd"])
+            entry = {"metric": "small-seq training attention HBM GB/s", "unit": "GB/s",
+                     "fwd_us_median": round(fm * 1e3, 2), "bwd_us_median": round(bm * 1e3, 2),
+                     "fwd_GBps": round(fb / (fm * 1e-3) / 1e9, 1),
+                     "bwd_GBps": round(bb / (bm * 1e-3) / 1e9, 1),
+                     "fwd_frac_of_peak": round(fb / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "bwd_frac_of_peak": round(bb / (bm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "fwd_bytes": fb, "bwd_bytes": bb}
+            log(f"{name}: {entry}")
+            result_wl[name] = entry
+            del wk
+            torch.cuda.empty_cache()
+            continue
         if wk.num_ctx_seqs is not None:
             rmx = run_mixed_bench(wk, args.steps, args.warmup)
             fm, sm = med(rmx["fused"]), med(rmx["separate"])

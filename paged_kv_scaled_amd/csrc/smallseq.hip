@@ -60,20 +60,18 @@ struct SmallParams {
   const uint32_t* guard;
 };
 
-// The lane's EPL elements of a row of D storage elements starting at `row`, widened.
+// The lane's EPL elements of a row of D storage elements starting at `row`, as packed
+// pairs (word i holds elements 2i, 2i+1).
 template <typename T, int D>
-__device__ __forceinline__ void load_f32(const typename T::storage* base, int64_t row, int c,
-                                         float (&x)[SmallShape<D>::EPL]) {
+__device__ __forceinline__ void load_words(const typename T::storage* base, int64_t row, int c,
+                                           uint32_t (&x)[SmallShape<D>::EPL / 2]) {
   using C = SmallShape<D>;
   const u32x4_t* p = reinterpret_cast<const u32x4_t*>(base + row + c * C::EPL);
 #pragma unroll
   for (int v = 0; v < C::NV; ++v) {
     const u32x4_t w = p[v];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[v * 8 + 2 * i] = lo_of(T{}, w[i]);
-      x[v * 8 + 2 * i + 1] = hi_of(T{}, w[i]);
-    }
+    for (int i = 0; i < 4; ++i) x[v * 4 + i] = w[i];
   }
 }
 
@@ -89,6 +87,15 @@ __device__ __forceinline__ void store_row(typename T::storage* base, int64_t row
     for (int i = 0; i < 4; ++i) w[i] = pack2(T{}, x[v * 8 + 2 * i], x[v * 8 + 2 * i + 1]);
     p[v] = w;
   }
+}
+
+// <a, b> over the lane's elements (packed pairs, fp32 accumulate).
+template <typename T, int N>
+__device__ __forceinline__ float dot_words(const uint32_t (&a)[N], const uint32_t (&b)[N]) {
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) d = dot2(T{}, a[i], b[i], d);
+  return d;
 }
 
 // Sum over the LPT lanes of one key row (lanes t*LPT .. t*LPT+LPT-1).
@@ -113,26 +120,36 @@ __device__ __forceinline__ float keys_max(float x) {
   return x;
 }
 
-// K and V rows of the item's keys (key t + r*TPR in round r), widened; keys past L re-read
-// key 0 (finite data, never used).
+// K and V rows of the item's keys (key t + r*TPR in round r) as packed pairs.  The length
+// and the page ids load together (ids for keys past the length are read but not used:
+// the table row holds max_blocks_per_seq >= pages of max_kv entries); keys past L re-read
+// key 0.  Returns L (clamped to max_kv); nothing is loaded when it is 0.
 template <typename T, int D>
-__device__ __forceinline__ void load_kv(const SmallParams& p, int s, int kvh, int L, int t, int c,
-                                        float (&k)[SmallShape<D>::NR][SmallShape<D>::EPL],
-                                        float (&v)[SmallShape<D>::NR][SmallShape<D>::EPL]) {
+__device__ __forceinline__ int load_kv(const SmallParams& p, int s, int kvh, int t, int c,
+                                       uint32_t (&k)[SmallShape<D>::NR][SmallShape<D>::EPL / 2],
+                                       uint32_t (&v)[SmallShape<D>::NR][SmallShape<D>::EPL / 2]) {
   using C = SmallShape<D>;
   using S = typename T::storage;
   const int32_t* table = p.block_tables + (int64_t)s * p.mb;
   const int bmask = (1 << p.block_shift) - 1;
   const int64_t row_elems = (int64_t)p.Hkv * D;
+  int ids[C::NR];
+#pragma unroll
+  for (int r = 0; r < C::NR; ++r) ids[r] = table[min(t + r * C::TPR, p.max_kv - 1) >> p.block_shift];
+  const int id0 = table[0];
+  const int L = min(p.seq_lens[s], p.max_kv);
+  if (L <= 0) return 0;
 #pragma unroll
   for (int r = 0; r < C::NR; ++r) {
-    int pos = t + r * C::TPR;
-    pos = pos < L ? pos : 0;
-    const int64_t blk = table[pos >> p.block_shift];
+    const int pos_raw = t + r * C::TPR;
+    const bool in = pos_raw < L;
+    const int pos = in ? pos_raw : 0;
+    const int64_t blk = in ? ids[r] : id0;
     const int64_t row = blk * p.block_stride + (int64_t)(pos & bmask) * row_elems + (int64_t)kvh * D;
-    load_f32<T, D>(reinterpret_cast<const S*>(p.kc), row, c, k[r]);
-    load_f32<T, D>(reinterpret_cast<const S*>(p.vc), row, c, v[r]);
+    load_words<T, D>(reinterpret_cast<const S*>(p.kc), row, c, k[r]);
+    load_words<T, D>(reinterpret_cast<const S*>(p.vc), row, c, v[r]);
   }
+  return L;
 }
 
 template <typename T, int D>
@@ -141,14 +158,16 @@ smallseq_fwd_kernel(const SmallParams p) {
   if (guard_tripped(p.guard)) return;
   using C = SmallShape<D>;
   using S = typename T::storage;
+  constexpr int W = C::EPL / 2;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = lane / C::LPT, c = lane % C::LPT;
   const int64_t item = (int64_t)blockIdx.x * kSmallWaves + threadIdx.x / kWave;
   if (item >= (int64_t)p.S * p.Hkv) return;
   const int s = (int)(item / p.Hkv), kvh = (int)(item % p.Hkv);
-  const int L = min(p.seq_lens[s], p.max_kv);
-  float k[C::NR][C::EPL], v[C::NR][C::EPL];
-  if (L > 0) load_kv<T, D>(p, s, kvh, L, t, c, k, v);
+  uint32_t k[C::NR][W], v[C::NR][W], q[W];
+  // the first head's query row loads together with the length, page ids and K/V
+  load_words<T, D>(reinterpret_cast<const S*>(p.query), ((int64_t)s * p.H + kvh * p.g) * D, c, q);
+  const int L = load_kv<T, D>(p, s, kvh, t, c, k, v);
   for (int hi = 0; hi < p.g; ++hi) {
     const int h = kvh * p.g + hi;
     const int64_t qrow = ((int64_t)s * p.H + h) * D;
@@ -158,16 +177,12 @@ smallseq_fwd_kernel(const SmallParams p) {
 #pragma unroll
     for (int r = 0; r < C::NR; ++r) pr[r] = 0.f;
     if (L > 0) {
-      float q[C::EPL];
-      load_f32<T, D>(reinterpret_cast<const S*>(p.query), qrow, c, q);
+      if (hi > 0) load_words<T, D>(reinterpret_cast<const S*>(p.query), qrow, c, q);
       float z[C::NR];
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < C::NR; ++r) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < C::EPL; ++e) d = __builtin_fmaf(q[e], k[r][e], d);
-        d = row_sum<C::LPT>(d) * p.scale;
+        const float d = row_sum<C::LPT>(dot_words<T>(q, k[r])) * p.scale;
         z[r] = (t + r * C::TPR < L) ? d : -INFINITY;
         mx = fmaxf(mx, z[r]);
       }
@@ -184,7 +199,10 @@ smallseq_fwd_kernel(const SmallParams p) {
       for (int r = 0; r < C::NR; ++r) {
         pr[r] *= inv;
 #pragma unroll
-        for (int e = 0; e < C::EPL; ++e) o[e] = __builtin_fmaf(pr[r], v[r][e], o[e]);
+        for (int i = 0; i < W; ++i) {
+          o[2 * i] = __builtin_fmaf(pr[r], lo_of(T{}, v[r][i]), o[2 * i]);
+          o[2 * i + 1] = __builtin_fmaf(pr[r], hi_of(T{}, v[r][i]), o[2 * i + 1]);
+        }
       }
 #pragma unroll
       for (int e = 0; e < C::EPL; ++e) o[e] = keys_sum<C::LPT>(o[e]);
@@ -200,24 +218,35 @@ smallseq_fwd_kernel(const SmallParams p) {
   }
 }
 
-template <typename T, int D>
+// GROUP: more than one query head per kv head, so dK and dV sum over the heads in fp32
+// registers; with one head per kv head each key row is written as soon as it is known.
+template <typename T, int D, bool GROUP>
 __global__ void __launch_bounds__(kSmallThreads)
 smallseq_bwd_kernel(const SmallParams p) {
   if (guard_tripped(p.guard)) return;
   using C = SmallShape<D>;
   using S = typename T::storage;
+  constexpr int W = C::EPL / 2;
+  constexpr int NA = GROUP ? C::NR : 1;       // rounds of fp32 dK / dV accumulators
   const int lane = threadIdx.x & (kWave - 1);
   const int t = lane / C::LPT, c = lane % C::LPT;
   const int64_t item = (int64_t)blockIdx.x * kSmallWaves + threadIdx.x / kWave;
   if (item >= (int64_t)p.S * p.Hkv) return;
   const int s = (int)(item / p.Hkv), kvh = (int)(item % p.Hkv);
-  const int L = min(p.seq_lens[s], p.max_kv);
-  float k[C::NR][C::EPL], v[C::NR][C::EPL], dk[C::NR][C::EPL], dv[C::NR][C::EPL];
+  uint32_t k[C::NR][W], v[C::NR][W];
+  float dk[NA][C::EPL], dv[NA][C::EPL];
 #pragma unroll
-  for (int r = 0; r < C::NR; ++r)
+  for (int r = 0; r < NA; ++r)
 #pragma unroll
     for (int e = 0; e < C::EPL; ++e) dk[r][e] = dv[r][e] = 0.f;
-  if (L > 0) load_kv<T, D>(p, s, kvh, L, t, c, k, v);
+  // the first head's query and output-gradient rows load together with the length, page
+  // ids and K/V
+  uint32_t q[W], go[W];
+  const int64_t qrow0 = ((int64_t)s * p.H + kvh * p.g) * D;
+  load_words<T, D>(reinterpret_cast<const S*>(p.query), qrow0, c, q);
+  load_words<T, D>(reinterpret_cast<const S*>(p.d_out), qrow0, c, go);
+  const int L = load_kv<T, D>(p, s, kvh, t, c, k, v);
+  const int64_t base = p.cu_kv[s];
   for (int hi = 0; hi < p.g; ++hi) {
     const int h = kvh * p.g + hi;
     const int64_t qrow = ((int64_t)s * p.H + h) * D;
@@ -225,36 +254,45 @@ smallseq_bwd_kernel(const SmallParams p) {
 #pragma unroll
     for (int e = 0; e < C::EPL; ++e) dq[e] = 0.f;
     if (L > 0) {
-      float q[C::EPL], go[C::EPL];
-      load_f32<T, D>(reinterpret_cast<const S*>(p.query), qrow, c, q);
-      load_f32<T, D>(reinterpret_cast<const S*>(p.d_out), qrow, c, go);
+      if (hi > 0) {
+        load_words<T, D>(reinterpret_cast<const S*>(p.query), qrow, c, q);
+        load_words<T, D>(reinterpret_cast<const S*>(p.d_out), qrow, c, go);
+      }
       const S* wrow = reinterpret_cast<const S*>(p.weights) + ((int64_t)s * p.H + h) * p.max_kv;
       float pr[C::NR], dp[C::NR];
       float dsum = 0.f;
 #pragma unroll
       for (int r = 0; r < C::NR; ++r) {
         const int key = t + r * C::TPR;
-        const bool in = key < L;
-        pr[r] = in ? lo_of(T{}, (uint32_t)wrow[key]) : 0.f;
-        // grad_V
-#pragma unroll
-        for (int e = 0; e < C::EPL; ++e) dv[r][e] = __builtin_fmaf(pr[r], go[e], dv[r][e]);
-        // grad_attn
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < C::EPL; ++e) d = __builtin_fmaf(go[e], v[r][e], d);
-        dp[r] = row_sum<C::LPT>(d);
+        pr[r] = key < L ? lo_of(T{}, (uint32_t)wrow[key]) : 0.f;
+        dp[r] = row_sum<C::LPT>(dot_words<T>(go, v[r]));            // grad_attn
         dsum = __builtin_fmaf(pr[r], dp[r], dsum);
       }
       dsum = keys_sum<C::LPT>(dsum);
 #pragma unroll
       for (int r = 0; r < C::NR; ++r) {
-        // softmax backward, then grad_K (this lane's key) and grad_Q (summed over keys)
-        const float ds = pr[r] * (dp[r] - dsum) * p.scale;
+        const int key = t + r * C::TPR;
+        const float ds = pr[r] * (dp[r] - dsum) * p.scale;           // softmax bwd (scaled)
+        float rk[C::EPL], rv[C::EPL];
 #pragma unroll
-        for (int e = 0; e < C::EPL; ++e) {
-          dk[r][e] = __builtin_fmaf(ds, q[e], dk[r][e]);
-          dq[e] = __builtin_fmaf(ds, k[r][e], dq[e]);
+        for (int i = 0; i < W; ++i) {
+          dq[2 * i] = __builtin_fmaf(ds, lo_of(T{}, k[r][i]), dq[2 * i]);          // grad_Q
+          dq[2 * i + 1] = __builtin_fmaf(ds, hi_of(T{}, k[r][i]), dq[2 * i + 1]);
+          rk[2 * i] = ds * lo_of(T{}, q[i]);                                       // grad_K
+          rk[2 * i + 1] = ds * hi_of(T{}, q[i]);
+          rv[2 * i] = pr[r] * lo_of(T{}, go[i]);                                   // grad_V
+          rv[2 * i + 1] = pr[r] * hi_of(T{}, go[i]);
+        }
+        if constexpr (GROUP) {
+#pragma unroll
+          for (int e = 0; e < C::EPL; ++e) {
+            dk[r][e] += rk[e];
+            dv[r][e] += rv[e];
+          }
+        } else if (key < L) {
+          const int64_t row = ((base + key) * p.Hkv + kvh) * D;
+          store_row<T, D>(reinterpret_cast<S*>(p.d_key), row, c, rk);
+          store_row<T, D>(reinterpret_cast<S*>(p.d_value), row, c, rv);
         }
       }
 #pragma unroll
@@ -262,15 +300,16 @@ smallseq_bwd_kernel(const SmallParams p) {
     }
     if (t == 0) store_row<T, D>(reinterpret_cast<S*>(p.d_query), qrow, c, dq);
   }
-  // dK, dV rows of the item's keys, THD at cu_kv[s] + key
-  const int64_t base = p.cu_kv[s];
+  if constexpr (GROUP) {
+    // dK, dV rows of the item's keys, THD at cu_kv[s] + key
 #pragma unroll
-  for (int r = 0; r < C::NR; ++r) {
-    const int key = t + r * C::TPR;
-    if (key < L) {
-      const int64_t row = ((base + key) * p.Hkv + kvh) * D;
-      store_row<T, D>(reinterpret_cast<S*>(p.d_key), row, c, dk[r]);
-      store_row<T, D>(reinterpret_cast<S*>(p.d_value), row, c, dv[r]);
+    for (int r = 0; r < C::NR; ++r) {
+      const int key = t + r * C::TPR;
+      if (key < L) {
+        const int64_t row = ((base + key) * p.Hkv + kvh) * D;
+        store_row<T, D>(reinterpret_cast<S*>(p.d_key), row, c, dk[r]);
+        store_row<T, D>(reinterpret_cast<S*>(p.d_value), row, c, dv[r]);
+      }
     }
   }
 }
@@ -280,8 +319,9 @@ void launch_small(const SmallParams& p, int d, bool backward, hipStream_t stream
   const int64_t items = (int64_t)p.S * p.Hkv;
   const dim3 grid((unsigned)((items + kSmallWaves - 1) / kSmallWaves)), block(kSmallThreads);
 #define PKV_SMALL(DD)                                                                        \
-  if (backward) hipLaunchKernelGGL((smallseq_bwd_kernel<T, DD>), grid, block, 0, stream, p); \
-  else hipLaunchKernelGGL((smallseq_fwd_kernel<T, DD>), grid, block, 0, stream, p)
+  if (!backward) hipLaunchKernelGGL((smallseq_fwd_kernel<T, DD>), grid, block, 0, stream, p); \
+  else if (p.g > 1) hipLaunchKernelGGL((smallseq_bwd_kernel<T, DD, true>), grid, block, 0, stream, p); \
+  else hipLaunchKernelGGL((smallseq_bwd_kernel<T, DD, false>), grid, block, 0, stream, p)
   switch (d) {
     case 16: PKV_SMALL(16); break;
     case 64: PKV_SMALL(64); break;
