@@ -176,3 +176,69 @@ def test_checks_flag_unsorted_spans(checks):
     bits, msg = B.check_device_error()
     assert bits == B.PKV_CHECK_SPANS
     assert torch.all(out == 8.0)
+
+
+def test_checks_cover_fp8_write(checks):
+    """The quantising scatter takes the same slot check; nothing is written when it fails."""
+    w = wl.with_fp8_cache(wl.random_small(4, "bf16", head_dim=64))
+    d = Dev(w)
+    slots = d.slots.clone()
+    slots[0] = w.num_blocks * w.block_size
+    B.kv_cache_write_fp8(d.key, d.value, slots, d.kc, d.vc, w.k_scale, w.v_scale)
+    bits, _ = B.check_device_error()
+    assert bits == B.PKV_CHECK_SLOT_RANGE
+    torch.cuda.synchronize()
+    assert bool(torch.all(d.kc == 0x7F)) and bool(torch.all(d.vc == 0x7F))
+
+
+def test_checks_cover_mixed_batch(checks):
+    """A generation sequence's block id one past the pool (two slack blocks behind it), then
+    a context segment longer than its sequence: each flagged, the output untouched."""
+    w = wl.mixed_batch(seed=56, num_ctx=2, num_gen=5, ctx_hi=200, q_lo=20, q_hi=80, lo=100, hi=600)
+    d = Dev(w)
+    d.write_all()
+    shape = (w.num_blocks + 2, w.block_size, w.num_kv_heads, w.head_dim)
+    kbig = torch.zeros(shape, dtype=d.kc.dtype, device="cuda")
+    vbig = torch.zeros(shape, dtype=d.vc.dtype, device="cuda")
+    kbig[:w.num_blocks] = d.kc
+    vbig[:w.num_blocks] = d.vc
+    d.kc, d.vc = kbig[:w.num_blocks], vbig[:w.num_blocks]
+    d.tables[4, 0] = w.num_blocks
+    out = torch.full_like(d.query, 6.0)
+    d.mixed(out)
+    bits, msg = B.check_device_error()
+    assert bits == B.PKV_CHECK_TABLE and "block_tables" in msg
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 6.0))
+    d.tables[4, 0] = int(w.block_tables[4, 0])
+    d.seq_lens[0] = int(w.q_lens[0]) - 1          # fewer keys than the chunk's rows
+    d.mixed(out)
+    bits, msg = B.check_device_error()
+    assert bits & B.PKV_CHECK_CU_Q
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 6.0))
+
+
+def test_checks_cover_smallseq_backward(checks):
+    """cu_seq_lens that disagree with seq_lens (dK / dV carry 32 slack rows): flagged, and
+    the gradients stay untouched."""
+    w = wl.smallseq_train(seed=57, num_seqs=20)
+    d = Dev(w)
+    d.write_all(split_new=False)
+    dt = d.query.dtype
+    weights = torch.zeros((20, 16, 16), dtype=dt, device="cuda")
+    B.smallseq_attention_fwd(torch.empty_like(d.query), weights, d.query, d.kc, d.vc, d.tables,
+                             d.seq_lens, w.scale, 16)
+    assert B.check_device_error() == (0, "")
+    cu = d.cu_k.clone()
+    cu[5] += 1
+    d_out = torch.from_numpy(w.d_out.view(np.int16)).cuda().view(dt)
+    dq = torch.full_like(d.query, 8.0)
+    dk = torch.full((w.key.shape[0] + 32,) + tuple(d.key.shape[1:]), 8.0, dtype=dt, device="cuda")
+    dv = torch.full_like(dk, 8.0)
+    B.smallseq_attention_bwd(dq, dk[:w.key.shape[0]], dv[:w.key.shape[0]], d_out, d.query, weights,
+                             d.kc, d.vc, d.tables, d.seq_lens, cu, w.scale, 16)
+    bits, msg = B.check_device_error()
+    assert bits == B.PKV_CHECK_SEQ_LEN
+    torch.cuda.synchronize()
+    assert bool(torch.all(dq == 8.0)) and bool(torch.all(dk == 8.0)) and bool(torch.all(dv == 8.0))
