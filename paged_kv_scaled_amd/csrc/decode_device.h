@@ -99,6 +99,8 @@ struct DecodeParams {
   float scale_log2;         // scale * log2(e) (times k_scale for an FP8 cache)
   float out_scale;          // v_scale for an FP8 cache, else 1
   const uint32_t* guard;    // device error word when device checks are on, else null
+  void* weights;            // small-seq training forward: [S, H, max_kv] attention weights
+  int32_t max_kv;
 };
 
 template <typename T, int D>
@@ -214,15 +216,13 @@ __device__ __forceinline__ float reduce_token(float x) {
   return x;
 }
 
+// Scores of the two keys of a step for every head, in log2 units (-inf past the end).
 template <typename T, int D, int HPW>
-__device__ __forceinline__ void compute_step(const Step<T, D>& st,
-                                             const uint32_t (&q)[HPW][DecodeShape<T, D>::WPL],
-                                             float (&m)[HPW], float (&l)[HPW],
-                                             float (&acc)[HPW][DecodeShape<T, D>::EPL],
-                                             float scale_log2) {
+__device__ __forceinline__ void score_step(const Step<T, D>& st,
+                                           const uint32_t (&q)[HPW][DecodeShape<T, D>::WPL],
+                                           float scale_log2, float (&sc)[2][HPW]) {
   using C = DecodeShape<T, D>;
   constexpr bool kHalf = T::bytes == 2;
-  float sc[2][HPW];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
 #pragma unroll
@@ -240,6 +240,15 @@ __device__ __forceinline__ void compute_step(const Step<T, D>& st,
       sc[r][hh] = st.valid[r] ? d * scale_log2 : -INFINITY;
     }
   }
+}
+
+// Online-softmax update of (m, l, acc) with a step's scores and V rows.
+template <typename T, int D, int HPW>
+__device__ __forceinline__ void update_step(const Step<T, D>& st, const float (&sc)[2][HPW],
+                                            float (&m)[HPW], float (&l)[HPW],
+                                            float (&acc)[HPW][DecodeShape<T, D>::EPL]) {
+  using C = DecodeShape<T, D>;
+  constexpr bool kHalf = T::bytes == 2;
   // lazy max update: rescale only when a score exceeds the running max by > 2^8
   bool grow = false;
 #pragma unroll
@@ -303,6 +312,17 @@ __device__ __forceinline__ void compute_step(const Step<T, D>& st,
       }
     }
   }
+}
+
+template <typename T, int D, int HPW>
+__device__ __forceinline__ void compute_step(const Step<T, D>& st,
+                                             const uint32_t (&q)[HPW][DecodeShape<T, D>::WPL],
+                                             float (&m)[HPW], float (&l)[HPW],
+                                             float (&acc)[HPW][DecodeShape<T, D>::EPL],
+                                             float scale_log2) {
+  float sc[2][HPW];
+  score_step<T, D, HPW>(st, q, scale_log2, sc);
+  update_step<T, D, HPW>(st, sc, m, l, acc);
 }
 
 // Attention state of one wave over keys [lo, hi) of sequence s for the query heads
@@ -566,6 +586,100 @@ decode_items_kernel(const DecodeParams p) {
     for (int k = 0; k < NSTEP; ++k) compute_step<T, D, HPW>(st[k], q, m, l, acc, p.scale_log2);
   }
   if (live) write_output<T, D, HPW>(p, s, h0, nh, c, l, acc);
+}
+
+// Item mode that also writes the attention weights (the small-seq training forward, at
+// most kWeightKeys keys): the scores of the item's keys stay in registers (log2 units),
+// and once the final max and sum are known every lane of the group writes the weights of
+// keys c and c + 8, P = 2^(z - m) / l, zero past the length.
+constexpr int kWeightKeys = 16;
+
+template <typename T, int D, int HPW>
+__global__ void __launch_bounds__(kDecodeThreads)
+decode_items_weights_kernel(const DecodeParams p) {
+  if (guard_tripped(p.guard)) return;
+  using C = DecodeShape<T, D>;
+  using S = typename T::storage;
+  static_assert(C::LPT == 8 && C::TPR == 8, "item mode needs 8 lanes per row");
+  constexpr int NSTEP = 2;
+  constexpr int ITER = kWeightKeys / (2 * NSTEP);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = lane / C::LPT, c = lane % C::LPT;
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+  if (wave * C::TPR >= p.total_items) return;            // uniform over the wave
+  const int64_t item_raw = wave * C::TPR + t;
+  const bool live = item_raw < p.total_items;
+  const int64_t item = live ? item_raw : p.total_items - 1;
+  const int HG = p.Hkv * p.groups_per_kv;
+  const int hg = (int)(item % HG);
+  const int s = (int)(item / HG);
+  const int L = min(p.seq_lens[s], p.max_kv);
+  const int kvh = hg / p.groups_per_kv, sub = hg % p.groups_per_kv;
+  const int h0 = kvh * p.g + sub * HPW;
+  const int nh = min(HPW, p.g - sub * HPW);
+  const int last_page = L > 0 ? (L - 1) >> p.block_shift : -1;
+  const int32_t pid = c <= last_page ? p.block_tables[(int64_t)s * p.mb + c] : 0;
+  uint32_t q[HPW][C::WPL];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const S*>(p.query) + ((int64_t)s * p.H + h0 + (hh < nh ? hh : 0)) * D);
+#pragma unroll
+    for (int v = 0; v < C::VPL; ++v) {
+      const u32x4_t qq = qp[C::vec(v, c)];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) q[hh][v * 4 + w] = qq[w];
+    }
+  }
+  float m[HPW], l[HPW], acc[HPW][C::EPL];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::EPL; ++e) acc[hh][e] = 0.f;
+  }
+  int Lw = L;
+#pragma unroll
+  for (int off = C::LPT; off < kWave; off <<= 1) Lw = max(Lw, __shfl_xor(Lw, off, kWave));
+  const int64_t head_off = (int64_t)kvh * D;
+  float z[ITER * NSTEP][2][HPW];                           // key 2*i + r at z[i][r]
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) z[it * NSTEP + k][r][hh] = -INFINITY;
+    const int base = it * 2 * NSTEP;
+    if (base < Lw) {                                       // uniform over the wave
+      Step<T, D> st[NSTEP];
+#pragma unroll
+      for (int k = 0; k < NSTEP; ++k) load_item_step<T, D>(st[k], p, pid, head_off, base + 2 * k, L, t, c);
+#pragma unroll
+      for (int k = 0; k < NSTEP; ++k) {
+        score_step<T, D, HPW>(st[k], q, p.scale_log2, z[it * NSTEP + k]);
+        update_step<T, D, HPW>(st[k], z[it * NSTEP + k], m, l, acc);
+      }
+    }
+  }
+  if (!live) return;
+  write_output<T, D, HPW>(p, s, h0, nh, c, l, acc);
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    if (hh >= nh) continue;
+    S* wrow = reinterpret_cast<S*>(p.weights) + ((int64_t)s * p.H + h0 + hh) * p.max_kv;
+    const float inv = L > 0 ? 1.f / l[hh] : 0.f;
+    const float mh = L > 0 ? m[hh] : 0.f;
+#pragma unroll
+    for (int key = 0; key < kWeightKeys; ++key) {
+      if ((key & (C::LPT - 1)) != c || key >= p.max_kv) continue;
+      const float zk = z[key >> 1][key & 1][hh];
+      const float pk = key < L ? fast_exp2(zk - mh) * inv : 0.f;
+      wrow[key] = (S)(pack2(T{}, pk, 0.f) & 0xFFFFu);
+    }
+  }
 }
 
 // ---- stream mode -----------------------------------------------------------------------

@@ -21,8 +21,7 @@
 // registers while the wave walks the g query heads of its kv head, so dK and dV sum over
 // the group in registers and are written once.  Dot products reduce over the LPT lanes of
 // a key with xor shuffles; sums over keys reduce over the key lanes and the rounds.
-#include "common.h"
-#include "kernels.h"
+#include "decode_device.h"
 
 namespace pkv {
 
@@ -314,8 +313,51 @@ smallseq_bwd_kernel(const SmallParams p) {
   }
 }
 
+// The forward with one or two query heads per kv head and head_dim 64 / 128 runs as the
+// decode item mode with weights (eight items per wave, so that their dependent loads
+// overlap); other shapes take smallseq_fwd_kernel.
+template <typename T>
+bool launch_fwd_items(const SmallParams& sp, int d, hipStream_t stream) {
+  if (!(d == 128 || d == 64) || sp.g > 2) return false;
+  DecodeParams p{};
+  p.out = sp.out;
+  p.query = sp.query;
+  p.kc = sp.kc;
+  p.vc = sp.vc;
+  p.block_stride = sp.block_stride;
+  p.block_tables = sp.block_tables;
+  p.seq_lens = sp.seq_lens;
+  p.mb = sp.mb;
+  p.S = sp.S;
+  p.H = sp.H;
+  p.Hkv = sp.Hkv;
+  p.g = sp.g;
+  p.block_shift = sp.block_shift;
+  p.groups_per_kv = 1;
+  p.nsplit = 1;
+  p.split_len = sp.max_kv;
+  p.total_items = (int64_t)sp.S * sp.Hkv;
+  p.scale_log2 = sp.scale * kLog2e;
+  p.out_scale = 1.f;
+  p.guard = sp.guard;
+  p.weights = sp.weights;
+  p.max_kv = sp.max_kv;
+  const int64_t waves = (p.total_items + 7) / 8;
+  const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)), block(kDecodeThreads);
+#define PKV_ITEMS(DD, HH) \
+  hipLaunchKernelGGL((decode_items_weights_kernel<T, DD, HH>), grid, block, 0, stream, p)
+  if (d == 128) {
+    if (sp.g == 1) PKV_ITEMS(128, 1); else PKV_ITEMS(128, 2);
+  } else {
+    if (sp.g == 1) PKV_ITEMS(64, 1); else PKV_ITEMS(64, 2);
+  }
+#undef PKV_ITEMS
+  return true;
+}
+
 template <typename T>
 void launch_small(const SmallParams& p, int d, bool backward, hipStream_t stream) {
+  if (!backward && launch_fwd_items<T>(p, d, stream)) return;
   const int64_t items = (int64_t)p.S * p.Hkv;
   const dim3 grid((unsigned)((items + kSmallWaves - 1) / kSmallWaves)), block(kSmallThreads);
 #define PKV_SMALL(DD)                                                                        \

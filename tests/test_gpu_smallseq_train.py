@@ -81,7 +81,7 @@ def test_smallseq_train_dtypes_and_head_dims(gpu, dtype, D):
     _run(wl.smallseq_train(seed=20 + D, num_seqs=300, dtype=dtype, head_dim=D))
 
 
-@pytest.mark.parametrize("H,Hkv", [(8, 2), (12, 3), (4, 1)])
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (12, 3), (4, 1), (8, 4), (6, 3)])
 def test_smallseq_train_gqa(gpu, H, Hkv):
     """Grouped heads: dK and dV sum over the heads of a kv head."""
     _run(wl.smallseq_train(seed=30 + H, num_seqs=200, num_heads=H, num_kv_heads=Hkv,
