@@ -88,6 +88,21 @@ __device__ __forceinline__ void store_row(typename T::storage* base, int64_t row
   }
 }
 
+// Store of the lane's D/8 contiguous elements (8 lanes per row).
+template <typename T, int D>
+__device__ __forceinline__ void store_row_c(typename T::storage* base, int64_t row, int c,
+                                            const float (&x)[D / 8]) {
+  constexpr int EPL = D / 8;
+  u32x4_t* p = reinterpret_cast<u32x4_t*>(base + row + c * EPL);
+#pragma unroll
+  for (int v = 0; v < EPL / 8; ++v) {
+    u32x4_t w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack2(T{}, x[v * 8 + 2 * i], x[v * 8 + 2 * i + 1]);
+    p[v] = w;
+  }
+}
+
 // <a, b> over the lane's elements (packed pairs, fp32 accumulate).
 template <typename T, int N>
 __device__ __forceinline__ float dot_words(const uint32_t (&a)[N], const uint32_t (&b)[N]) {
@@ -313,6 +328,145 @@ smallseq_bwd_kernel(const SmallParams p) {
   }
 }
 
+// Backward with one query head per kv head, eight items per wave (as decode item mode):
+// each group of 8 lanes owns one (sequence, head) item and walks its keys itself, so the
+// dependent loads of eight items overlap.  Lane c holds elements c*EPL .. c*EPL+EPL-1 of
+// every row and page c of the item.  Pass 1 reads the V rows (grad_attn, then the
+// softmax-backward mean); pass 2 reads the K rows, accumulates grad_Q in the lane and
+// writes the grad_K and grad_V rows of each key.
+template <typename T, int D>
+__global__ void __launch_bounds__(kSmallThreads)
+smallseq_bwd_items_kernel(const SmallParams p) {
+  if (guard_tripped(p.guard)) return;
+  using S = typename T::storage;
+  constexpr int LPT = 8;
+  constexpr int EPL = D / LPT;
+  constexpr int W = EPL / 2;
+  constexpr int NV = EPL / 8;
+  constexpr int KB = 4;                                   // keys whose loads go together
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = lane / LPT, c = lane % LPT;
+  const int64_t wave = (int64_t)blockIdx.x * kSmallWaves + threadIdx.x / kWave;
+  const int64_t items = (int64_t)p.S * p.Hkv;
+  if (wave * 8 >= items) return;                          // uniform over the wave
+  const int64_t item_raw = wave * 8 + t;
+  const bool live = item_raw < items;
+  const int64_t item = live ? item_raw : items - 1;
+  const int s = (int)(item / p.Hkv), kvh = (int)(item % p.Hkv);
+  const int L = min(p.seq_lens[s], p.max_kv);
+  const int last_page = L > 0 ? (L - 1) >> p.block_shift : -1;
+  const int32_t pid = c <= last_page ? p.block_tables[(int64_t)s * p.mb + c] : 0;
+  const int64_t qrow = ((int64_t)s * p.H + kvh) * D;       // g == 1: head = kv head
+  uint32_t q[W], go[W];
+  {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const S*>(p.query) + qrow + c * EPL);
+    const u32x4_t* gp = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const S*>(p.d_out) + qrow + c * EPL);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const u32x4_t a = qp[v], b = gp[v];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        q[v * 4 + i] = a[i];
+        go[v * 4 + i] = b[i];
+      }
+    }
+  }
+  // the item's weights (every lane of the group reads the same row); keys past L re-read
+  // entry min(k, L-1), inside the row, and count as 0
+  float pr[kSmallMaxKv];
+  {
+    const S* wrow = reinterpret_cast<const S*>(p.weights) + ((int64_t)s * p.H + kvh) * p.max_kv;
+#pragma unroll
+    for (int k = 0; k < kSmallMaxKv; ++k) {
+      const uint32_t w = wrow[min(k, max(L - 1, 0))];
+      pr[k] = k < L ? lo_of(T{}, w) : 0.f;
+    }
+  }
+  int Lw = L;
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) Lw = max(Lw, __shfl_xor(Lw, off, kWave));
+  const int bmask = (1 << p.block_shift) - 1;
+  const int64_t row_elems = (int64_t)p.Hkv * D;
+  auto row_of = [&](int k) -> int64_t {                    // cache row of key k (a real key)
+    const int pos = min(k, max(L - 1, 0));
+    const int64_t blk = __shfl(pid, t * LPT + (pos >> p.block_shift), kWave);
+    return blk * p.block_stride + (int64_t)(pos & bmask) * row_elems + (int64_t)kvh * D + c * EPL;
+  };
+  // pass 1: dP = <dO, V[k]> and the mean sum_k P dP
+  float dp[kSmallMaxKv];
+  float dsum = 0.f;
+#pragma unroll
+  for (int k0 = 0; k0 < kSmallMaxKv; k0 += KB) {
+#pragma unroll
+    for (int k = k0; k < k0 + KB; ++k) dp[k] = 0.f;
+    if (k0 < Lw) {
+      uint32_t vr[KB][W];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const S*>(p.vc) + row_of(k0 + kk));
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const u32x4_t a = vp[v];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vr[kk][v * 4 + i] = a[i];
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < W; ++i) d = dot2(T{}, go[i], vr[kk][i], d);
+#pragma unroll
+        for (int off = 1; off < LPT; off <<= 1) d += __shfl_xor(d, off, kWave);
+        dp[k0 + kk] = d;
+        dsum = __builtin_fmaf(pr[k0 + kk], d, dsum);
+      }
+    }
+  }
+  // pass 2: dS, grad_Q (in the lane), grad_K and grad_V rows
+  float dq[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dq[e] = 0.f;
+  const int64_t base = p.cu_kv[s];
+#pragma unroll
+  for (int k0 = 0; k0 < kSmallMaxKv; k0 += KB) {
+    if (k0 < Lw) {
+      uint32_t kr[KB][W];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const S*>(p.kc) + row_of(k0 + kk));
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const u32x4_t a = kp[v];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kr[kk][v * 4 + i] = a[i];
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int k = k0 + kk;
+        const float ds = pr[k] * (dp[k] - dsum) * p.scale;
+        float rk[EPL], rv[EPL];
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+          dq[2 * i] = __builtin_fmaf(ds, lo_of(T{}, kr[kk][i]), dq[2 * i]);
+          dq[2 * i + 1] = __builtin_fmaf(ds, hi_of(T{}, kr[kk][i]), dq[2 * i + 1]);
+          rk[2 * i] = ds * lo_of(T{}, q[i]);
+          rk[2 * i + 1] = ds * hi_of(T{}, q[i]);
+          rv[2 * i] = pr[k] * lo_of(T{}, go[i]);
+          rv[2 * i + 1] = pr[k] * hi_of(T{}, go[i]);
+        }
+        if (live && k < L) {
+          const int64_t row = ((base + k) * p.Hkv + kvh) * D;
+          store_row_c<T, D>(reinterpret_cast<S*>(p.d_key), row, c, rk);
+          store_row_c<T, D>(reinterpret_cast<S*>(p.d_value), row, c, rv);
+        }
+      }
+    }
+  }
+  if (live) store_row_c<T, D>(reinterpret_cast<S*>(p.d_query), qrow, c, dq);
+}
+
 // The forward with one or two query heads per kv head and head_dim 64 / 128 runs as the
 // decode item mode with weights (eight items per wave, so that their dependent loads
 // overlap); other shapes take smallseq_fwd_kernel.
@@ -358,6 +512,13 @@ bool launch_fwd_items(const SmallParams& sp, int d, hipStream_t stream) {
 template <typename T>
 void launch_small(const SmallParams& p, int d, bool backward, hipStream_t stream) {
   if (!backward && launch_fwd_items<T>(p, d, stream)) return;
+  if (backward && p.g == 1 && (d == 128 || d == 64)) {
+    const int64_t waves = ((int64_t)p.S * p.Hkv + 7) / 8;
+    const dim3 grid((unsigned)((waves + kSmallWaves - 1) / kSmallWaves)), block(kSmallThreads);
+    if (d == 128) hipLaunchKernelGGL((smallseq_bwd_items_kernel<T, 128>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((smallseq_bwd_items_kernel<T, 64>), grid, block, 0, stream, p);
+    return;
+  }
   const int64_t items = (int64_t)p.S * p.Hkv;
   const dim3 grid((unsigned)((items + kSmallWaves - 1) / kSmallWaves)), block(kSmallThreads);
 #define PKV_SMALL(DD)                                                                        \
