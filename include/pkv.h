@@ -409,6 +409,12 @@ int pkv_set_device_checks(int enable);
  * HIP runtime fails.  This call synchronises: it is for tests and debugging. */
 int pkv_check_device_error(void* stream, uint32_t* bits);
 
+/* Launch log: with it on, every kernel launch prints one line to stderr naming the
+ * kernel, its grid and block and the variant chosen (decode mode, heads per wave,
+ * prefill tiling, ...).  Initially on when PKV_LOG is set to a value other than 0 in the
+ * environment; pkv_set_log(enable) switches it for every later call.  Returns PKV_OK. */
+int pkv_set_log(int enable);
+
 /* Message of the last failed call on this thread ("" if none).  Valid until the
  * next pkv_* call on the same thread. */
 const char* pkv_last_error(void);

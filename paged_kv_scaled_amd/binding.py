@@ -59,6 +59,7 @@ SIGNATURES = {
                                                          _F, _P, _P, _I32, _I32, _I32,
                                                          ctypes.c_int, _P]),
     "pkv_set_device_checks": (ctypes.c_int, [ctypes.c_int]),
+    "pkv_set_log": (ctypes.c_int, [ctypes.c_int]),
     "pkv_check_device_error": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32)]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_int, []),
@@ -317,6 +318,11 @@ def paged_attention_prefill_spans(out, query, cu_seqlens_q, seq_lens, key_cache,
                                                  _ptr(full_spans if n else None),
                                                  _ptr(cu_spans if n else None), n, int(max_q_len),
                                                  int(max_seq_len), _dtype_code(query), _stream()))
+
+
+def set_log(enable: bool):
+    """Print one line per kernel launch to stderr (kernel, grid, block, variant)."""
+    _check(load().pkv_set_log(1 if enable else 0))
 
 
 def set_device_checks(enable: bool):

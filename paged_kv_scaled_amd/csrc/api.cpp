@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/pkv.h"
@@ -293,11 +294,45 @@ int smallseq_common(pkv::SmallArgs& a, const void* query, const void* key_cache,
 
 }  // namespace
 
+namespace pkv {
+
+// -1: not read yet; then 0 / 1 (PKV_LOG in the environment, or pkv_set_log)
+static std::atomic<int> g_log{-1};
+
+bool log_enabled() {
+  int v = g_log.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = getenv("PKV_LOG");
+    const int on = (e != nullptr && e[0] != '\0' && e[0] != '0') ? 1 : 0;
+    int expected = -1;
+    g_log.compare_exchange_strong(expected, on, std::memory_order_relaxed);
+    v = g_log.load(std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
+void log_launch(const char* kernel, long long grid, int block, const char* fmt, ...) {
+  char detail[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(detail, sizeof(detail), fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "pkv: %s grid=%lld block=%d %s\n", kernel, grid, block, detail);
+}
+
+}  // namespace pkv
+
 extern "C" {
 
 int pkv_version(void) { return (1 << 16) | 0; }
 
 const char* pkv_last_error(void) { return g_err; }
+
+int pkv_set_log(int enable) {
+  clear_error();
+  pkv::g_log.store(enable != 0 ? 1 : 0, std::memory_order_relaxed);
+  return PKV_OK;
+}
 
 int pkv_set_device_checks(int enable) {
   clear_error();

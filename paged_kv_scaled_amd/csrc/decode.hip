@@ -21,6 +21,9 @@ void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t strea
   constexpr int NS = DecodeSteps<T, D, HPW>::value;
   if (pl.stream) {
     const int blocks = (int)((dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock);
+    PKV_LOG_LAUNCH("decode_stream_kernel", blocks, kDecodeThreads,
+                   "D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld", D, HPW, NS, dp.nranges,
+                   (long long)dp.total_items);
     hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, NS>), dim3(blocks), dim3(kDecodeThreads),
                        0, stream, dp);
     return;
@@ -29,6 +32,9 @@ void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t strea
     if (pl.num_splits == 1 && pl.max_seq_len <= kItemPages << dp.block_shift) {
       const int64_t waves = (dp.total_items + C::TPR - 1) / C::TPR;
       const int blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+      PKV_LOG_LAUNCH("decode_items_kernel", blocks, kDecodeThreads,
+                     "D=%d heads_per_wave=%d items=%lld (8 per wave)", D, HPW,
+                     (long long)dp.total_items);
       hipLaunchKernelGGL((decode_items_kernel<T, D, HPW, kItemSteps>), dim3(blocks),
                          dim3(kDecodeThreads), 0, stream, dp);
       return;
@@ -36,6 +42,9 @@ void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t strea
   }
   const int64_t wanted = (dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock;
   const int blocks = (int)(wanted < 8192 ? wanted : 8192);
+  PKV_LOG_LAUNCH("decode_split_kernel", blocks, kDecodeThreads,
+                 "D=%d heads_per_wave=%d split_len=%d splits=%d items=%lld", D, HPW, dp.split_len,
+                 dp.nsplit, (long long)dp.total_items);
   if (pl.max_seq_len <= C::STEP)
     hipLaunchKernelGGL((decode_split_kernel<T, D, HPW, 1>), dim3(blocks), dim3(kDecodeThreads),
                        0, stream, dp);
@@ -57,6 +66,8 @@ void launch_hpw(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream
 template <typename T, int D>
 void launch_merge(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream) {
   const int blocks = (int)(((int64_t)dp.S * dp.H + kWavesPerBlock - 1) / kWavesPerBlock);
+  PKV_LOG_LAUNCH(pl.stream ? "decode_merge_stream_kernel" : "decode_merge_split_kernel", blocks,
+                 kDecodeThreads, "rows=%lld", (long long)dp.S * dp.H);
   if (pl.stream)
     hipLaunchKernelGGL((decode_merge_stream_kernel<T, D>), dim3(blocks), dim3(kDecodeThreads), 0,
                        stream, dp);

@@ -106,6 +106,13 @@ DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
                        int block_size, int max_seq_len, bool mixed = false);
 
 hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream);
+// Launch log: with PKV_LOG=1 in the environment (read once), every kernel launch prints
+// one line to stderr -- the kernel, its grid and block, and the variant chosen.
+bool log_enabled();
+void log_launch(const char* kernel, long long grid, int block, const char* fmt, ...);
+#define PKV_LOG_LAUNCH(...) \
+  do { if (::pkv::log_enabled()) ::pkv::log_launch(__VA_ARGS__); } while (0)
+
 // Small-seq training path (one query row per sequence, at most 16 keys).
 struct SmallArgs {
   void* out;                     // forward output [S, H, D]

@@ -113,6 +113,10 @@ hipError_t launch_mixed(const AttnArgs& ctx, const AttnArgs& gen, const DecodePl
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int hpw = pl.heads_per_wave;
+  PKV_LOG_LAUNCH("mixed_kernel", blocks, kWaves * 64,
+                 "prefill_blocks=%lld decode_blocks=%lld decode=%s items=%lld heads_per_wave=%d",
+                 (long long)pblocks, (long long)dblocks, pl.stream ? "stream" : "split",
+                 (long long)mp.dc.total_items, hpw);
   if (ctx.dtype == kBF16) {
     if (ctx.head_dim == 128) launch_mixed_d<BF16, 128>(mp, hpw, (unsigned)blocks, stream);
     else launch_mixed_d<BF16, 64>(mp, hpw, (unsigned)blocks, stream);

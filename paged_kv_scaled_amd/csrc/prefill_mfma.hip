@@ -16,6 +16,9 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
   int64_t nb = 0;
   if (!prefill_params(a, p, nb)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nb), block(kWaves * 64);
+  PKV_LOG_LAUNCH("prefill_mfma_kernel", nb, kWaves * 64,
+                 "D=%d heads_per_wg=%d rows_per_wg=%d groups=%d qtiles=%d mask=%d fp8=%d",
+                 a.head_dim, p.hw, 32 << p.rb_log2, p.ngroups, p.qtiles, p.mask, a.kv_fp8);
 #define PKV_PREFILL(TT)                                                                        \
   if (a.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_kernel<TT, 128>), grid, block, 0, stream, p); \
   else hipLaunchKernelGGL((prefill_mfma_kernel<TT, 64>), grid, block, 0, stream, p)

@@ -150,6 +150,8 @@ void launch_valu_t(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.num_tokens * a.num_heads;
   const int blocks = (int)((items + kValuWaves - 1) / kValuWaves);
   const float sl2 = a.scale * (a.kv_fp8 ? a.k_scale : 1.f) * kLog2e;
+  PKV_LOG_LAUNCH("prefill_valu_kernel", blocks, kValuThreads, "D=%d rows=%d heads=%d mask=%d fp8=%d",
+                 a.head_dim, a.num_tokens, a.num_heads, a.mask, a.kv_fp8);
   const float osc = a.kv_fp8 ? a.v_scale : 1.f;
   if (a.head_dim <= 64)
     hipLaunchKernelGGL((prefill_valu_kernel<T, 64>), dim3(blocks), dim3(kValuThreads), 0, stream, a, sl2, osc);

@@ -184,6 +184,8 @@ hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream) {
   const int blocks = (int)(blocks64 < 65536 ? blocks64 : 65536);
   const int shift = log2_exact(a.block_size);
   const int64_t num_slots = (int64_t)a.num_blocks * a.block_size;
+  PKV_LOG_LAUNCH("kv_scatter_kernel", blocks, kScatterThreads, "vector=%dB tokens=%d", vec,
+                 a.num_tokens);
 #define PKV_SCATTER(V)                                                                       \
   hipLaunchKernelGGL(kv_scatter_kernel<V>, dim3(blocks), dim3(kScatterThreads), 0, stream,  \
                      (const char*)a.key, (const char*)a.value, ts_b, a.slots, a.num_tokens,  \
@@ -218,6 +220,8 @@ hipError_t launch_kv_scatter_fp8(const ScatterArgs& a, float k_inv, float v_inv,
   const int blocks = (int)(blocks64 < 65536 ? blocks64 : 65536);
   const int shift = log2_exact(a.block_size);
   const int64_t num_slots = (int64_t)a.num_blocks * a.block_size;
+  PKV_LOG_LAUNCH("kv_scatter_fp8_kernel", blocks, kScatterThreads, "elements_per_lane=%d tokens=%d",
+                 n, a.num_tokens);
 #define PKV_SCATTER8(S, N)                                                                     \
   hipLaunchKernelGGL((kv_scatter_fp8_kernel<S, N>), dim3(blocks), dim3(kScatterThreads), 0,    \
                      stream, (const S::storage*)a.key, (const S::storage*)a.value,            \
@@ -243,6 +247,8 @@ hipError_t launch_kv_gather(const GatherArgs& a, hipStream_t stream) {
   const int64_t per_seq = (int64_t)a.max_seq_len * row_vecs;
   const dim3 grid((unsigned)((per_seq + kScatterThreads - 1) / kScatterThreads), a.num_seqs);
   const int shift = log2_exact(a.block_size);
+  PKV_LOG_LAUNCH("kv_gather_kernel", (long long)grid.x * grid.y, kScatterThreads, "vector=%dB seqs=%d",
+                 vec, a.num_seqs);
 #define PKV_GATHER(V)                                                                           \
   hipLaunchKernelGGL(kv_gather_kernel<V>, grid, dim3(kScatterThreads), 0, stream,              \
                      (char*)a.key_out, (char*)a.value_out, a.cu_seq_lens,                      \

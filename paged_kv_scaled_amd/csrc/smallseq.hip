@@ -498,6 +498,9 @@ bool launch_fwd_items(const SmallParams& sp, int d, hipStream_t stream) {
   p.max_kv = sp.max_kv;
   const int64_t waves = (p.total_items + 7) / 8;
   const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)), block(kDecodeThreads);
+  PKV_LOG_LAUNCH("decode_items_weights_kernel", grid.x, kDecodeThreads,
+                 "D=%d heads_per_item=%d items=%lld max_kv=%d", d, sp.g, (long long)p.total_items,
+                 sp.max_kv);
 #define PKV_ITEMS(DD, HH) \
   hipLaunchKernelGGL((decode_items_weights_kernel<T, DD, HH>), grid, block, 0, stream, p)
   if (d == 128) {
@@ -515,12 +518,16 @@ void launch_small(const SmallParams& p, int d, bool backward, hipStream_t stream
   if (backward && p.g == 1 && (d == 128 || d == 64)) {
     const int64_t waves = ((int64_t)p.S * p.Hkv + 7) / 8;
     const dim3 grid((unsigned)((waves + kSmallWaves - 1) / kSmallWaves)), block(kSmallThreads);
+    PKV_LOG_LAUNCH("smallseq_bwd_items_kernel", grid.x, kSmallThreads, "D=%d items=%lld max_kv=%d",
+                   d, (long long)p.S * p.Hkv, p.max_kv);
     if (d == 128) hipLaunchKernelGGL((smallseq_bwd_items_kernel<T, 128>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((smallseq_bwd_items_kernel<T, 64>), grid, block, 0, stream, p);
     return;
   }
   const int64_t items = (int64_t)p.S * p.Hkv;
   const dim3 grid((unsigned)((items + kSmallWaves - 1) / kSmallWaves)), block(kSmallThreads);
+  PKV_LOG_LAUNCH(backward ? "smallseq_bwd_kernel" : "smallseq_fwd_kernel", grid.x, kSmallThreads,
+                 "D=%d heads_per_kv=%d items=%lld max_kv=%d", d, p.g, (long long)items, p.max_kv);
 #define PKV_SMALL(DD)                                                                        \
   if (!backward) hipLaunchKernelGGL((smallseq_fwd_kernel<T, DD>), grid, block, 0, stream, p); \
   else if (p.g > 1) hipLaunchKernelGGL((smallseq_bwd_kernel<T, DD, true>), grid, block, 0, stream, p); \

@@ -274,3 +274,9 @@ def test_smallseq_rejections(lib):
                                        16 * 16 * 128, FAKE, 1, FAKE, NULL, 4, 40, 16, 16, 128,
                                        5, 16, 0.088, 16, B.PKV_BF16, NULL)
     assert r == B.PKV_ERR_INVALID_ARG and "cu_seq_lens" in B.last_error()
+
+
+def test_launch_log_switch(lib):
+    """The launch-log switch needs no GPU (the lines themselves are checked on the GPU)."""
+    assert lib.pkv_set_log(1) == B.PKV_OK
+    assert lib.pkv_set_log(0) == B.PKV_OK
