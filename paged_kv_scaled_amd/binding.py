@@ -75,11 +75,12 @@ class PkvError(RuntimeError):
 
 
 def load(path: Optional[str] = None):
-    """Load libpkv.so (raises if it was not built)."""
+    """Load libpkv.so (raises if it was not built).  PKV_LIBRARY in the environment names
+    another build of it (a sanitizer build, for instance)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("PKV_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m paged_kv_scaled_amd.build`")
     lib = ctypes.CDLL(p)
