@@ -410,77 +410,39 @@ def device_info():
     return info
 
 
-def committed_traffic(kernel_file: str, profile: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken on the
-    current kernel source (sha256 of the .hip file matches); else None."""
+DECODE_SOURCES = ("decode_device.h", "decode.hip", "common.h")
+
+
+def kernel_sources_sha(files=DECODE_SOURCES) -> str:
+    """sha256 over the sources that make the decode kernels (in this order)."""
     import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "paged_kv_scaled_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def committed_traffic(profile: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on the
+    current decode kernel sources (their sha256 matches); else None."""
     import re
-    src = os.path.join(ROOT, "paged_kv_scaled_amd", "csrc", kernel_file)
     prof = os.path.join(ROOT, "profiles", profile)
-    if not (os.path.exists(src) and os.path.exists(prof)):
+    if not os.path.exists(prof):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     text = open(prof).read()
     m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
     m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_sha and m_val) or m_sha.group(1) != sha:
+    if not (m_sha and m_val) or m_sha.group(1) != kernel_sources_sha():
         return None
     return float(m_val.group(1))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads",
-                    default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal,mixed_spans,"
-                            "decode_batch_fp8,mixed_batch,smallseq_train")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--calibration-copy", action="store_true",
-                    help="kept for old command lines: the 1 GiB device copy (the reference kernel "
-                         "of the counter passes) now always runs")
-    ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the measured copy and GEMM ceilings")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(sharding is described, not built). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
+def run_workloads(args, names):
+    """Every named workload but the default decode step: one entry each."""
     import numpy as np
     import torch
-    from paged_kv_scaled_amd import binding as B
     from paged_kv_scaled_amd import workloads as wl
-
-    assert torch.cuda.is_available(), "bench.py needs the GPU"
-    B.load()
-    names = [n for n in args.workloads.split(",") if n]
     result_wl = {}
-
-    # ---- default workload: decode batch step -------------------------------------------
-    log("generating decode_batch")
-    w = wl.decode_batch()
-    r = run_decode_step_bench(w, args.steps, args.warmup)
-    dbytes = decode_bytes(w)
-    sbytes = scatter_bytes(w, w.new_token_rows())
-    step_bytes = dbytes + sbytes
-    ms_step = r["wall_ms"] / args.steps
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-    dec_ms = r["dec_avg_ms"]
-    achieved = dbytes / (dec_ms * 1e-3) / 1e9
-    log(f"decode_batch: step {ms_step*1e3:.1f} us, decode launch {dec_ms*1e3:.1f} us "
-        f"(back to back; {med(r['dec_ms'])*1e3:.1f} us with an event pair around each), "
-        f"{achieved:.0f} GB/s ({achieved/HBM_PEAK_GBS*100:.1f}% of HBM peak)")
-    traffic = committed_traffic("decode.hip", "decode_batch_traffic.md")
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "paged_attention_decode (decode_stream_kernel + decode_merge_stream_kernel)",
-                "bytes_per_launch": dbytes, "launch_us_avg": round(dec_ms * 1e3, 2),
-                "launch_us_median_event_pair": round(med(r["dec_ms"]) * 1e3, 2)}
-
-    # ---- other workloads ------------------------------------------------------------------
     for name in names:
         if name == "decode_batch":
             continue
@@ -539,6 +501,70 @@ def main():
         result_wl[name] = entry
         del wk
         torch.cuda.empty_cache()
+
+    return result_wl
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads",
+                    default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal,mixed_spans,"
+                            "decode_batch_fp8,mixed_batch,smallseq_train")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="kept for old command lines: the 1 GiB device copy (the reference kernel "
+                         "of the counter passes) now always runs")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured copy and GEMM ceilings")
+    ap.add_argument("--workloads-only", action="store_true",
+                    help="profiling runs: skip the default decode step (and the ceilings and "
+                         "the CPU baseline) and print only the per-workload entries")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(sharding is described, not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from paged_kv_scaled_amd import binding as B
+    from paged_kv_scaled_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    B.load()
+    names = [n for n in args.workloads.split(",") if n]
+
+    if args.workloads_only:
+        result_wl = run_workloads(args, names)
+        print(json.dumps({"workloads": result_wl}), flush=True)
+        return
+
+    # ---- default workload: decode batch step -------------------------------------------
+    log("generating decode_batch")
+    w = wl.decode_batch()
+    r = run_decode_step_bench(w, args.steps, args.warmup)
+    dbytes = decode_bytes(w)
+    sbytes = scatter_bytes(w, w.new_token_rows())
+    step_bytes = dbytes + sbytes
+    ms_step = r["wall_ms"] / args.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    dec_ms = r["dec_avg_ms"]
+    achieved = dbytes / (dec_ms * 1e-3) / 1e9
+    log(f"decode_batch: step {ms_step*1e3:.1f} us, decode launch {dec_ms*1e3:.1f} us "
+        f"(back to back; {med(r['dec_ms'])*1e3:.1f} us with an event pair around each), "
+        f"{achieved:.0f} GB/s ({achieved/HBM_PEAK_GBS*100:.1f}% of HBM peak)")
+    traffic = committed_traffic("decode_batch_traffic.md")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "paged_attention_decode (decode_stream_kernel + decode_merge_stream_kernel)",
+                "bytes_per_launch": dbytes, "launch_us_avg": round(dec_ms * 1e3, 2),
+                "launch_us_median_event_pair": round(med(r["dec_ms"]) * 1e3, 2)}
+
+    result_wl = run_workloads(args, names)
 
     copy_gbs = copy_calibration()
     gemm_tf = None if args.no_ceilings else gemm_ceiling()
