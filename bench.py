@@ -410,7 +410,7 @@ def device_info():
     return info
 
 
-DECODE_SOURCES = ("decode_device.h", "decode.hip", "common.h")
+DECODE_SOURCES = ("decode_device.h", "decode_mfma.h", "decode.hip", "common.h")
 
 
 def kernel_sources_sha(files=DECODE_SOURCES) -> str:

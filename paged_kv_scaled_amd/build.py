@@ -36,7 +36,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
 # MFMA is first canonicalised (one extra VALU op per score), and NaN keys or queries give
 # undefined results either way.
 _MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]
-EXTRA = {"prefill_mfma.hip": _MFMA_FLAGS, "mixed.hip": _MFMA_FLAGS}
+# The decode kernels' matrix-core core keeps its accumulators in VGPRs for the same reason,
+# but stays in IEEE mode: decode results with NaN inputs are defined (NaN rows).
+EXTRA = {"prefill_mfma.hip": _MFMA_FLAGS, "mixed.hip": _MFMA_FLAGS,
+         "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

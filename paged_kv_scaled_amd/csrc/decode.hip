@@ -15,10 +15,58 @@ int heads_per_wave(int g) {
   return 8;
 }
 
+// Stream and split mode run on the matrix-core core (decode_mfma.h) where the vector
+// core's arithmetic per key is the larger cost: bf16 / fp16 queries at head_dim 64 or
+// 128, pages of at least 8 tokens, and 8 heads per wave (4 with an FP8 cache, whose codes
+// the vector core also widens per head group).  Measured per launch (32 sequences of
+// 1000..3000 keys, 8 kv heads, D 128): 8 heads per wave 93.6 -> 58.7 us (bf16) and
+// 95.5 -> 38.3 us (FP8); 4 heads over FP8 70 -> 61 us on the decode batch; 4 heads over
+// bf16 equal (55 us); 1 head 46 -> 52 us, where the vector core stays.  Item mode, fp32
+// and the other shapes always take the vector core.
+template <typename T, int D, int HPW>
+constexpr bool mfma_decode_shape() {
+  return T::bytes == 2 && (D == 64 || D == 128) && HPW >= (KvFp8<T>::value ? 4 : 8);
+}
+
+template <typename T, int D, int HPW>
+bool launch_main_mfma(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream) {
+  if constexpr (mfma_decode_shape<T, D, HPW>()) {
+    using C = DecodeShape<T, D>;
+    constexpr int MS = MSteps<T>::value;
+    if (dp.block_shift < 3) return false;
+    if (pl.stream) {
+      const int blocks = (int)((dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock);
+      PKV_LOG_LAUNCH("decode_stream_kernel", blocks, kDecodeThreads,
+                     "core=mfma D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld", D, HPW, MS,
+                     dp.nranges, (long long)dp.total_items);
+      hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, MS, true>), dim3(blocks),
+                         dim3(kDecodeThreads), 0, stream, dp);
+      return true;
+    }
+    if constexpr (C::LPT == 8 && C::TPR == 8) {
+      if (pl.num_splits == 1 && pl.max_seq_len <= kItemPages << dp.block_shift) return false;
+    }
+    const int64_t wanted = (dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int blocks = (int)(wanted < 8192 ? wanted : 8192);
+    PKV_LOG_LAUNCH("decode_split_kernel", blocks, kDecodeThreads,
+                   "core=mfma D=%d heads_per_wave=%d split_len=%d splits=%d items=%lld", D, HPW,
+                   dp.split_len, dp.nsplit, (long long)dp.total_items);
+    hipLaunchKernelGGL((decode_split_kernel<T, D, HPW, MS, true>), dim3(blocks),
+                       dim3(kDecodeThreads), 0, stream, dp);
+    return true;
+  } else {
+    (void)dp;
+    (void)pl;
+    (void)stream;
+    return false;
+  }
+}
+
 template <typename T, int D, int HPW>
 void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream) {
   using C = DecodeShape<T, D>;
   constexpr int NS = DecodeSteps<T, D, HPW>::value;
+  if (launch_main_mfma<T, D, HPW>(dp, pl, stream)) return;
   if (pl.stream) {
     const int blocks = (int)((dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock);
     PKV_LOG_LAUNCH("decode_stream_kernel", blocks, kDecodeThreads,

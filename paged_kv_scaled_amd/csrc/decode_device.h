@@ -6,7 +6,8 @@
 // h / (H / Hkv).  The ROCm TransformerEngine small-seq PR's s_q = 1, s_kv <= 16 varlen
 // cross attention is the same call with one sequence per query token.
 //
-// How (MI355X design, HBM-bound, vector ALU only):
+// How (MI355X design, HBM-bound; this is the vector-ALU core, and decode_mfma.h holds the
+// matrix-core core that stream and split mode use where the arithmetic per key weighs):
 //  * a wave handles one group of HPW query heads sharing a kv head over a contiguous
 //    segment of one sequence's keys;
 //  * lanes = (token t of a round, column c): a round covers TPR tokens, each token's
@@ -457,10 +458,21 @@ __device__ __forceinline__ void write_partial(const DecodeParams& p, int64_t slo
   }
 }
 
+}  // namespace
+
+}  // namespace pkv
+
+#include "decode_mfma.h"
+
+namespace pkv {
+
+namespace {
+
 // ---- split mode ------------------------------------------------------------------------
 
-// One (sequence, split, head group) item of split mode, walked by the calling wave.
-template <typename T, int D, int HPW, int NSTEP>
+// One (sequence, split, head group) item of split mode, walked by the calling wave (MF:
+// on the matrix-core core of decode_mfma.h).
+template <typename T, int D, int HPW, int NSTEP, bool MF = false>
 __device__ __forceinline__ void split_item(const DecodeParams& p, int64_t item) {
   using C = DecodeShape<T, D>;
   const int lane = threadIdx.x & (kWave - 1);
@@ -478,30 +490,41 @@ __device__ __forceinline__ void split_item(const DecodeParams& p, int64_t item) 
   const int kvh = hg / p.groups_per_kv, sub = hg % p.groups_per_kv;
   const int h0 = kvh * p.g + sub * HPW;
   const int nh = min(HPW, p.g - sub * HPW);
-  float m[HPW], l[HPW], acc[HPW][C::EPL];
-  attend_segment<T, D, HPW, NSTEP>(p, s, kvh, h0, nh, start, end, lane, m, l, acc);
-  if (t == 0) {
+  if constexpr (MF) {
+    MState<D> ms;
+    attend_segment_mfma<T, D, NSTEP>(p, s, kvh, h0, nh, start, end, lane, ms);
     if (ns == 1)
-      write_output<T, D, HPW>(p, s, h0, nh, c, l, acc);
+      write_output_mfma<T, D>(p, s, h0, nh, lane, ms);
     else
-      write_partial<T, D, HPW>(p, (int64_t)p.S * p.nsplit, (int64_t)s * p.nsplit + j, h0, nh, c,
-                               m, l, acc);
+      write_partial_mfma<T, D>(p, (int64_t)p.S * p.nsplit, (int64_t)s * p.nsplit + j, h0, nh,
+                               lane, ms);
+    return;
+  } else {
+    float m[HPW], l[HPW], acc[HPW][C::EPL];
+    attend_segment<T, D, HPW, NSTEP>(p, s, kvh, h0, nh, start, end, lane, m, l, acc);
+    if (t == 0) {
+      if (ns == 1)
+        write_output<T, D, HPW>(p, s, h0, nh, c, l, acc);
+      else
+        write_partial<T, D, HPW>(p, (int64_t)p.S * p.nsplit, (int64_t)s * p.nsplit + j, h0, nh,
+                                 c, m, l, acc);
+    }
   }
 }
 
 // Waves wave, wave + nwaves, ... walk the items.
-template <typename T, int D, int HPW, int NSTEP>
+template <typename T, int D, int HPW, int NSTEP, bool MF = false>
 __device__ __forceinline__ void split_items(const DecodeParams& p, int64_t wave, int64_t nwaves) {
   for (int64_t item = wave; item < p.total_items; item += nwaves)
-    split_item<T, D, HPW, NSTEP>(p, item);
+    split_item<T, D, HPW, NSTEP, MF>(p, item);
 }
 
-template <typename T, int D, int HPW, int NSTEP>
+template <typename T, int D, int HPW, int NSTEP, bool MF = false>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_split_kernel(const DecodeParams p) {
   if (guard_tripped(p.guard)) return;
-  split_items<T, D, HPW, NSTEP>(p, (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave),
-                                (int64_t)gridDim.x * kWavesPerBlock);
+  split_items<T, D, HPW, NSTEP, MF>(p, (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave),
+                                    (int64_t)gridDim.x * kWavesPerBlock);
 }
 
 // ---- item mode -------------------------------------------------------------------------
@@ -736,8 +759,9 @@ __device__ __forceinline__ void stream_locate(const DecodeParams& p, int64_t x, 
   start0 = before;
 }
 
-// One stream-mode item (head group, key range), walked by the calling wave.
-template <typename T, int D, int HPW, int NSTEP>
+// One stream-mode item (head group, key range), walked by the calling wave (MF: on the
+// matrix-core core of decode_mfma.h).
+template <typename T, int D, int HPW, int NSTEP, bool MF = false>
 __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item) {
   using C = DecodeShape<T, D>;
   const int lane = threadIdx.x & (kWave - 1);
@@ -763,14 +787,23 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item)
     const int seg_lo = (int)((lo > P ? lo : P) - P);
     const int seg_hi = (int)((hi < P + L ? hi : P + L) - P);
     if (seg_hi > seg_lo) {
-      float m[HPW], l[HPW], acc[HPW][C::EPL];
-      attend_segment<T, D, HPW, NSTEP>(p, s, kvh, h0, nh, seg_lo, seg_hi, lane, m, l, acc);
-      if (t == 0) {
+      const int64_t slot = (int64_t)r * 2 + (first ? 0 : 1);
+      if constexpr (MF) {
+        MState<D> ms;
+        attend_segment_mfma<T, D, NSTEP>(p, s, kvh, h0, nh, seg_lo, seg_hi, lane, ms);
         if (seg_lo == 0 && seg_hi == L)
-          write_output<T, D, HPW>(p, s, h0, nh, c, l, acc);
+          write_output_mfma<T, D>(p, s, h0, nh, lane, ms);
         else
-          write_partial<T, D, HPW>(p, (int64_t)p.nranges * 2, (int64_t)r * 2 + (first ? 0 : 1),
-                                   h0, nh, c, m, l, acc);
+          write_partial_mfma<T, D>(p, (int64_t)p.nranges * 2, slot, h0, nh, lane, ms);
+      } else {
+        float m[HPW], l[HPW], acc[HPW][C::EPL];
+        attend_segment<T, D, HPW, NSTEP>(p, s, kvh, h0, nh, seg_lo, seg_hi, lane, m, l, acc);
+        if (t == 0) {
+          if (seg_lo == 0 && seg_hi == L)
+            write_output<T, D, HPW>(p, s, h0, nh, c, l, acc);
+          else
+            write_partial<T, D, HPW>(p, (int64_t)p.nranges * 2, slot, h0, nh, c, m, l, acc);
+        }
       }
       first = false;
     }
@@ -778,13 +811,13 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item)
   }
 }
 
-template <typename T, int D, int HPW, int NSTEP>
+template <typename T, int D, int HPW, int NSTEP, bool MF = false>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_stream_kernel(const DecodeParams p) {
   if (guard_tripped(p.guard)) return;
   const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
   if (wave >= p.total_items) return;
-  stream_item<T, D, HPW, NSTEP>(p, wave);
+  stream_item<T, D, HPW, NSTEP, MF>(p, wave);
 }
 
 // ---- merge -----------------------------------------------------------------------------

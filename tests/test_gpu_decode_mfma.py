@@ -1,0 +1,132 @@
+"""The matrix-core decode core (stream and split mode at 8 query heads per wave with a
+bf16 / fp16 cache; 4 or more with an FP8 cache) against the fp64 oracle.
+
+Every cache slot that no token was written to holds NaN (the Dev sentinel), so a key
+outside a segment that leaked into a probability or a V product would show up as NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import reference as ref
+from paged_kv_scaled_amd import binding as B
+from paged_kv_scaled_amd import workloads as wl
+
+from gpu_helpers import Dev, as_f64, compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, rows=None):
+    d = Dev(w)
+    d.write_all()
+    out = d.decode()
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    assert not np.isnan(got).any(), "NaN reached an output row"
+    want, _ = ref.workload_attention(w, rows=rows)
+    if rows is not None:
+        got, want = got[rows], want[rows]
+    return compare(got, want, w.dtype, w.name)
+
+
+def _batch(name, seed, dtype, lens, H, Hkv, D, bs=16):
+    lens = np.asarray(lens, np.int32)
+    return wl.build(name, seed, dtype, lens, np.minimum(lens, 1), H, Hkv, D, bs, wl.MASK_NONE,
+                    decode=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_mfma_stream_g8(gpu, dtype, head_dim):
+    """Stream mode, 64 q / 8 kv heads: lengths that are not multiples of 8 or 32, so range
+    boundaries and sequence ends fall inside steps and inside 8-key groups."""
+    rng = np.random.default_rng(60 + head_dim)
+    lens = rng.integers(1, 2500, size=12)
+    lens[:4] = [1, 31, 33, 257]
+    _run(_batch("mfma_stream", 61, dtype, lens, 64, 8, head_dim))
+
+
+def test_mfma_decode_batch_shape_g8(gpu):
+    """The decode batch's length mix (256..4096) with 64 q heads: every output row."""
+    lens = np.random.default_rng(1).integers(256, 4097, size=24)
+    _run(_batch("mfma_batch_g8", 62, "bf16", lens, 64, 8, 128))
+
+
+@pytest.mark.parametrize("bs", [8, 32, 64])
+def test_mfma_block_sizes(gpu, bs):
+    """Pages of 8 tokens (one 8-key group per page: every group its own table entry, many
+    table windows per sequence) up to 64."""
+    lens = np.array([3000, 8, 9, 700, 1234], np.int32)
+    _run(_batch("mfma_bs", 63, "bf16", lens, 16, 2, 128, bs=bs))
+
+
+def test_mfma_small_pages_take_vector_core(gpu):
+    """Pages of 4 tokens cannot hold an 8-key group: the vector core runs, same results."""
+    lens = np.array([900, 5, 333], np.int32)
+    _run(_batch("mfma_bs4", 64, "bf16", lens, 16, 2, 128, bs=4))
+
+
+def test_mfma_split_mode(gpu):
+    """More than 1024 sequences: split mode (256-key splits, partials, split merge)."""
+    rng = np.random.default_rng(65)
+    lens = rng.integers(1, 900, size=1100).astype(np.int32)
+    w = _batch("mfma_split", 65, "f16", lens, 16, 2, 128)
+    rows = np.unique(np.concatenate([np.arange(8), rng.choice(len(lens), 160, replace=False)]))
+    _run(w, rows=rows)
+
+
+def test_mfma_empty_and_tiny_sequences(gpu):
+    """Empty sequences give zero rows; one-key sequences return that key's V row exactly."""
+    lens = np.array([0, 1, 0, 2, 513, 3000, 0], np.int32)
+    S, H, Hkv, D = len(lens), 16, 2, 128
+    w = _batch("mfma_edge", 66, "bf16", lens, H, Hkv, D)
+    # the generator gives empty sequences no query row: one per sequence ([S, H, D])
+    q = wl.round_to_storage(np.random.default_rng(6).standard_normal((S, H, D)).astype(np.float32), "bf16")
+    w.query = q
+    w.q_lens = np.ones(S, np.int32)
+    w.cu_seqlens_q = np.arange(S + 1, dtype=np.int32)
+    d = Dev(w)
+    B.kv_cache_write(d.key, d.value, d.slots, d.kc, d.vc)
+    out = d.decode()
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    for s in (0, 2, 6):
+        assert np.all(got[s] == 0)
+    v = ref.widen(w.value, "bf16")
+    g = H // Hkv
+    for h in range(H):
+        assert np.array_equal(got[1, h], v[w.cu_seq_lens[1], h // g])
+    keys = ref.split_logical(ref.widen(w.key, "bf16"), w.cu_seq_lens)
+    vals = ref.split_logical(v, w.cu_seq_lens)
+    live = [1, 3, 4, 5]
+    want, _ = ref.paged_attention(ref.widen(q[live], "bf16"), [keys[i] for i in live],
+                                  [vals[i] for i in live], np.arange(len(live) + 1, dtype=np.int32),
+                                  lens[live], Hkv, w.scale, wl.MASK_NONE)
+    compare(got[live], want, "bf16", "mfma_edge")
+
+
+def test_mfma_constant_value_rows(gpu):
+    """Constant V gives the constant for any query (closed form), exactly."""
+    w = _batch("mfma_const", 67, "bf16", np.random.default_rng(7).integers(1, 3000, size=9), 64, 8, 128)
+    w.value[:] = wl.round_to_storage(np.full(1, 0.8125, np.float32), "bf16")[0]
+    d = Dev(w)
+    d.write_all()
+    out = d.decode()
+    torch.cuda.synchronize()
+    assert np.all(as_f64(out) == 0.8125)
+
+
+def test_mfma_large_scores_rescale(gpu):
+    """Scores spread over hundreds of log2 units: the running max moves many times (the
+    lazy rescale) and the result stays on the oracle."""
+    w = _batch("mfma_rescale", 68, "bf16", [2000, 777, 64], 64, 8, 128)
+    w.scale = 2.0
+    _run(w)
+
+
+def test_mfma_fp8_g8(gpu):
+    """FP8 cache at 8 heads per wave, stream mode, D 128 and 64."""
+    for D in (128, 64):
+        lens = np.random.default_rng(69).integers(1, 3000, size=10)
+        _run(wl.with_fp8_cache(_batch("mfma_fp8_g8", 69, "bf16", lens, 64, 8, D)))
