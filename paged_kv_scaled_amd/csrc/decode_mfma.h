@@ -27,8 +27,8 @@
 //    B operand of product i: column n = dim n D/16 + i, k slots = keys 8a .. 8a+7.
 //    No LDS and no cross-lane traffic;
 //  * O: lane l holds heads 4a + j (j < 4), dims n D/16 + i of product i.
-// Steps start at multiples of 32 keys of the sequence, so every 8-key group lies in one
-// page.  Keys of a step outside the segment [lo, hi) get probability 0 and their V
+// Steps start at multiples of 8 keys of the sequence (the segment start rounded down), so
+// every 8-key group lies in one page.  Keys of a step outside the segment [lo, hi) get probability 0 and their V
 // words are zeroed (a stale slot of a page may hold anything, NaN included); groups
 // entirely past the end re-read the last group instead of following a table entry
 // that may not exist.  Softmax: the same lazy running max as the vector core (move
@@ -146,7 +146,7 @@ __device__ __forceinline__ void load_words(uint32_t* dst, const void* base, int6
   }
 }
 
-// Loads of the step starting at key sb (a multiple of 32) of a segment ending at hi.
+// Loads of the step starting at key sb (a multiple of 8) of a segment ending at hi.
 template <typename T, int D>
 __device__ __forceinline__ void mload_step(MStep<T, D>& st, const DecodeParams& p,
                                            const TableWindow& tw, int64_t head_off, int sb,
@@ -301,7 +301,7 @@ __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s
     const int32_t* table = p.block_tables + (int64_t)s * p.mb;
     const int64_t head_off = (int64_t)kvh * D;
     const int last_page = (hi - 1) >> p.block_shift;
-    const int start = lo & ~(kMStep - 1);
+    const int start = lo & ~(kMGroup - 1);
     TableWindow tw;
     table_window_load(tw, table, start >> p.block_shift, last_page, lane);
     for (int base = start; base < hi; base += NSTEP * kMStep) {
