@@ -158,7 +158,8 @@ DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
   // Stream mode whenever some sequence needs more than one split and the batch is small
   // enough for every wave to scan the lengths.
   pl.stream = pl.num_splits > 1 && num_seqs <= kStreamMaxSeqs;
-  pl.num_ranges = pl.stream ? (int)(kStreamWaves / groups > 1 ? kStreamWaves / groups : 1) : 0;
+  const int waves = mixed ? kStreamWavesMixed : kStreamWaves;
+  pl.num_ranges = pl.stream ? (int)(waves / groups > 1 ? waves / groups : 1) : 0;
   const size_t slots = pl.stream ? (size_t)num_heads * pl.num_ranges * 2
                                  : (pl.num_splits > 1 ? (size_t)num_seqs * num_heads * pl.num_splits : 0);
   pl.workspace_bytes = slots * (size_t)head_dim * sizeof(float) + slots * 2 * sizeof(float);

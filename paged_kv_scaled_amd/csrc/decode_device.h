@@ -44,8 +44,10 @@ constexpr int kDecodeThreads = 256;
 constexpr int kWavesPerBlock = kDecodeThreads / kWave;
 constexpr float kLazyRescale = 8.0f;   // log2 units
 constexpr int kStreamMaxSeqs = 1024;   // stream mode scans seq_lens in every wave
-constexpr int kStreamWaves = 2048;     // waves of the stream grid (all head groups): one round
-                                       // at two waves per SIMD on 256 CUs
+constexpr int kStreamWaves = 1024;     // waves of the stream grid (all head groups): one wave
+                                       // per SIMD on 256 CUs
+constexpr int kStreamWavesMixed = 2048;   // the same inside the mixed-batch kernel, whose
+                                          // decode blocks hold 8 waves (two per SIMD)
 constexpr int kStreamMinRange = 64;    // shortest range, keys
 
 template <typename T, int D>

@@ -100,9 +100,9 @@ def test_decode_rejections(lib):
 def test_decode_workspace_size_plan(lib):
     # one split per sequence -> no workspace
     assert lib.pkv_decode_workspace_size(30720, 16, 16, 128, 16, 16) == 0
-    # stream mode: 2048 waves over 8 wave groups (4 heads a wave) = 256 key ranges;
-    # 32 heads x 256 ranges x 2 partial slots x (128 + 2) floats
-    assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 4096) == 32 * 256 * 2 * 130 * 4
+    # stream mode: 1024 waves over 8 wave groups (4 heads a wave) = 128 key ranges;
+    # 32 heads x 128 ranges x 2 partial slots x (128 + 2) floats
+    assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 4096) == 32 * 128 * 2 * 130 * 4
     # split mode beyond 1024 sequences: splits grow to 64 blocks (1024 keys), 5 of them
     assert lib.pkv_decode_workspace_size(2000, 8, 8, 128, 16, 5000) == 2000 * 8 * 5 * 130 * 4
     assert lib.pkv_decode_workspace_size(2000, 8, 8, 128, 16, 300) == 0
