@@ -17,15 +17,18 @@ int heads_per_wave(int g) {
 
 // Stream and split mode run on the matrix-core core (decode_mfma.h) where the vector
 // core's arithmetic per key is the larger cost: bf16 / fp16 queries at head_dim 64 or
-// 128, pages of at least 8 tokens, and 8 heads per wave (4 with an FP8 cache, whose codes
-// the vector core also widens per head group).  Measured per launch (32 sequences of
-// 1000..3000 keys, 8 kv heads, D 128): 8 heads per wave 93.6 -> 58.7 us (bf16) and
-// 95.5 -> 38.3 us (FP8); 4 heads over FP8 70 -> 61 us on the decode batch; 4 heads over
-// bf16 equal (55 us); 1 head 46 -> 52 us, where the vector core stays.  Item mode, fp32
-// and the other shapes always take the vector core.
+// 128, pages of at least 8 tokens, and 8 heads per wave; 4 with an FP8 cache (whose codes
+// the vector core also widens per head group) or at head_dim 64 (where its per-key
+// overhead is spread over half the bytes).  Measured per launch (32 sequences of
+// 1000..3000 keys, 8 kv heads, D 128 unless stated): 8 heads per wave 93.6 -> 58.7 us
+// (bf16) and 95.5 -> 38.3 us (FP8); 4 heads over FP8 70 -> 61 us on the decode batch;
+// 4 heads at D 64 38.9 -> 35.8 us; 4 heads over bf16 at D 128 100.3 -> 102.9 us on the
+// decode batch and 1 head 46 -> 52 us, where the vector core stays.  Item mode, fp32 and
+// the other shapes always take the vector core.
 template <typename T, int D, int HPW>
 constexpr bool mfma_decode_shape() {
-  return T::bytes == 2 && (D == 64 || D == 128) && HPW >= (KvFp8<T>::value ? 4 : 8);
+  return T::bytes == 2 && (D == 64 || D == 128) &&
+         HPW >= ((KvFp8<T>::value || D == 64) ? 4 : 8);
 }
 
 template <typename T, int D, int HPW>

@@ -1,5 +1,6 @@
 """The matrix-core decode core (stream and split mode at 8 query heads per wave with a
-bf16 / fp16 cache; 4 or more with an FP8 cache) against the fp64 oracle.
+bf16 / fp16 cache at head_dim 128; 4 or more with an FP8 cache or at head_dim 64) against
+the fp64 oracle.
 
 Every cache slot that no token was written to holds NaN (the Dev sentinel), so a key
 outside a segment that leaked into a probability or a V product would show up as NaN.
@@ -45,6 +46,15 @@ def test_mfma_stream_g8(gpu, dtype, head_dim):
     lens = rng.integers(1, 2500, size=12)
     lens[:4] = [1, 31, 33, 257]
     _run(_batch("mfma_stream", 61, dtype, lens, 64, 8, head_dim))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_mfma_stream_d64_g4(gpu, dtype):
+    """head_dim 64 at 4 heads per wave (32 q / 8 kv heads) runs on the matrix cores too."""
+    rng = np.random.default_rng(70)
+    lens = rng.integers(1, 3000, size=16)
+    lens[:3] = [7, 8, 4095]
+    _run(_batch("mfma_d64_g4", 70, dtype, lens, 32, 8, 64))
 
 
 def test_mfma_decode_batch_shape_g8(gpu):
