@@ -118,8 +118,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   constexpr int KS = D / 16;          // k-steps of the QK^T product
   constexpr int DB = D / 32;          // 32-dim blocks of O^T
   constexpr int TG = kBN * (D / 8) / NT;         // tokens per thread (1, 2 or 4)
-  __shared__ __align__(16) uint8_t s_k[L::KBYTES];
-  __shared__ __align__(16) uint8_t s_v[L::VBYTES];
+  // two tile slots: tile k is stored into slot k % 2 while the waves may still compute
+  // tile k - 1 from the other, so one barrier per tile suffices
+  __shared__ __align__(16) uint8_t s_k2[2][L::KBYTES];
+  __shared__ __align__(16) uint8_t s_v2[2][L::VBYTES];
   __shared__ int32_t s_tbl[kTableChunk];
 
   const int tid = threadIdx.x;
@@ -242,7 +244,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
       return x;
     }
   };
-  auto store_tile = [&](const KR (&kraw)[TG], const KR (&vraw)[TG]) {
+  auto store_tile = [&](const KR (&kraw)[TG], const KR (&vraw)[TG], uint8_t* s_k, uint8_t* s_v) {
     u32x4_t vreg[TG];
 #pragma unroll
     for (int i = 0; i < TG; ++i) {
@@ -290,7 +292,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   // refilled with the tile two ahead, then every wave computes on the LDS tile.  Two tiles
   // in flight cover the gather latency when the keys come from HBM rather than L2.
   auto tile_step = [&](int k0, KR (&kreg)[TG], KR (&vreg)[TG]) {
-    store_tile(kreg, vreg);
+    // Slot (k0 / kBN) % 2 last held tile k0 - 2 kBN, which every wave finished computing
+    // before it reached the previous tile's barrier.
+    uint8_t* s_k = s_k2[(k0 / kBN) & 1];
+    uint8_t* s_v = s_v2[(k0 / kBN) & 1];
+    store_tile(kreg, vreg, s_k, s_v);
     __syncthreads();
     const int k2 = k0 + 2 * kBN;
     if (k2 < kv_end) {
@@ -409,7 +415,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
         }
       }
     }
-    __syncthreads();
   };
   if (kv_end > 0) {
     load_tile(0, kra, vra);
