@@ -86,6 +86,15 @@ def test_mfma_split_mode(gpu):
     _run(w, rows=rows)
 
 
+def test_mfma_split_mode_d64_g4(gpu):
+    """Split mode at head_dim 64 and 4 heads per wave (bf16), the other matrix-core shape."""
+    rng = np.random.default_rng(71)
+    lens = rng.integers(1, 1200, size=1030).astype(np.int32)
+    w = _batch("mfma_split_d64", 71, "bf16", lens, 32, 8, 64)
+    rows = np.unique(np.concatenate([np.arange(6), rng.choice(len(lens), 120, replace=False)]))
+    _run(w, rows=rows)
+
+
 def test_mfma_empty_and_tiny_sequences(gpu):
     """Empty sequences give zero rows; one-key sequences return that key's V row exactly."""
     lens = np.array([0, 1, 0, 2, 513, 3000, 0], np.int32)
