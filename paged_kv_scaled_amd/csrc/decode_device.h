@@ -792,7 +792,9 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item)
       const int64_t slot = (int64_t)r * 2 + (first ? 0 : 1);
       if constexpr (MF) {
         MState<D> ms;
-        attend_segment_mfma<T, D, NSTEP>(p, s, kvh, h0, nh, seg_lo, seg_hi, lane, ms);
+        // one wave per SIMD: a rolling buffer where a load batch would be one step
+        attend_segment_mfma<T, D, NSTEP, NSTEP == 1>(p, s, kvh, h0, nh, seg_lo, seg_hi, lane,
+                                                      ms);
         if (seg_lo == 0 && seg_hi == L)
           write_output_mfma<T, D>(p, s, h0, nh, lane, ms);
         else

@@ -276,7 +276,10 @@ __device__ __forceinline__ void mcompute_step(MStep<T, D>& st, const u32x4_t (&q
 
 // State of one wave over keys [lo, hi) of sequence s for heads h0 .. h0+nh-1 (nh <= 8)
 // of kv head kvh.  On return s.l is the head's full sum in every lane of column n.
-template <typename T, int D, int NSTEP>
+// ROLL: a rolling double buffer of one step each (the loads of step k + 2 go out as soon as
+// step k is computed), for the stream grid, whose single wave per SIMD has no other wave
+// to hide its arithmetic behind; otherwise batches of NSTEP steps loaded together.
+template <typename T, int D, int NSTEP, bool ROLL = false>
 __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s, int kvh, int h0,
                                                     int nh, int lo, int hi, int lane,
                                                     MState<D>& st) {
@@ -304,22 +307,48 @@ __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s
     const int start = lo & ~(kMGroup - 1);
     TableWindow tw;
     table_window_load(tw, table, start >> p.block_shift, last_page, lane);
-    for (int base = start; base < hi; base += NSTEP * kMStep) {
-      const int it_last = (min(base + NSTEP * kMStep, hi) - 1) >> p.block_shift;
-      if (it_last >= tw.chunk_base + kWave)
-        table_window_load(tw, table, base >> p.block_shift, last_page, lane);
-      MStep<T, D> ms[NSTEP];
+    auto compute = [&](MStep<T, D>& b, int sb) {
+      if (sb >= lo && sb + kMStep <= hi)
+        mcompute_step<T, D, true>(b, q, st, p.scale_log2, sb, lo, hi, a);
+      else
+        mcompute_step<T, D, false>(b, q, st, p.scale_log2, sb, lo, hi, a);
+    };
+    if constexpr (ROLL) {
+      // steps past the end re-read the last group (no branch around a load) and are
+      // never computed
+      const int last_group = (hi - 1) & ~(kMGroup - 1);
+      auto load = [&](MStep<T, D>& b, int sb) {
+        const int need = (min(sb + kMStep, hi) - 1) >> p.block_shift;
+        if (need >= tw.chunk_base + kWave)
+          table_window_load(tw, table, min(sb, last_group) >> p.block_shift, last_page, lane);
+        mload_step<T, D>(b, p, tw, head_off, sb, hi, a, n);
+      };
+      MStep<T, D> b0, b1;
+      load(b0, start);
+      load(b1, start + kMStep);
+      for (int sb = start;; sb += 2 * kMStep) {
+        compute(b0, sb);
+        if (sb + kMStep >= hi) break;
+        load(b0, sb + 2 * kMStep);
+        compute(b1, sb + kMStep);
+        if (sb + 2 * kMStep >= hi) break;
+        load(b1, sb + 3 * kMStep);
+      }
+    } else {
+      for (int base = start; base < hi; base += NSTEP * kMStep) {
+        const int it_last = (min(base + NSTEP * kMStep, hi) - 1) >> p.block_shift;
+        if (it_last >= tw.chunk_base + kWave)
+          table_window_load(tw, table, base >> p.block_shift, last_page, lane);
+        MStep<T, D> ms[NSTEP];
 #pragma unroll
-      for (int k = 0; k < NSTEP; ++k)
-        mload_step<T, D>(ms[k], p, tw, head_off, base + k * kMStep, hi, a, n);
+        for (int k = 0; k < NSTEP; ++k)
+          mload_step<T, D>(ms[k], p, tw, head_off, base + k * kMStep, hi, a, n);
 #pragma unroll
-      for (int k = 0; k < NSTEP; ++k) {
-        const int sb = base + k * kMStep;
-        if (sb >= hi) break;
-        if (sb >= lo && sb + kMStep <= hi)
-          mcompute_step<T, D, true>(ms[k], q, st, p.scale_log2, sb, lo, hi, a);
-        else
-          mcompute_step<T, D, false>(ms[k], q, st, p.scale_log2, sb, lo, hi, a);
+        for (int k = 0; k < NSTEP; ++k) {
+          const int sb = base + k * kMStep;
+          if (sb >= hi) break;
+          compute(ms[k], sb);
+        }
       }
     }
   }
