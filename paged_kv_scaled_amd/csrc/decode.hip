@@ -16,28 +16,40 @@ int heads_per_wave(int g) {
 }
 
 // Stream and split mode run on the matrix-core core (decode_mfma.h) where the vector
-// core's arithmetic per key is the larger cost: bf16 / fp16 queries at head_dim 64 or
-// 128, pages of at least 8 tokens, and 8 heads per wave; 4 with an FP8 cache (whose codes
-// the vector core also widens per head group) or at head_dim 64 (where its per-key
-// overhead is spread over half the bytes).  Measured per launch (32 sequences of
-// 1000..3000 keys, 8 kv heads, D 128 unless stated): 8 heads per wave 93.6 -> 58.7 us
-// (bf16) and 95.5 -> 38.3 us (FP8); 4 heads over FP8 70 -> 61 us on the decode batch;
-// 4 heads at D 64 38.9 -> 35.8 us; 4 heads over bf16 at D 128 100.3 -> 102.9 us on the
-// decode batch and 1 head 46 -> 52 us, where the vector core stays.  Item mode, fp32 and
-// the other shapes always take the vector core.
+// core's arithmetic per key is the larger cost, for bf16 / fp16 queries at head_dim 64 or
+// 128 with pages of at least 8 tokens.
+//  * Stream mode (one wave per SIMD; with a bf16 / fp16 cache the core keeps a rolling
+//    double buffer): from 4 heads per wave.  Measured per launch at 1024 stream waves:
+//    decode batch (4 heads) 99.3 -> 96.4 us, 32 sequences of 1000..3000 keys at 4 heads
+//    52.2 -> 50.0 us and at 8 heads 55.9 -> 51.4 us; at 1 and 2 heads the vector core
+//    stays ahead (46.2 vs 48.5 us, 48.0 vs 49.8 us).
+//  * Split mode (many short items, bound by occupancy: the matrix-core kernel allows 2
+//    waves per SIMD, the vector kernel 4): from 8 heads per wave, or 4 with an FP8 cache
+//    (whose codes the vector core widens per head group) or at head_dim 64.  Measured:
+//    1100 sequences at 4 heads 149 us (vector) against 175 us (bf16), but 119 -> 95 us
+//    over FP8.
+// Item mode, fp32 and the other shapes always take the vector core.
+template <typename T, int D>
+constexpr bool mfma_decode_type() {
+  return T::bytes == 2 && (D == 64 || D == 128);
+}
+
 template <typename T, int D, int HPW>
-constexpr bool mfma_decode_shape() {
-  return T::bytes == 2 && (D == 64 || D == 128) &&
-         HPW >= ((KvFp8<T>::value || D == 64) ? 4 : 8);
+constexpr bool mfma_stream_shape() {
+  return mfma_decode_type<T, D>() && HPW >= 4;
+}
+
+template <typename T, int D, int HPW>
+constexpr bool mfma_split_shape() {
+  return mfma_decode_type<T, D>() && HPW >= ((KvFp8<T>::value || D == 64) ? 4 : 8);
 }
 
 template <typename T, int D, int HPW>
 bool launch_main_mfma(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream) {
-  if constexpr (mfma_decode_shape<T, D, HPW>()) {
-    using C = DecodeShape<T, D>;
-    constexpr int MS = MSteps<T>::value;
-    if (dp.block_shift < 3) return false;
-    if (pl.stream) {
+  if (dp.block_shift < 3) return false;
+  constexpr int MS = MSteps<T>::value;
+  if (pl.stream) {
+    if constexpr (mfma_stream_shape<T, D, HPW>()) {
       const int blocks = (int)((dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock);
       PKV_LOG_LAUNCH("decode_stream_kernel", blocks, kDecodeThreads,
                      "core=mfma D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld", D, HPW, MS,
@@ -46,6 +58,10 @@ bool launch_main_mfma(const DecodeParams& dp, const DecodePlan& pl, hipStream_t 
                          dim3(kDecodeThreads), 0, stream, dp);
       return true;
     }
+    return false;
+  }
+  if constexpr (mfma_split_shape<T, D, HPW>()) {
+    using C = DecodeShape<T, D>;
     if constexpr (C::LPT == 8 && C::TPR == 8) {
       if (pl.num_splits == 1 && pl.max_seq_len <= kItemPages << dp.block_shift) return false;
     }
@@ -57,12 +73,8 @@ bool launch_main_mfma(const DecodeParams& dp, const DecodePlan& pl, hipStream_t 
     hipLaunchKernelGGL((decode_split_kernel<T, D, HPW, MS, true>), dim3(blocks),
                        dim3(kDecodeThreads), 0, stream, dp);
     return true;
-  } else {
-    (void)dp;
-    (void)pl;
-    (void)stream;
-    return false;
   }
+  return false;
 }
 
 template <typename T, int D, int HPW>
@@ -73,8 +85,8 @@ void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t strea
   if (pl.stream) {
     const int blocks = (int)((dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock);
     PKV_LOG_LAUNCH("decode_stream_kernel", blocks, kDecodeThreads,
-                   "D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld", D, HPW, NS, dp.nranges,
-                   (long long)dp.total_items);
+                   "core=vector D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld", D, HPW, NS,
+                   dp.nranges, (long long)dp.total_items);
     hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, NS>), dim3(blocks), dim3(kDecodeThreads),
                        0, stream, dp);
     return;
@@ -84,7 +96,7 @@ void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t strea
       const int64_t waves = (dp.total_items + C::TPR - 1) / C::TPR;
       const int blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
       PKV_LOG_LAUNCH("decode_items_kernel", blocks, kDecodeThreads,
-                     "D=%d heads_per_wave=%d items=%lld (8 per wave)", D, HPW,
+                     "core=vector D=%d heads_per_wave=%d items=%lld (8 per wave)", D, HPW,
                      (long long)dp.total_items);
       hipLaunchKernelGGL((decode_items_kernel<T, D, HPW, kItemSteps>), dim3(blocks),
                          dim3(kDecodeThreads), 0, stream, dp);
@@ -94,8 +106,8 @@ void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t strea
   const int64_t wanted = (dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock;
   const int blocks = (int)(wanted < 8192 ? wanted : 8192);
   PKV_LOG_LAUNCH("decode_split_kernel", blocks, kDecodeThreads,
-                 "D=%d heads_per_wave=%d split_len=%d splits=%d items=%lld", D, HPW, dp.split_len,
-                 dp.nsplit, (long long)dp.total_items);
+                 "core=vector D=%d heads_per_wave=%d split_len=%d splits=%d items=%lld", D, HPW,
+                 dp.split_len, dp.nsplit, (long long)dp.total_items);
   if (pl.max_seq_len <= C::STEP)
     hipLaunchKernelGGL((decode_split_kernel<T, D, HPW, 1>), dim3(blocks), dim3(kDecodeThreads),
                        0, stream, dp);

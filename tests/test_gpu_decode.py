@@ -66,6 +66,17 @@ def test_decode_long_sequence_many_splits(gpu):
     _run(w)
 
 
+@pytest.mark.parametrize("H", [8, 16])
+def test_decode_stream_vector_core(gpu, H):
+    """Stream mode at 1 and 2 query heads per kv head (8 kv heads, D 128, bf16): the vector
+    core, which the matrix cores take over from 4 heads per wave."""
+    lens = np.random.default_rng(25).integers(1, 3000, size=20).astype(np.int32)
+    lens[:3] = [1, 33, 2999]
+    w = wl.build("stream_vector", 25, "bf16", lens, np.ones(len(lens), np.int32), H, 8, 128, 16,
+                 wl.MASK_NONE, decode=True)
+    _run(w)
+
+
 def test_decode_gqa_wide(gpu):
     """g = 16 (two 8-head waves per kv head) and g = 6 (a partly filled wave)."""
     for H, Hkv in [(32, 2), (12, 2)]:
