@@ -276,9 +276,9 @@ __device__ __forceinline__ void mcompute_step(MStep<T, D>& st, const u32x4_t (&q
 
 // State of one wave over keys [lo, hi) of sequence s for heads h0 .. h0+nh-1 (nh <= 8)
 // of kv head kvh.  On return s.l is the head's full sum in every lane of column n.
-// ROLL: a rolling double buffer of one step each (the loads of step k + 2 go out as soon as
-// step k is computed), for the stream grid, whose single wave per SIMD has no other wave
-// to hide its arithmetic behind; otherwise batches of NSTEP steps loaded together.
+// ROLL: a rolling double buffer of NSTEP steps each (the loads of batch k + 2 go out as soon
+// as batch k is computed), for the stream grid, whose single wave per SIMD has no other
+// wave to hide its arithmetic behind; otherwise batches of NSTEP steps loaded together.
 template <typename T, int D, int NSTEP, bool ROLL = false>
 __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s, int kvh, int h0,
                                                     int nh, int lo, int hi, int lane,
@@ -314,25 +314,36 @@ __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s
         mcompute_step<T, D, false>(b, q, st, p.scale_log2, sb, lo, hi, a);
     };
     if constexpr (ROLL) {
-      // steps past the end re-read the last group (no branch around a load) and are
+      // batches past the end re-read the last group (no branch around a load) and are
       // never computed
+      constexpr int BATCH = NSTEP * kMStep;
       const int last_group = (hi - 1) & ~(kMGroup - 1);
-      auto load = [&](MStep<T, D>& b, int sb) {
-        const int need = (min(sb + kMStep, hi) - 1) >> p.block_shift;
+      auto load = [&](MStep<T, D> (&b)[NSTEP], int base) {
+        const int need = (min(base + BATCH, hi) - 1) >> p.block_shift;
         if (need >= tw.chunk_base + kWave)
-          table_window_load(tw, table, min(sb, last_group) >> p.block_shift, last_page, lane);
-        mload_step<T, D>(b, p, tw, head_off, sb, hi, a, n);
+          table_window_load(tw, table, min(base, last_group) >> p.block_shift, last_page, lane);
+#pragma unroll
+        for (int k = 0; k < NSTEP; ++k)
+          mload_step<T, D>(b[k], p, tw, head_off, base + k * kMStep, hi, a, n);
       };
-      MStep<T, D> b0, b1;
+      auto compute_batch = [&](MStep<T, D> (&b)[NSTEP], int base) {
+#pragma unroll
+        for (int k = 0; k < NSTEP; ++k) {
+          const int sb = base + k * kMStep;
+          if (sb >= hi) break;
+          compute(b[k], sb);
+        }
+      };
+      MStep<T, D> b0[NSTEP], b1[NSTEP];
       load(b0, start);
-      load(b1, start + kMStep);
-      for (int sb = start;; sb += 2 * kMStep) {
-        compute(b0, sb);
-        if (sb + kMStep >= hi) break;
-        load(b0, sb + 2 * kMStep);
-        compute(b1, sb + kMStep);
-        if (sb + 2 * kMStep >= hi) break;
-        load(b1, sb + 3 * kMStep);
+      load(b1, start + BATCH);
+      for (int base = start;; base += 2 * BATCH) {
+        compute_batch(b0, base);
+        if (base + BATCH >= hi) break;
+        load(b0, base + 2 * BATCH);
+        compute_batch(b1, base + BATCH);
+        if (base + 2 * BATCH >= hi) break;
+        load(b1, base + 3 * BATCH);
       }
     } else {
       for (int base = start; base < hi; base += NSTEP * kMStep) {
