@@ -166,9 +166,13 @@ size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  * sequence attending all L_s cached tokens (the new token already written
  * by pkv_kv_cache_write).  Flash decoding: the keys of a sequence are cut into
  * splits, each split reduces to (partial output, max, sum) in the workspace,
- * and a log-sum-exp merge combines them.  The small-seq varlen cross-attention
- * case of the ROCm TransformerEngine PR (s_q = 1, s_kv <= 16, one sequence per
- * query token) is this call with num_seqs = number of query tokens.
+ * and a log-sum-exp merge combines them.  Scores, running max and sums are
+ * fp32; the probabilities are rounded to the query type for the P.V products,
+ * which run on MFMA for bf16/fp16 at 4 or more query heads per kv head (fewer
+ * heads, fp32 and head_dim 16: the vector ALU).  The small-seq varlen
+ * cross-attention case of the ROCm TransformerEngine PR (s_q = 1, s_kv <= 16,
+ * one sequence per query token) is this call with num_seqs = number of query
+ * tokens.
  *
  * out, query      [num_seqs, num_heads, head_dim] dense.
  * block_tables    int32 [num_seqs, max_blocks_per_seq] (row stride max_blocks_per_seq).
