@@ -168,8 +168,9 @@ size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  * splits, each split reduces to (partial output, max, sum) in the workspace,
  * and a log-sum-exp merge combines them.  Scores, running max and sums are
  * fp32; the probabilities are rounded to the query type for the P.V products,
- * which run on MFMA for bf16/fp16 at 4 or more query heads per kv head (fewer
- * heads, fp32 and head_dim 16: the vector ALU).  The small-seq varlen
+ * which run on MFMA or on the vector ALU depending on the shape (bf16/fp16 with
+ * several query heads per kv head mostly take MFMA; fp32 and head_dim 16 never
+ * do).  The small-seq varlen
  * cross-attention case of the ROCm TransformerEngine PR (s_q = 1, s_kv <= 16,
  * one sequence per query token) is this call with num_seqs = number of query
  * tokens.
