@@ -25,9 +25,9 @@ int heads_per_wave(int g) {
 //    stays ahead (46.2 vs 48.5 us, 48.0 vs 49.8 us).
 //  * Split mode (many short items, bound by occupancy: the matrix-core kernel allows 2
 //    waves per SIMD, the vector kernel 4): from 8 heads per wave, or 4 with an FP8 cache
-//    (whose codes the vector core widens per head group) or at head_dim 64.  Measured:
-//    1100 sequences at 4 heads 149 us (vector) against 175 us (bf16), but 119 -> 95 us
-//    over FP8.
+//    (whose codes the vector core widens per head group) or at head_dim 64.  Measured
+//    when batches beyond 1024 sequences still took split mode: 1100 sequences at 4
+//    heads 149 us (vector) against 175 us (bf16), but 119 -> 95 us over FP8.
 // Item mode, fp32 and the other shapes always take the vector core.
 template <typename T, int D>
 constexpr bool mfma_decode_type() {
@@ -54,8 +54,12 @@ bool launch_main_mfma(const DecodeParams& dp, const DecodePlan& pl, hipStream_t 
       PKV_LOG_LAUNCH("decode_stream_kernel", blocks, kDecodeThreads,
                      "core=mfma D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld", D, HPW, MS,
                      dp.nranges, (long long)dp.total_items);
-      hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, MS, true>), dim3(blocks),
-                         dim3(kDecodeThreads), 0, stream, dp);
+      if (pl.prefix)
+        hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, MS, true, true>), dim3(blocks),
+                           dim3(kDecodeThreads), 0, stream, dp);
+      else
+        hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, MS, true>), dim3(blocks),
+                           dim3(kDecodeThreads), 0, stream, dp);
       return true;
     }
     return false;
@@ -87,8 +91,12 @@ void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t strea
     PKV_LOG_LAUNCH("decode_stream_kernel", blocks, kDecodeThreads,
                    "core=vector D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld", D, HPW, NS,
                    dp.nranges, (long long)dp.total_items);
-    hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, NS>), dim3(blocks), dim3(kDecodeThreads),
-                       0, stream, dp);
+    if (pl.prefix)
+      hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, NS, false, true>), dim3(blocks),
+                         dim3(kDecodeThreads), 0, stream, dp);
+    else
+      hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, NS>), dim3(blocks), dim3(kDecodeThreads),
+                         0, stream, dp);
     return;
   }
   if constexpr (C::LPT == 8 && C::TPR == 8) {
@@ -131,10 +139,14 @@ void launch_merge(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stre
   const int blocks = (int)(((int64_t)dp.S * dp.H + kWavesPerBlock - 1) / kWavesPerBlock);
   PKV_LOG_LAUNCH(pl.stream ? "decode_merge_stream_kernel" : "decode_merge_split_kernel", blocks,
                  kDecodeThreads, "rows=%lld", (long long)dp.S * dp.H);
-  if (pl.stream)
-    hipLaunchKernelGGL((decode_merge_stream_kernel<T, D>), dim3(blocks), dim3(kDecodeThreads), 0,
-                       stream, dp);
-  else
+  if (pl.stream) {
+    if (pl.prefix)
+      hipLaunchKernelGGL((decode_merge_stream_kernel<T, D, true>), dim3(blocks),
+                         dim3(kDecodeThreads), 0, stream, dp);
+    else
+      hipLaunchKernelGGL((decode_merge_stream_kernel<T, D>), dim3(blocks), dim3(kDecodeThreads), 0,
+                         stream, dp);
+  } else
     hipLaunchKernelGGL((decode_merge_split_kernel<T, D>), dim3(blocks), dim3(kDecodeThreads), 0,
                        stream, dp);
 }
@@ -170,14 +182,19 @@ DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
   pl.max_seq_len = max_seq_len;
   pl.num_splits = max_seq_len > 0 ? (max_seq_len + split - 1) / split : 1;
   if (pl.num_splits < 1) pl.num_splits = 1;
-  // Stream mode whenever some sequence needs more than one split and the batch is small
-  // enough for every wave to scan the lengths.
-  pl.stream = pl.num_splits > 1 && num_seqs <= kStreamMaxSeqs;
+  // Stream mode whenever some sequence needs more than one split.  Up to kStreamMaxSeqs
+  // sequences every wave scans the lengths itself; beyond (not in a mixed batch) a
+  // planning kernel writes prefix sums and range starts for the waves to read.
+  pl.stream = pl.num_splits > 1 && (num_seqs <= kStreamMaxSeqs || !mixed);
+  pl.prefix = pl.stream && num_seqs > kStreamMaxSeqs;
   const int waves = mixed ? kStreamWavesMixed : kStreamWaves;
   pl.num_ranges = pl.stream ? (int)(waves / groups > 1 ? waves / groups : 1) : 0;
   const size_t slots = pl.stream ? (size_t)num_heads * pl.num_ranges * 2
                                  : (pl.num_splits > 1 ? (size_t)num_seqs * num_heads * pl.num_splits : 0);
   pl.workspace_bytes = slots * (size_t)head_dim * sizeof(float) + slots * 2 * sizeof(float);
+  if (pl.prefix)   // cu[S + 1] and rpos[ranges] (int64), rstart[ranges] (int32)
+    pl.workspace_bytes += ((size_t)num_seqs + 1 + pl.num_ranges) * sizeof(int64_t) +
+                          (size_t)pl.num_ranges * sizeof(int32_t);
   return pl;
 }
 
@@ -196,6 +213,11 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& pl, hipStream_t st
       default: launch_all<F32>(dp, pl, a.head_dim, merge, stream); break;
     }
   };
+  if (pl.prefix) {
+    PKV_LOG_LAUNCH("decode_stream_plan_kernel", 1, kPlanThreads, "seqs=%d ranges=%d",
+                   a.num_seqs, pl.num_ranges);
+    hipLaunchKernelGGL(decode_stream_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, dp);
+  }
   dispatch(false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(pl.stream || pl.num_splits > 1)) return e;

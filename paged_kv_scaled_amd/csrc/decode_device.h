@@ -22,15 +22,19 @@
 //  * probabilities of two rounds are paired and multiplied into V with dot2 as well;
 //  * at the end of a segment the lanes of a column merge their states (shuffles).
 //
-// Work decomposition (two modes, picked on the host from the sizes):
-//  * stream mode (long contexts, up to 1024 sequences): the concatenated key axis of
+// Work decomposition (picked on the host from the sizes):
+//  * stream mode (some sequence longer than one split): the concatenated key axis of
 //    all sequences is cut into `nranges` equal ranges per head group, one wave each,
 //    so every wave does the same work whatever the length mix.  A sequence that lies
 //    inside one range is finished by that wave; a range boundary inside a sequence
-//    leaves (acc, m, l) partials that the merge kernel combines;
-//  * split mode (short sequences or very large batches): fixed splits of split_len keys
-//    per sequence, waves walk (sequence, split, head group) items in a grid-stride loop;
-//    sequences with one split are written directly.
+//    leaves (acc, m, l) partials that the merge kernel combines.  Up to kStreamMaxSeqs
+//    sequences each wave finds its range's first sequence by scanning the lengths;
+//    beyond, a one-block planning kernel writes the length prefix sums and every range's
+//    first sequence into the workspace, and the waves read them;
+//  * split mode (every sequence within one split, or the generation rows of a mixed
+//    batch beyond kStreamMaxSeqs): fixed splits of split_len keys per sequence, waves
+//    walk (sequence, split, head group) items in a grid-stride loop; sequences with one
+//    split are written directly.
 #pragma once
 
 #include "common.h"
@@ -43,7 +47,7 @@ namespace {
 constexpr int kDecodeThreads = 256;
 constexpr int kWavesPerBlock = kDecodeThreads / kWave;
 constexpr float kLazyRescale = 8.0f;   // log2 units
-constexpr int kStreamMaxSeqs = 1024;   // stream mode scans seq_lens in every wave
+constexpr int kStreamMaxSeqs = 1024;   // up to here every stream wave scans seq_lens
 constexpr int kStreamWaves = 1024;     // waves of the stream grid (all head groups): one wave
                                        // per SIMD on 256 CUs
 constexpr int kStreamWavesMixed = 2048;   // the same inside the mixed-batch kernel, whose
@@ -104,6 +108,11 @@ struct DecodeParams {
   const uint32_t* guard;    // device error word when device checks are on, else null
   void* weights;            // small-seq training forward: [S, H, max_kv] attention weights
   int32_t max_kv;
+  // prefix stream mode (workspace, after the partials): cu[s] = keys of sequences < s
+  // (cu[S] = total), and for range r its first sequence rstart[r] starting at rpos[r]
+  int64_t* cu;
+  int64_t* rpos;
+  int32_t* rstart;
 };
 
 template <typename T, int D>
@@ -763,7 +772,9 @@ __device__ __forceinline__ void stream_locate(const DecodeParams& p, int64_t x, 
 
 // One stream-mode item (head group, key range), walked by the calling wave (MF: on the
 // matrix-core core of decode_mfma.h).
-template <typename T, int D, int HPW, int NSTEP, bool MF = false>
+// PFX: the batch has more sequences than a wave scans; the planning kernel's prefix sums
+// and range starts in the workspace take the place of the scans.
+template <typename T, int D, int HPW, int NSTEP, bool MF = false, bool PFX = false>
 __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item) {
   using C = DecodeShape<T, D>;
   const int lane = threadIdx.x & (kWave - 1);
@@ -771,8 +782,14 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item)
   const int HG = p.Hkv * p.groups_per_kv;
   const int hg = (int)(item % HG);
   const int r = (int)(item / HG);
-  const int len0 = lane < p.S ? p.seq_lens[lane] : 0;
-  const int64_t total = stream_total(p, lane, len0);
+  int len0 = 0;
+  int64_t total;
+  if constexpr (PFX) {
+    total = p.cu[p.S];
+  } else {
+    len0 = lane < p.S ? p.seq_lens[lane] : 0;
+    total = stream_total(p, lane, len0);
+  }
   const int64_t R = stream_range_len(total, p.nranges);
   const int64_t lo = (int64_t)r * R;
   const int64_t hi = min(total, lo + R);
@@ -782,7 +799,12 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item)
   const int nh = min(HPW, p.g - sub * HPW);
   int s;
   int64_t P;
-  stream_locate(p, lo, lane, len0, s, P);
+  if constexpr (PFX) {
+    s = p.rstart[r];
+    P = p.rpos[r];
+  } else {
+    stream_locate(p, lo, lane, len0, s, P);
+  }
   bool first = true;
   for (; s < p.S && P < hi; ++s) {
     const int L = p.seq_lens[s];
@@ -815,13 +837,63 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item)
   }
 }
 
-template <typename T, int D, int HPW, int NSTEP, bool MF = false>
+template <typename T, int D, int HPW, int NSTEP, bool MF = false, bool PFX = false>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_stream_kernel(const DecodeParams p) {
   if (guard_tripped(p.guard)) return;
   const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
   if (wave >= p.total_items) return;
-  stream_item<T, D, HPW, NSTEP, MF>(p, wave);
+  stream_item<T, D, HPW, NSTEP, MF, PFX>(p, wave);
+}
+
+// Prefix stream mode, one block before the stream kernel: cu = exclusive prefix sums of
+// the lengths (cu[S] = total), then for every range r the first sequence whose keys reach
+// past its start r * R (empty sequences before it skipped) and where that sequence starts.
+constexpr int kPlanThreads = 1024;
+
+__global__ void __launch_bounds__(kPlanThreads)
+decode_stream_plan_kernel(const DecodeParams p) {
+  if (guard_tripped(p.guard)) return;
+  constexpr int NW = kPlanThreads / kWave;
+  __shared__ int64_t s_wave[NW];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  int64_t carry = 0;
+  for (int c0 = 0; c0 < p.S; c0 += kPlanThreads) {
+    const int i = c0 + tid;
+    int64_t v = i < p.S ? (int64_t)p.seq_lens[i] : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int64_t y = __shfl_up(v, off, kWave);
+      if (lane >= off) v += y;
+    }
+    if (lane == kWave - 1) s_wave[w] = v;
+    __syncthreads();
+    int64_t before = 0, chunk = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int64_t x = s_wave[k];
+      before += k < w ? x : 0;
+      chunk += x;
+    }
+    if (i < p.S) p.cu[i + 1] = carry + before + v;
+    carry += chunk;
+    __syncthreads();                 // s_wave is rewritten by the next chunk
+  }
+  if (tid == 0) p.cu[0] = 0;
+  __threadfence_block();
+  __syncthreads();                   // cu complete and visible to the block
+  const int64_t R = stream_range_len(carry, p.nranges);
+  for (int r = tid; r < p.nranges; r += kPlanThreads) {
+    const int64_t x = (int64_t)r * R;
+    // smallest s with cu[s + 1] > x (S when the range is empty)
+    int a = 0, b = p.S;
+    while (a < b) {
+      const int mid = (a + b) >> 1;
+      if (p.cu[mid + 1] > x) b = mid; else a = mid + 1;
+    }
+    p.rstart[r] = a;
+    p.rpos[r] = p.cu[min(a, p.S)];
+  }
 }
 
 // ---- merge -----------------------------------------------------------------------------
@@ -920,7 +992,7 @@ decode_merge_split_kernel(const DecodeParams p) {
 // by the stream kernel; empty sequences get zeros; the others combine one partial per
 // range they touch (the first range's partial is its second slot unless the sequence
 // starts exactly at that range's start).
-template <typename T, int D>
+template <typename T, int D, bool PFX = false>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_merge_stream_kernel(const DecodeParams p) {
   if (guard_tripped(p.guard)) return;
@@ -937,19 +1009,25 @@ decode_merge_stream_kernel(const DecodeParams p) {
     store_row<T, D>(p, sh, lane, zero, 0.f);
     return;
   }
-  // one pass over the lengths: the batch total and the start P of sequence s
+  // the batch total and the start P of sequence s: from the planning kernel's prefix
+  // sums, or one pass over the lengths
   int64_t total = 0, P = 0;
-  for (int c0 = 0; c0 < p.S; c0 += kWave) {
-    const int x = (c0 + lane < p.S) ? p.seq_lens[c0 + lane] : 0;
-    int before = (c0 + lane < s) ? x : 0;
-    int all = x;
+  if constexpr (PFX) {
+    total = p.cu[p.S];
+    P = p.cu[s];
+  } else {
+    for (int c0 = 0; c0 < p.S; c0 += kWave) {
+      const int x = (c0 + lane < p.S) ? p.seq_lens[c0 + lane] : 0;
+      int before = (c0 + lane < s) ? x : 0;
+      int all = x;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      all += __shfl_xor(all, off, kWave);
-      before += __shfl_xor(before, off, kWave);
+      for (int off = 1; off < kWave; off <<= 1) {
+        all += __shfl_xor(all, off, kWave);
+        before += __shfl_xor(before, off, kWave);
+      }
+      total += all;
+      P += before;
     }
-    total += all;
-    P += before;
   }
   const int64_t R = stream_range_len(total, p.nranges);
   const int64_t r0 = P / R, r1 = (P + L - 1) / R;
@@ -984,8 +1062,17 @@ inline DecodeParams decode_params(const AttnArgs& a, const DecodePlan& pl) {
   dp.out_scale = a.kv_fp8 ? a.v_scale : 1.f;
   dp.guard = a.guard;
   const size_t slots = pl.workspace_bytes / ((size_t)(a.head_dim + 2) * sizeof(float));
+  // partial slots (the prefix mode's tables follow them in the workspace)
+  const size_t nslots = pl.prefix ? (size_t)a.num_heads * pl.num_ranges * 2 : slots;
   dp.ws_acc = pl.workspace_bytes ? reinterpret_cast<float*>(a.workspace) : nullptr;
-  dp.ws_ml = pl.workspace_bytes ? dp.ws_acc + slots * a.head_dim : nullptr;
+  dp.ws_ml = pl.workspace_bytes ? dp.ws_acc + nslots * a.head_dim : nullptr;
+  if (pl.prefix) {
+    // after the partials (a multiple of 8 bytes: the slot count is even)
+    uint8_t* base = reinterpret_cast<uint8_t*>(dp.ws_ml + nslots * 2);
+    dp.cu = reinterpret_cast<int64_t*>(base);
+    dp.rpos = dp.cu + (a.num_seqs + 1);
+    dp.rstart = reinterpret_cast<int32_t*>(dp.rpos + pl.num_ranges);
+  }
   const int64_t groups = (int64_t)a.num_kv_heads * pl.groups_per_kv;
   dp.total_items = pl.stream ? groups * pl.num_ranges : (int64_t)a.num_seqs * pl.num_splits * groups;
   return dp;

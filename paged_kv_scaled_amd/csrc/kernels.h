@@ -96,6 +96,9 @@ struct DecodePlan {
   int split_len;        // keys per split (split mode)
   int num_splits;       // splits of the longest sequence (split mode)
   bool stream;          // equal ranges of the concatenated key axis instead of splits
+  bool prefix;          // stream mode over more sequences than a wave can scan: a planning
+                        // kernel first writes the length prefix sums and every range's
+                        // first sequence into the workspace
   int num_ranges;       // ranges per head group (stream mode)
   int max_seq_len;
   size_t workspace_bytes;

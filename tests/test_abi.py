@@ -103,8 +103,11 @@ def test_decode_workspace_size_plan(lib):
     # stream mode: 1024 waves over 8 wave groups (4 heads a wave) = 128 key ranges;
     # 32 heads x 128 ranges x 2 partial slots x (128 + 2) floats
     assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 4096) == 32 * 128 * 2 * 130 * 4
-    # split mode beyond 1024 sequences: splits grow to 64 blocks (1024 keys), 5 of them
-    assert lib.pkv_decode_workspace_size(2000, 8, 8, 128, 16, 5000) == 2000 * 8 * 5 * 130 * 4
+    # beyond 1024 sequences stream mode adds the planning tables: 128 ranges (1024 waves,
+    # 8 wave groups), partials 8 heads x 128 x 2 slots, then int64 cu[S + 1], int64
+    # rpos[128], int32 rstart[128]
+    assert lib.pkv_decode_workspace_size(2000, 8, 8, 128, 16, 5000) == \
+        8 * 128 * 2 * 130 * 4 + (2000 + 1 + 128) * 8 + 128 * 4
     assert lib.pkv_decode_workspace_size(2000, 8, 8, 128, 16, 300) == 0
     assert lib.pkv_decode_workspace_size(64, 30, 8, 128, 16, 4096) == 0    # invalid -> 0
     assert lib.pkv_decode_workspace_size(1, 8, 8, 128, 16, 131072) > 0

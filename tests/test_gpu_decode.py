@@ -233,10 +233,10 @@ def test_decode_item_mode(gpu, H, Hkv, dtype, head_dim):
     compare(got[live], want, dtype, f"item_mode H{H} Hkv{Hkv}")
 
 
-def test_decode_split_mode_with_merge(gpu):
-    """More than 1024 sequences with contexts past one split: split mode (per-sequence
-    splits of 256 keys, partials in the workspace, the split merge kernel); rows of every
-    split count are checked."""
+def test_decode_prefix_stream_mode(gpu):
+    """More than 1024 sequences with contexts past one split: stream mode with the planning
+    kernel (prefix sums and range starts in the workspace), partials and the stream
+    merge; sequences spanning range boundaries and ranges spanning many sequences."""
     rng = np.random.default_rng(81)
     lens = rng.integers(1, 900, size=1100).astype(np.int32)
     lens[:4] = [256, 257, 512, 899]
@@ -244,6 +244,52 @@ def test_decode_split_mode_with_merge(gpu):
                  wl.MASK_NONE, decode=True)
     need = B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
                                    w.block_size, w.max_seq_len)
-    assert need > 0                                   # split mode keeps partials
+    assert need > 0                                   # partials and planning tables
     rows = np.unique(np.concatenate([np.arange(8), rng.choice(len(lens), 200, replace=False)]))
     _run(w, rows=rows)
+
+
+@pytest.mark.parametrize("H", [8, 32])
+def test_decode_prefix_stream_empty_sequences(gpu, H):
+    """1200 sequences, some empty (first, last and scattered), 8 kv heads at 1 and 4
+    query heads per kv head (vector and matrix-core cores): empty rows are zero, the
+    others match the oracle."""
+    rng = np.random.default_rng(83)
+    S, Hkv, D = 1200, 8, 128
+    lens = rng.integers(1, 700, size=S).astype(np.int32)
+    lens[[0, 5, 6, 500, S - 2, S - 1]] = 0
+    w = wl.build("prefix_empty", 83, "bf16", lens, np.minimum(lens, 1), H, Hkv, D, 16,
+                 wl.MASK_NONE, decode=True)
+    # the generator gives empty sequences no query row: one per sequence ([S, H, D])
+    q = wl.round_to_storage(rng.standard_normal((S, H, D)).astype(np.float32), "bf16")
+    w.query = q
+    w.q_lens = np.ones(S, np.int32)
+    w.cu_seqlens_q = np.arange(S + 1, dtype=np.int32)
+    d = Dev(w)
+    B.kv_cache_write(d.key, d.value, d.slots, d.kc, d.vc)
+    out = d.decode()
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    empty = np.flatnonzero(lens == 0)
+    assert np.all(got[empty] == 0)
+    live = np.sort(np.concatenate([[1, 4, 7, 499, 501, S - 3],
+                                   rng.choice(np.flatnonzero(lens > 0), 60, replace=False)]))
+    live = np.unique(live)
+    keys = ref.split_logical(ref.widen(w.key, "bf16"), w.cu_seq_lens)
+    vals = ref.split_logical(ref.widen(w.value, "bf16"), w.cu_seq_lens)
+    want, _ = ref.paged_attention(ref.widen(q[live], "bf16"), [keys[i] for i in live],
+                                  [vals[i] for i in live], np.arange(len(live) + 1, dtype=np.int32),
+                                  lens[live], Hkv, w.scale, wl.MASK_NONE)
+    compare(got[live], want, "bf16", f"prefix_empty H{H}")
+
+
+def test_decode_one_split_mode(gpu):
+    """Every sequence fits one split (at most 256 keys) but some exceed the 8 pages of
+    item mode: the split kernel with one split per sequence, written directly."""
+    lens = np.random.default_rng(84).integers(1, 257, size=300).astype(np.int32)
+    lens[:3] = [256, 129, 1]
+    w = wl.build("one_split", 84, "bf16", lens, np.ones(len(lens), np.int32), 32, 8, 128, 16,
+                 wl.MASK_NONE, decode=True)
+    assert B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                   w.block_size, w.max_seq_len) == 0
+    _run(w)

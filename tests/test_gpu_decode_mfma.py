@@ -77,8 +77,8 @@ def test_mfma_small_pages_take_vector_core(gpu):
     _run(_batch("mfma_bs4", 64, "bf16", lens, 16, 2, 128, bs=4))
 
 
-def test_mfma_split_mode(gpu):
-    """More than 1024 sequences: split mode (256-key splits, partials, split merge)."""
+def test_mfma_prefix_stream(gpu):
+    """More than 1024 sequences: stream mode with the planning kernel's tables."""
     rng = np.random.default_rng(65)
     lens = rng.integers(1, 900, size=1100).astype(np.int32)
     w = _batch("mfma_split", 65, "f16", lens, 16, 2, 128)
@@ -86,13 +86,22 @@ def test_mfma_split_mode(gpu):
     _run(w, rows=rows)
 
 
-def test_mfma_split_mode_d64_g4(gpu):
-    """Split mode at head_dim 64 and 4 heads per wave (bf16), the other matrix-core shape."""
+def test_mfma_prefix_stream_d64_g4(gpu):
+    """More than 1024 sequences at head_dim 64 and 4 heads per wave (bf16)."""
     rng = np.random.default_rng(71)
     lens = rng.integers(1, 1200, size=1030).astype(np.int32)
     w = _batch("mfma_split_d64", 71, "bf16", lens, 32, 8, 64)
     rows = np.unique(np.concatenate([np.arange(6), rng.choice(len(lens), 120, replace=False)]))
     _run(w, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_mfma_one_split_mode(gpu, dtype):
+    """Split mode on the matrix cores: every sequence within one 256-key split, some past
+    the 8 pages of item mode, 8 heads per wave."""
+    lens = np.random.default_rng(72).integers(1, 257, size=200).astype(np.int32)
+    lens[:3] = [256, 129, 1]
+    _run(_batch("mfma_one_split", 72, dtype, lens, 64, 8, 128))
 
 
 def test_mfma_empty_and_tiny_sequences(gpu):

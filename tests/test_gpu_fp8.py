@@ -128,8 +128,9 @@ def test_fp8_decode_item_mode(gpu):
     _decode(wl.with_fp8_cache(w))
 
 
-def test_fp8_decode_split_mode(gpu):
-    """More than 1024 sequences with contexts past one split: split mode and its merge."""
+def test_fp8_decode_prefix_stream(gpu):
+    """More than 1024 sequences with contexts past one split: stream mode with the
+    planning kernel's tables and the stream merge."""
     rng = np.random.default_rng(38)
     lens = rng.integers(1, 900, size=1100).astype(np.int32)
     w = wl.build("split_fp8", 38, "f16", lens, np.ones(len(lens), np.int32), 8, 2, 128, 16,
