@@ -1001,23 +1001,19 @@ decode_merge_stream_kernel(const DecodeParams p) {
   const int64_t sh = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
   if (sh >= (int64_t)p.S * p.H) return;
   const int s = (int)(sh / p.H), h = (int)(sh % p.H);
-  const int L = p.seq_lens[s];
-  if (L == 0) {
-    float zero[DPL];
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) zero[i] = 0.f;
-    store_row<T, D>(p, sh, lane, zero, 0.f);
-    return;
-  }
-  // the batch total and the start P of sequence s: from the planning kernel's prefix
-  // sums, or one pass over the lengths
+  // the length L of sequence s, the batch total and the start P of sequence s, all from
+  // one round of loads: the planning kernel's prefix sums, or one pass over the lengths
+  // (L taken from the pass itself)
   int64_t total = 0, P = 0;
+  int L = 0;
   if constexpr (PFX) {
+    L = p.seq_lens[s];
     total = p.cu[p.S];
     P = p.cu[s];
   } else {
     for (int c0 = 0; c0 < p.S; c0 += kWave) {
       const int x = (c0 + lane < p.S) ? p.seq_lens[c0 + lane] : 0;
+      if (c0 == (s & ~(kWave - 1))) L = __shfl(x, s & (kWave - 1), kWave);
       int before = (c0 + lane < s) ? x : 0;
       int all = x;
 #pragma unroll
@@ -1028,6 +1024,13 @@ decode_merge_stream_kernel(const DecodeParams p) {
       total += all;
       P += before;
     }
+  }
+  if (L == 0) {
+    float zero[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) zero[i] = 0.f;
+    store_row<T, D>(p, sh, lane, zero, 0.f);
+    return;
   }
   const int64_t R = stream_range_len(total, p.nranges);
   const int64_t r0 = P / R, r1 = (P + L - 1) / R;
