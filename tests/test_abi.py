@@ -97,6 +97,22 @@ def test_decode_rejections(lib):
     assert _decode(lib, S=0) == B.PKV_OK
 
 
+def test_decode_workspace_prefix_tables(lib):
+    """Stream mode beyond 1024 sequences adds the planning tables (int64 prefix sums per
+    sequence plus one, int64 start and int32 first sequence per range); 1024 sequences
+    scan without them; the generation rows of a mixed batch never use them (split mode
+    beyond 1024 sequences there)."""
+    part = 8 * 128 * 2 * 130 * 4            # 8 heads x 128 ranges x 2 slots x (D + 2) floats
+    assert lib.pkv_decode_workspace_size(1024, 8, 8, 128, 16, 5000) == part
+    assert lib.pkv_decode_workspace_size(1025, 8, 8, 128, 16, 5000) == \
+        part + (1025 + 1 + 128) * 8 + 128 * 4
+    # all sequences within one split: no partials, no tables, whatever the batch size
+    assert lib.pkv_decode_workspace_size(5000, 8, 8, 128, 16, 256) == 0
+    # mixed batch, 1500 generation sequences: split-mode partials only (5 splits of 1024)
+    mixed = lib.pkv_mixed_workspace_size(1500, 8, 8, 128, 16, 5000)
+    assert mixed > 0 and mixed % (130 * 4) == 0
+
+
 def test_decode_workspace_size_plan(lib):
     # one split per sequence -> no workspace
     assert lib.pkv_decode_workspace_size(30720, 16, 16, 128, 16, 16) == 0

@@ -293,3 +293,21 @@ def test_decode_one_split_mode(gpu):
     assert B.decode_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
                                    w.block_size, w.max_seq_len) == 0
     _run(w)
+
+
+@pytest.mark.parametrize("case", ["f16_bs8", "bf16_d64", "fp8", "f32"])
+def test_decode_prefix_stream_variants(gpu, case):
+    """Stream mode with the planning kernel across the other shapes: fp16 on pages of 8,
+    head_dim 64, an FP8 cache, fp32 (vector core): sampled rows against the oracle."""
+    rng = np.random.default_rng(85)
+    S = 1100
+    lens = rng.integers(1, 800, size=S).astype(np.int32)
+    dtype = {"f16_bs8": "f16", "bf16_d64": "bf16", "fp8": "bf16", "f32": "f32"}[case]
+    D = 64 if case == "bf16_d64" else 128
+    bs = 8 if case == "f16_bs8" else 16
+    w = wl.build(f"prefix_{case}", 85, dtype, lens, np.ones(S, np.int32), 16, 4, D, bs,
+                 wl.MASK_NONE, decode=True)
+    if case == "fp8":
+        w = wl.with_fp8_cache(w)
+    rows = np.unique(np.concatenate([np.arange(4), [S - 1], rng.choice(S, 100, replace=False)]))
+    _run(w, rows=rows)
