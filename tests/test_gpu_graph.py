@@ -17,7 +17,19 @@ pytestmark = pytest.mark.gpu
 
 
 def test_decode_step_replays_bit_exactly(gpu):
-    w = wl.decode_batch(seed=90, num_seqs=16, lo=200, hi=3000)
+    _replay_decode_step(wl.decode_batch(seed=90, num_seqs=16, lo=200, hi=3000))
+
+
+def test_decode_prefix_stream_step_replays_bit_exactly(gpu):
+    """More than 1024 sequences: the planning kernel is captured with the stream kernel
+    and the merge."""
+    lens = np.random.default_rng(92).integers(10, 600, size=1100).astype(np.int32)
+    w = wl.build("graph_prefix", 92, "bf16", lens, np.ones(len(lens), np.int32), 8, 2, 128, 16,
+                 wl.MASK_NONE, decode=True)
+    _replay_decode_step(w)
+
+
+def _replay_decode_step(w):
     d = Dev(w, fill="zero")
     ctx = torch.from_numpy(w.context_rows()).cuda()
     B.kv_cache_write(d.key[ctx], d.value[ctx], d.slots[ctx], d.kc, d.vc)
