@@ -97,6 +97,16 @@ def test_decode_rejections(lib):
     assert _decode(lib, S=0) == B.PKV_OK
 
 
+def test_decode_rejects_workspace_without_prefix_tables(lib):
+    """Beyond 1024 sequences a workspace sized for the partials alone is too small: the
+    call fails on the host, before any launch."""
+    part = 32 * 128 * 2 * 130 * 4           # the 1024-sequence size (no tables)
+    need = lib.pkv_decode_workspace_size(2000, 32, 8, 128, 16, 4096)
+    assert need == part + (2000 + 1 + 128) * 8 + 128 * 4
+    assert _decode(lib, S=2000, wsb=part) == B.PKV_ERR_WORKSPACE
+    assert "workspace" in B.last_error()
+
+
 def test_decode_workspace_prefix_tables(lib):
     """Stream mode beyond 1024 sequences adds the planning tables (int64 prefix sums per
     sequence plus one, int64 start and int32 first sequence per range); 1024 sequences
