@@ -154,7 +154,7 @@ int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_le
 /*
  * pkv_decode_workspace_size -- bytes of device workspace pkv_paged_attention_decode
  * needs for these sizes (0 when every sequence fits one split): fp32 partial
- * (output, max, sum) slots, plus, beyond 1024 sequences, the tables a planning
+ * (output, max, sum) slots, plus, beyond 256 sequences, the tables a planning
  * kernel writes (8 bytes per sequence and 20 per key range).  The caller
  * allocates it ahead of time (ROCm TransformerEngine small-seq PR: workspace
  * and aux buffers are pre-allocated from host max sequence lengths).

@@ -27,10 +27,11 @@
 //    all sequences is cut into `nranges` equal ranges per head group, one wave each,
 //    so every wave does the same work whatever the length mix.  A sequence that lies
 //    inside one range is finished by that wave; a range boundary inside a sequence
-//    leaves (acc, m, l) partials that the merge kernel combines.  Up to kStreamMaxSeqs
+//    leaves (acc, m, l) partials that the merge kernel combines.  Up to kStreamScanSeqs
 //    sequences each wave finds its range's first sequence by scanning the lengths;
 //    beyond, a one-block planning kernel writes the length prefix sums and every range's
-//    first sequence into the workspace, and the waves read them;
+//    first sequence into the workspace, and the waves read them (a mixed batch, which
+//    has no room for the planning launch, scans up to kStreamMaxSeqs);
 //  * split mode (every sequence within one split, or the generation rows of a mixed
 //    batch beyond kStreamMaxSeqs): fixed splits of split_len keys per sequence, waves
 //    walk (sequence, split, head group) items in a grid-stride loop; sequences with one
@@ -47,7 +48,10 @@ namespace {
 constexpr int kDecodeThreads = 256;
 constexpr int kWavesPerBlock = kDecodeThreads / kWave;
 constexpr float kLazyRescale = 8.0f;   // log2 units
-constexpr int kStreamMaxSeqs = 1024;   // up to here every stream wave scans seq_lens
+constexpr int kStreamScanSeqs = 256;   // plain decode: up to here every stream wave scans
+                                       // seq_lens, beyond the planning kernel's tables
+constexpr int kStreamMaxSeqs = 1024;   // mixed batch (no planning kernel): stream mode up to
+                                       // here, scanned by every wave; split mode beyond
 constexpr int kStreamWaves = 1024;     // waves of the stream grid (all head groups): one wave
                                        // per SIMD on 256 CUs
 constexpr int kStreamWavesMixed = 2048;   // the same inside the mixed-batch kernel, whose

@@ -98,9 +98,9 @@ def test_decode_rejections(lib):
 
 
 def test_decode_rejects_workspace_without_prefix_tables(lib):
-    """Beyond 1024 sequences a workspace sized for the partials alone is too small: the
+    """Beyond 256 sequences a workspace sized for the partials alone is too small: the
     call fails on the host, before any launch."""
-    part = 32 * 128 * 2 * 130 * 4           # the 1024-sequence size (no tables)
+    part = 32 * 128 * 2 * 130 * 4           # the partials (what 256 sequences need)
     need = lib.pkv_decode_workspace_size(2000, 32, 8, 128, 16, 4096)
     assert need == part + (2000 + 1 + 128) * 8 + 128 * 4
     assert _decode(lib, S=2000, wsb=part) == B.PKV_ERR_WORKSPACE
@@ -108,14 +108,18 @@ def test_decode_rejects_workspace_without_prefix_tables(lib):
 
 
 def test_decode_workspace_prefix_tables(lib):
-    """Stream mode beyond 1024 sequences adds the planning tables (int64 prefix sums per
-    sequence plus one, int64 start and int32 first sequence per range); 1024 sequences
-    scan without them; the generation rows of a mixed batch never use them (split mode
-    beyond 1024 sequences there)."""
+    """Stream mode beyond 256 sequences adds the planning tables (int64 prefix sums per
+    sequence plus one, int64 start and int32 first sequence per range); 256 sequences
+    scan without them; the generation rows of a mixed batch never use them (they scan up
+    to 1024 sequences and take split mode beyond)."""
     part = 8 * 128 * 2 * 130 * 4            # 8 heads x 128 ranges x 2 slots x (D + 2) floats
-    assert lib.pkv_decode_workspace_size(1024, 8, 8, 128, 16, 5000) == part
+    assert lib.pkv_decode_workspace_size(256, 8, 8, 128, 16, 5000) == part
+    assert lib.pkv_decode_workspace_size(257, 8, 8, 128, 16, 5000) == \
+        part + (257 + 1 + 128) * 8 + 128 * 4
     assert lib.pkv_decode_workspace_size(1025, 8, 8, 128, 16, 5000) == \
         part + (1025 + 1 + 128) * 8 + 128 * 4
+    # mixed batch, 1000 generation sequences: stream partials (2048 ranges), no tables
+    assert lib.pkv_mixed_workspace_size(1000, 8, 8, 128, 16, 5000) == 8 * 256 * 2 * 130 * 4
     # all sequences within one split: no partials, no tables, whatever the batch size
     assert lib.pkv_decode_workspace_size(5000, 8, 8, 128, 16, 256) == 0
     # mixed batch, 1500 generation sequences: split-mode partials only (5 splits of 1024)

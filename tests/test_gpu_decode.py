@@ -311,3 +311,14 @@ def test_decode_prefix_stream_variants(gpu, case):
         w = wl.with_fp8_cache(w)
     rows = np.unique(np.concatenate([np.arange(4), [S - 1], rng.choice(S, 100, replace=False)]))
     _run(w, rows=rows)
+
+
+def test_decode_prefix_stream_mid_batch(gpu):
+    """400 sequences of up to 3000 keys (32 q / 8 kv heads, bf16): past the 256 sequences a
+    wave scans, so the planning kernel's tables serve them."""
+    rng = np.random.default_rng(86)
+    lens = rng.integers(1, 3000, size=400).astype(np.int32)
+    w = wl.build("prefix_mid", 86, "bf16", lens, np.ones(len(lens), np.int32), 32, 8, 128, 16,
+                 wl.MASK_NONE, decode=True)
+    rows = np.unique(np.concatenate([np.arange(4), [399], rng.choice(400, 60, replace=False)]))
+    _run(w, rows=rows)
