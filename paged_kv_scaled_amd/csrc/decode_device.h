@@ -923,11 +923,15 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int64_t sh, int
 
 // Combine the n partials (acc, m, l) of one head with the log-sum-exp rule: slot0 for
 // partial 0, slot1 + (j - 1) * slot_step for partial j > 0.  The partials are taken in
-// batches of kMergeBatch whose (m, l) pairs and accumulator rows are all loaded before any
-// is used; the running max moves between batches with a rescale of the sums.
+// batches of MB whose (m, l) pairs and accumulator rows are all loaded before any is used;
+// the running max moves between batches with a rescale of the sums.  Batches of 8 hold
+// the usual two or three partials of a head in one round of loads; batches of 32 (a
+// stream-mode batch of few sequences, where one sequence spans dozens of ranges) cut the
+// dependent load rounds of a long sequence by 4 at the cost of more registers.
 constexpr int kMergeBatch = 8;
+constexpr int kMergeBatchWide = 32;
 
-template <typename T, int D>
+template <typename T, int D, int MB = kMergeBatch>
 __device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, int h,
                                             int64_t slots_per_head, int n, int lane,
                                             int64_t slot0, int64_t slot1, int64_t slot_step) {
@@ -938,15 +942,15 @@ __device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, i
   float M = -INFINITY, den = 0.f, num[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) num[i] = 0.f;
-  for (int j0 = 0; j0 < n; j0 += kMergeBatch) {
-    const int cnt = min(kMergeBatch, n - j0);
+  for (int j0 = 0; j0 < n; j0 += MB) {
+    const int cnt = min(MB, n - j0);
     // lane k < cnt: (m, l) of partial j0 + k; every lane: its dims of each row (rows past
     // cnt re-read the last one and get weight 0)
     const int64_t my = slot_of(j0 + min(lane, cnt - 1));
     float mj = p.ws_ml[my * 2], lj = p.ws_ml[my * 2 + 1];
-    float acc[kMergeBatch][DPL];
+    float acc[MB][DPL];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
+    for (int k = 0; k < MB; ++k) {
       const float* row = p.ws_acc + slot_of(j0 + min(k, cnt - 1)) * D;
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
@@ -965,7 +969,7 @@ __device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, i
 #pragma unroll
     for (int i = 0; i < DPL; ++i) num[i] *= alpha;
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
+    for (int k = 0; k < MB; ++k) {
       const float wk = __shfl(w, k, kWave);
 #pragma unroll
       for (int i = 0; i < DPL; ++i) num[i] += wk * acc[k][i];
@@ -996,7 +1000,7 @@ decode_merge_split_kernel(const DecodeParams p) {
 // by the stream kernel; empty sequences get zeros; the others combine one partial per
 // range they touch (the first range's partial is its second slot unless the sequence
 // starts exactly at that range's start).
-template <typename T, int D, bool PFX = false>
+template <typename T, int D, bool PFX = false, int MB = kMergeBatch>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_merge_stream_kernel(const DecodeParams p) {
   if (guard_tripped(p.guard)) return;
@@ -1040,8 +1044,8 @@ decode_merge_stream_kernel(const DecodeParams p) {
   const int64_t r0 = P / R, r1 = (P + L - 1) / R;
   if (r0 == r1) return;
   const int64_t slot0 = r0 * 2 + ((r0 * R < P) ? 1 : 0);
-  merge_slots<T, D>(p, sh, h, (int64_t)p.nranges * 2, (int)(r1 - r0 + 1), lane, slot0,
-                    (r0 + 1) * 2, 2);
+  merge_slots<T, D, MB>(p, sh, h, (int64_t)p.nranges * 2, (int)(r1 - r0 + 1), lane, slot0,
+                        (r0 + 1) * 2, 2);
 }
 
 // ---- host: kernel parameters from the call's arguments and plan --------------------------

@@ -158,3 +158,20 @@ def test_mfma_fp8_g8(gpu):
     for D in (128, 64):
         lens = np.random.default_rng(69).integers(1, 3000, size=10)
         _run(wl.with_fp8_cache(_batch("mfma_fp8_g8", 69, "bf16", lens, 64, 8, D)))
+
+
+@pytest.mark.parametrize("case", ["bf16_one_long", "f16_d64_four", "fp8_two", "f32_mha_one"])
+def test_wide_merge_few_sequences(gpu, case):
+    """Few long sequences in stream mode: every head merges dozens of partials, 32 to a
+    load round (the running max moves between rounds), also past a partial round."""
+    rng = np.random.default_rng(73)
+    if case == "bf16_one_long":
+        w = _batch("wide_one", 73, "bf16", [41000], 64, 8, 128)
+    elif case == "f16_d64_four":
+        w = _batch("wide_four", 74, "f16", [9000, 1, 20000, 777], 32, 8, 64)
+    elif case == "fp8_two":
+        w = wl.with_fp8_cache(_batch("wide_fp8", 75, "bf16", [30000, 12345], 64, 8, 128))
+    else:
+        w = _batch("wide_mha", 76, "f32", [int(rng.integers(20000, 30000))], 16, 16, 128)
+    w.scale = 1.5 * w.scale
+    _run(w)

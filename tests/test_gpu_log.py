@@ -35,6 +35,8 @@ def test_launch_log_names_the_chosen_kernels(gpu, capfd):
                      "kv_scatter_kernel", "prefill_mfma_kernel"], lines
     # the decode batch shape (4 heads per wave, bf16, stream mode) runs on the matrix cores
     assert re.search(r"decode_stream_kernel grid=\d+ block=256 core=mfma D=128 heads_per_wave=4", err)
+    # 8 sequences over 128 ranges per head group: 16 ranges per sequence, the wide merge
+    assert re.search(r"decode_merge_stream_kernel grid=\d+ block=256 rows=256 batch=32", err)
     assert re.search(r"prefill_mfma_kernel grid=\d+ block=512 D=128 heads_per_wg=4 rows_per_wg=64", err)
     # switched off: nothing more
     d.decode()
