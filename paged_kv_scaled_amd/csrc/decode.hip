@@ -136,15 +136,18 @@ void launch_hpw(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream
 
 template <typename T, int D>
 void launch_merge(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream) {
+  if (pl.wide_merge) {
+    const int rows = dp.S * dp.H;
+    PKV_LOG_LAUNCH("decode_merge_stream_wide_kernel", rows, kDecodeThreads, "rows=%d", rows);
+    hipLaunchKernelGGL((decode_merge_stream_wide_kernel<T, D>), dim3(rows), dim3(kDecodeThreads),
+                       0, stream, dp);
+    return;
+  }
   const int blocks = (int)(((int64_t)dp.S * dp.H + kWavesPerBlock - 1) / kWavesPerBlock);
   PKV_LOG_LAUNCH(pl.stream ? "decode_merge_stream_kernel" : "decode_merge_split_kernel", blocks,
-                 kDecodeThreads, "rows=%lld batch=%d", (long long)dp.S * dp.H,
-                 pl.wide_merge ? kMergeBatchWide : kMergeBatch);
+                 kDecodeThreads, "rows=%lld", (long long)dp.S * dp.H);
   if (pl.stream) {
-    if (pl.wide_merge)
-      hipLaunchKernelGGL((decode_merge_stream_kernel<T, D, false, kMergeBatchWide>), dim3(blocks),
-                         dim3(kDecodeThreads), 0, stream, dp);
-    else if (pl.prefix)
+    if (pl.prefix)
       hipLaunchKernelGGL((decode_merge_stream_kernel<T, D, true>), dim3(blocks),
                          dim3(kDecodeThreads), 0, stream, dp);
     else
@@ -197,10 +200,7 @@ DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
   pl.prefix = pl.stream && !mixed && num_seqs > kStreamScanSeqs;
   const int waves = mixed ? kStreamWavesMixed : kStreamWaves;
   pl.num_ranges = pl.stream ? (int)(waves / groups > 1 ? waves / groups : 1) : 0;
-  // Merge in batches of 32 partials where a sequence averages 16 ranges or more.  Measured
-  // (interleaved A/B, 64 q / 8 kv heads, D 128, bf16): one sequence of 27901 keys 37.2 ->
-  // 33.6 us and of 128382 keys 101 -> 95-97 us; 64-1024 sequences 0.5-2% slower with the
-  // wide batch, hence the cut-off.
+  // A workgroup per (sequence, head) merges where a sequence averages 16 ranges or more.
   pl.wide_merge = pl.stream && !mixed && (int64_t)num_seqs * 16 <= pl.num_ranges;
   const size_t slots = pl.stream ? (size_t)num_heads * pl.num_ranges * 2
                                  : (pl.num_splits > 1 ? (size_t)num_seqs * num_heads * pl.num_splits : 0);

@@ -921,29 +921,43 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int64_t sh, int
   }
 }
 
-// Combine the n partials (acc, m, l) of one head with the log-sum-exp rule: slot0 for
-// partial 0, slot1 + (j - 1) * slot_step for partial j > 0.  The partials are taken in
-// batches of MB whose (m, l) pairs and accumulator rows are all loaded before any is used;
-// the running max moves between batches with a rescale of the sums.  Batches of 8 hold
-// the usual two or three partials of a head in one round of loads; batches of 32 (a
-// stream-mode batch of few sequences, where one sequence spans dozens of ranges) cut the
-// dependent load rounds of a long sequence by 4 at the cost of more registers.
+// Combine partials (acc, m, l) of one head with the log-sum-exp rule: slot0 for partial
+// 0, slot1 + (j - 1) * slot_step for partial j > 0.  The partials are taken in batches of
+// MB whose (m, l) pairs and accumulator rows are all loaded before any is used; the
+// running max moves between batches with a rescale of the sums.  Batches of 8 hold the
+// usual two or three partials of a head in one round of loads; batches of 32 serve the
+// workgroup merge of a stream-mode batch of few sequences, where one sequence spans
+// dozens of ranges.
 constexpr int kMergeBatch = 8;
 constexpr int kMergeBatchWide = 32;
 
-template <typename T, int D, int MB = kMergeBatch>
-__device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, int h,
-                                            int64_t slots_per_head, int n, int lane,
-                                            int64_t slot0, int64_t slot1, int64_t slot_step) {
-  constexpr int DPL = (D + kWave - 1) / kWave;
+// One wave's running merge state: max M, sum den (this lane's share until summed over
+// the wave) and this lane's dims d = lane + i * 64 of the numerator.
+template <int D>
+struct MergeState {
+  static constexpr int DPL = (D + kWave - 1) / kWave;
+  float M = -INFINITY, den = 0.f, num[DPL];
+  __device__ MergeState() {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) num[i] = 0.f;
+  }
+  __device__ void sum_den() {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) den += shfl_xor_f(den, off);
+  }
+};
+
+// Fold partials j_begin <= j < j_end into st.
+template <int D, int MB>
+__device__ __forceinline__ void merge_run(const DecodeParams& p, int h, int64_t slots_per_head,
+                                          int j_begin, int j_end, int lane, int64_t slot0,
+                                          int64_t slot1, int64_t slot_step, MergeState<D>& st) {
+  constexpr int DPL = MergeState<D>::DPL;
   auto slot_of = [&](int j) -> int64_t {
     return (int64_t)h * slots_per_head + (j == 0 ? slot0 : slot1 + (int64_t)(j - 1) * slot_step);
   };
-  float M = -INFINITY, den = 0.f, num[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) num[i] = 0.f;
-  for (int j0 = 0; j0 < n; j0 += MB) {
-    const int cnt = min(MB, n - j0);
+  for (int j0 = j_begin; j0 < j_end; j0 += MB) {
+    const int cnt = min(MB, j_end - j0);
     // lane k < cnt: (m, l) of partial j0 + k; every lane: its dims of each row (rows past
     // cnt re-read the last one and get weight 0)
     const int64_t my = slot_of(j0 + min(lane, cnt - 1));
@@ -962,23 +976,31 @@ __device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, i
     float bm = mj;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) bm = fmaxf(bm, shfl_xor_f(bm, off));
-    const float Mn = fmaxf(M, bm);
-    const float alpha = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+    const float Mn = fmaxf(st.M, bm);
+    const float alpha = (st.M == -INFINITY) ? 0.f : fast_exp2(st.M - Mn);
     const float w = (mj == -INFINITY) ? 0.f : fast_exp2(mj - Mn);
-    den = den * alpha + w * lj;
+    st.den = st.den * alpha + w * lj;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) num[i] *= alpha;
+    for (int i = 0; i < DPL; ++i) st.num[i] *= alpha;
 #pragma unroll
     for (int k = 0; k < MB; ++k) {
       const float wk = __shfl(w, k, kWave);
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) num[i] += wk * acc[k][i];
+      for (int i = 0; i < DPL; ++i) st.num[i] += wk * acc[k][i];
     }
-    M = Mn;
+    st.M = Mn;
   }
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) den += shfl_xor_f(den, off);
-  store_row<T, D>(p, sh, lane, num, den > 0.f ? 1.f / den : 0.f);
+}
+
+// Merge the n partials of one head in one wave and write its output row.
+template <typename T, int D>
+__device__ __forceinline__ void merge_slots(const DecodeParams& p, int64_t sh, int h,
+                                            int64_t slots_per_head, int n, int lane,
+                                            int64_t slot0, int64_t slot1, int64_t slot_step) {
+  MergeState<D> st;
+  merge_run<D, kMergeBatch>(p, h, slots_per_head, 0, n, lane, slot0, slot1, slot_step, st);
+  st.sum_den();
+  store_row<T, D>(p, sh, lane, st.num, st.den > 0.f ? 1.f / st.den : 0.f);
 }
 
 template <typename T, int D>
@@ -996,32 +1018,25 @@ decode_merge_split_kernel(const DecodeParams p) {
   merge_slots<T, D>(p, sh, h, (int64_t)p.S * p.nsplit, ns, lane, base, base + 1, 1);
 }
 
-// Stream mode: one wave per (sequence, head).  Sequences inside one range were written
-// by the stream kernel; empty sequences get zeros; the others combine one partial per
-// range they touch (the first range's partial is its second slot unless the sequence
-// starts exactly at that range's start).
-template <typename T, int D, bool PFX = false, int MB = kMergeBatch>
-__global__ void __launch_bounds__(kDecodeThreads)
-decode_merge_stream_kernel(const DecodeParams p) {
-  if (guard_tripped(p.guard)) return;
-  constexpr int DPL = (D + kWave - 1) / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t sh = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
-  if (sh >= (int64_t)p.S * p.H) return;
-  const int s = (int)(sh / p.H), h = (int)(sh % p.H);
-  // the length L of sequence s, the batch total and the start P of sequence s, all from
-  // one round of loads: the planning kernel's prefix sums, or one pass over the lengths
-  // (L taken from the pass itself)
+// Where sequence s sits on the concatenated key axis: its length L, its start P and the
+// batch total, all from one round of loads: the planning kernel's prefix sums, or one pass
+// of the wave over the lengths (L taken from the pass itself).
+struct SeqPos {
   int64_t total = 0, P = 0;
   int L = 0;
+};
+
+template <bool PFX>
+__device__ __forceinline__ SeqPos stream_seq_pos(const DecodeParams& p, int s, int lane) {
+  SeqPos q;
   if constexpr (PFX) {
-    L = p.seq_lens[s];
-    total = p.cu[p.S];
-    P = p.cu[s];
+    q.L = p.seq_lens[s];
+    q.total = p.cu[p.S];
+    q.P = p.cu[s];
   } else {
     for (int c0 = 0; c0 < p.S; c0 += kWave) {
       const int x = (c0 + lane < p.S) ? p.seq_lens[c0 + lane] : 0;
-      if (c0 == (s & ~(kWave - 1))) L = __shfl(x, s & (kWave - 1), kWave);
+      if (c0 == (s & ~(kWave - 1))) q.L = __shfl(x, s & (kWave - 1), kWave);
       int before = (c0 + lane < s) ? x : 0;
       int all = x;
 #pragma unroll
@@ -1029,23 +1044,104 @@ decode_merge_stream_kernel(const DecodeParams p) {
         all += __shfl_xor(all, off, kWave);
         before += __shfl_xor(before, off, kWave);
       }
-      total += all;
-      P += before;
+      q.total += all;
+      q.P += before;
     }
   }
-  if (L == 0) {
-    float zero[DPL];
+  return q;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void store_zero_row(const DecodeParams& p, int64_t sh, int lane) {
+  float zero[MergeState<D>::DPL];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) zero[i] = 0.f;
-    store_row<T, D>(p, sh, lane, zero, 0.f);
+  for (int i = 0; i < MergeState<D>::DPL; ++i) zero[i] = 0.f;
+  store_row<T, D>(p, sh, lane, zero, 0.f);
+}
+
+// Stream mode: one wave per (sequence, head).  Sequences inside one range were written
+// by the stream kernel; empty sequences get zeros; the others combine one partial per
+// range they touch (the first range's partial is its second slot unless the sequence
+// starts exactly at that range's start).
+template <typename T, int D, bool PFX = false>
+__global__ void __launch_bounds__(kDecodeThreads)
+decode_merge_stream_kernel(const DecodeParams p) {
+  if (guard_tripped(p.guard)) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t sh = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+  if (sh >= (int64_t)p.S * p.H) return;
+  const int s = (int)(sh / p.H), h = (int)(sh % p.H);
+  const SeqPos q = stream_seq_pos<PFX>(p, s, lane);
+  if (q.L == 0) {
+    store_zero_row<T, D>(p, sh, lane);
     return;
   }
-  const int64_t R = stream_range_len(total, p.nranges);
-  const int64_t r0 = P / R, r1 = (P + L - 1) / R;
+  const int64_t R = stream_range_len(q.total, p.nranges);
+  const int64_t r0 = q.P / R, r1 = (q.P + q.L - 1) / R;
   if (r0 == r1) return;
-  const int64_t slot0 = r0 * 2 + ((r0 * R < P) ? 1 : 0);
-  merge_slots<T, D, MB>(p, sh, h, (int64_t)p.nranges * 2, (int)(r1 - r0 + 1), lane, slot0,
-                        (r0 + 1) * 2, 2);
+  const int64_t slot0 = r0 * 2 + ((r0 * R < q.P) ? 1 : 0);
+  merge_slots<T, D>(p, sh, h, (int64_t)p.nranges * 2, (int)(r1 - r0 + 1), lane, slot0,
+                    (r0 + 1) * 2, 2);
+}
+
+// Stream mode over a few long sequences (each spanning dozens of ranges; no planning
+// tables): one workgroup per (sequence, head).  Its waves fold equal runs of the
+// partials, 32 per round of loads, and wave 0 combines the waves' states through LDS.
+// Every early return depends on (sequence, head) alone, so the whole workgroup takes it
+// before the barrier.
+template <typename T, int D>
+__global__ void __launch_bounds__(kDecodeThreads)
+decode_merge_stream_wide_kernel(const DecodeParams p) {
+  if (guard_tripped(p.guard)) return;
+  constexpr int DPL = MergeState<D>::DPL;
+  __shared__ float s_m[kWavesPerBlock], s_den[kWavesPerBlock], s_num[kWavesPerBlock][D];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int64_t sh = blockIdx.x;
+  const int s = (int)(sh / p.H), h = (int)(sh % p.H);
+  const SeqPos q = stream_seq_pos<false>(p, s, lane);
+  if (q.L == 0) {
+    if (wave == 0) store_zero_row<T, D>(p, sh, lane);
+    return;
+  }
+  const int64_t R = stream_range_len(q.total, p.nranges);
+  const int64_t r0 = q.P / R, r1 = (q.P + q.L - 1) / R;
+  if (r0 == r1) return;
+  const int64_t slot0 = r0 * 2 + ((r0 * R < q.P) ? 1 : 0);
+  const int n = (int)(r1 - r0 + 1);
+  const int per = (n + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int jb = min(n, wave * per), je = min(n, jb + per);
+  MergeState<D> st;
+  merge_run<D, kMergeBatchWide>(p, h, (int64_t)p.nranges * 2, jb, je, lane, slot0, (r0 + 1) * 2,
+                                2, st);
+  st.sum_den();
+  if (lane == 0) {
+    s_m[wave] = st.M;
+    s_den[wave] = st.den;
+  }
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    const int d = lane + i * kWave;
+    if (d < D) s_num[wave][d] = st.num[i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float Mg = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) Mg = fmaxf(Mg, s_m[w]);
+  float den = 0.f, num[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) num[i] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    const float a = (s_m[w] == -INFINITY) ? 0.f : fast_exp2(s_m[w] - Mg);
+    den += a * s_den[w];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int d = lane + i * kWave;
+      if (d < D) num[i] += a * s_num[w][d];
+    }
+  }
+  store_row<T, D>(p, sh, lane, num, den > 0.f ? 1.f / den : 0.f);
 }
 
 // ---- host: kernel parameters from the call's arguments and plan --------------------------

@@ -100,7 +100,8 @@ struct DecodePlan {
                         // kernel first writes the length prefix sums and every range's
                         // first sequence into the workspace
   int num_ranges;       // ranges per head group (stream mode)
-  bool wide_merge;      // stream mode over few sequences: merge 32 partials per load round
+  bool wide_merge;      // stream mode over few long sequences: one workgroup merges each
+                        // (sequence, head)
   int max_seq_len;
   size_t workspace_bytes;
 };

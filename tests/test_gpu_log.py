@@ -31,12 +31,14 @@ def test_launch_log_names_the_chosen_kernels(gpu, capfd):
     err = capfd.readouterr().err
     lines = [l for l in err.splitlines() if l.startswith("pkv: ")]
     names = [l.split()[1] for l in lines]
-    assert names == ["kv_scatter_kernel", "decode_stream_kernel", "decode_merge_stream_kernel",
-                     "kv_scatter_kernel", "prefill_mfma_kernel"], lines
+    assert names == ["kv_scatter_kernel", "decode_stream_kernel",
+                     "decode_merge_stream_wide_kernel", "kv_scatter_kernel",
+                     "prefill_mfma_kernel"], lines
     # the decode batch shape (4 heads per wave, bf16, stream mode) runs on the matrix cores
     assert re.search(r"decode_stream_kernel grid=\d+ block=256 core=mfma D=128 heads_per_wave=4", err)
-    # 8 sequences over 128 ranges per head group: 16 ranges per sequence, the wide merge
-    assert re.search(r"decode_merge_stream_kernel grid=\d+ block=256 rows=256 batch=32", err)
+    # 8 sequences over 128 ranges per head group, 16 ranges per sequence: one workgroup
+    # merges each (sequence, head)
+    assert re.search(r"decode_merge_stream_wide_kernel grid=256 block=256 rows=256", err)
     assert re.search(r"prefill_mfma_kernel grid=\d+ block=512 D=128 heads_per_wg=4 rows_per_wg=64", err)
     # switched off: nothing more
     d.decode()
