@@ -21,11 +21,19 @@ def test_decode_step_replays_bit_exactly(gpu):
 
 
 def test_decode_prefix_stream_step_replays_bit_exactly(gpu):
-    """More than 1024 sequences: the planning kernel is captured with the stream kernel
+    """More than 256 sequences: the planning kernel is captured with the stream kernel
     and the merge."""
     lens = np.random.default_rng(92).integers(10, 600, size=1100).astype(np.int32)
     w = wl.build("graph_prefix", 92, "bf16", lens, np.ones(len(lens), np.int32), 8, 2, 128, 16,
                  wl.MASK_NONE, decode=True)
+    _replay_decode_step(w)
+
+
+def test_decode_few_long_sequences_step_replays_bit_exactly(gpu):
+    """Two long sequences: the workgroup merge (LDS and a barrier) is captured with the
+    stream kernel."""
+    w = wl.build("graph_wide", 93, "bf16", np.array([9000, 15000], np.int32),
+                 np.ones(2, np.int32), 32, 8, 128, 16, wl.MASK_NONE, decode=True)
     _replay_decode_step(w)
 
 
