@@ -36,6 +36,9 @@
 //    batch beyond kStreamMaxSeqs): fixed splits of split_len keys per sequence, waves
 //    walk (sequence, split, head group) items in a grid-stride loop; sequences with one
 //    split are written directly.
+// The merge combines one (sequence, head)'s partials by their log-sum-exp weights: one wave
+// per (sequence, head), or one workgroup per (sequence, head) when a stream-mode batch has
+// so few sequences that each spans dozens of ranges.
 #pragma once
 
 #include "common.h"

@@ -133,7 +133,7 @@ def test_decode_workspace_size_plan(lib):
     # stream mode: 1024 waves over 8 wave groups (4 heads a wave) = 128 key ranges;
     # 32 heads x 128 ranges x 2 partial slots x (128 + 2) floats
     assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 4096) == 32 * 128 * 2 * 130 * 4
-    # beyond 1024 sequences stream mode adds the planning tables: 128 ranges (1024 waves,
+    # beyond 256 sequences stream mode adds the planning tables: 128 ranges (1024 waves,
     # 8 wave groups), partials 8 heads x 128 x 2 slots, then int64 cu[S + 1], int64
     # rpos[128], int32 rstart[128]
     assert lib.pkv_decode_workspace_size(2000, 8, 8, 128, 16, 5000) == \

@@ -234,7 +234,7 @@ def test_decode_item_mode(gpu, H, Hkv, dtype, head_dim):
 
 
 def test_decode_prefix_stream_mode(gpu):
-    """More than 1024 sequences with contexts past one split: stream mode with the planning
+    """More than 256 sequences with contexts past one split: stream mode with the planning
     kernel (prefix sums and range starts in the workspace), partials and the stream
     merge; sequences spanning range boundaries and ranges spanning many sequences."""
     rng = np.random.default_rng(81)

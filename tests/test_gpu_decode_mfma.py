@@ -78,7 +78,7 @@ def test_mfma_small_pages_take_vector_core(gpu):
 
 
 def test_mfma_prefix_stream(gpu):
-    """More than 1024 sequences: stream mode with the planning kernel's tables."""
+    """More than 256 sequences: stream mode with the planning kernel's tables."""
     rng = np.random.default_rng(65)
     lens = rng.integers(1, 900, size=1100).astype(np.int32)
     w = _batch("mfma_split", 65, "f16", lens, 16, 2, 128)
@@ -87,7 +87,7 @@ def test_mfma_prefix_stream(gpu):
 
 
 def test_mfma_prefix_stream_d64_g4(gpu):
-    """More than 1024 sequences at head_dim 64 and 4 heads per wave (bf16)."""
+    """More than 256 sequences at head_dim 64 and 4 heads per wave (bf16)."""
     rng = np.random.default_rng(71)
     lens = rng.integers(1, 1200, size=1030).astype(np.int32)
     w = _batch("mfma_split_d64", 71, "bf16", lens, 32, 8, 64)

@@ -129,7 +129,7 @@ def test_fp8_decode_item_mode(gpu):
 
 
 def test_fp8_decode_prefix_stream(gpu):
-    """More than 1024 sequences with contexts past one split: stream mode with the
+    """More than 256 sequences with contexts past one split: stream mode with the
     planning kernel's tables and the stream merge."""
     rng = np.random.default_rng(38)
     lens = rng.integers(1, 900, size=1100).astype(np.int32)
