@@ -175,3 +175,28 @@ def test_wide_merge_few_sequences(gpu, case):
         w = _batch("wide_mha", 76, "f32", [int(rng.integers(20000, 30000))], 16, 16, 128)
     w.scale = 1.5 * w.scale
     _run(w)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_long_shapes(gpu, seed):
+    """Random batch sizes (1..300), GQA ratios, head_dim, page sizes, dtypes and FP8
+    caches with sequences past one split: whichever core (vector / matrix), mode (stream
+    with scans or tables, split) and merge (per wave, per workgroup) the host picks, the
+    sampled rows stay on the oracle and no unwritten slot leaks in."""
+    rng = np.random.default_rng(500 + seed)
+    S = int(rng.choice([1, 2, 3, 5, 8, 17, 64, 200, 300]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([8, 16, 32]))
+    dtype = str(rng.choice(["bf16", "f16"]))
+    fp8 = bool(rng.integers(0, 4) == 0)
+    # at most ~40M cached K elements so the host-side generation stays quick
+    cap = max(300, min(30000, 40_000_000 // (S * Hkv * D)))
+    lens = rng.integers(1, cap + 1, size=S).astype(np.int32)
+    lens[rng.integers(0, S)] = max(int(lens.max()), 257)      # some sequence past one split
+    w = _batch(f"rand_long_{seed}", 500 + seed, dtype, lens, g * Hkv, Hkv, D, bs=bs)
+    if fp8:
+        w = wl.with_fp8_cache(w)
+    rows = np.unique(np.concatenate([[0, S - 1], rng.choice(S, min(S, 40), replace=False)]))
+    _run(w, rows=rows)
