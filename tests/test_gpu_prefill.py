@@ -223,3 +223,32 @@ def test_prefill_wide_gqa(gpu, H, Hkv):
     lens = w.seq_lens
     w = wl.build("wide_gqa", 90 + H, "bf16", lens, w.q_lens, H, Hkv, 128, 16, wl.MASK_CAUSAL)
     _run(w)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_prefill_random_long_shapes(gpu, seed):
+    """Random chunked-prefill batches past several 64-row tiles and key tiles: cached
+    context 0..1500, chunks 1..400, GQA ratios 1..8, head_dim 64 / 128, pages of 8..64,
+    the three masks with random spans, bf16 / fp16, sometimes an FP8 cache; sampled rows
+    (first and last of every sequence among them) against the oracle."""
+    rng = np.random.default_rng(700 + seed)
+    S = int(rng.integers(1, 7))
+    Hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([8, 16, 32, 64]))
+    dtype = str(rng.choice(["bf16", "f16"]))
+    mask = int(rng.integers(0, 3))
+    ctx = rng.integers(0, 1501, size=S)
+    ql = rng.integers(1, 401, size=S)
+    lens = (ctx + ql).astype(np.int32)
+    w = wl.build(f"rand_prefill_{seed}", 700 + seed, dtype, lens, ql.astype(np.int32), g * Hkv,
+                 Hkv, D, bs, mask, span_len=int(rng.choice([16, 48, 100, 256])),
+                 scale=float(rng.uniform(0.05, 0.2)), spare_blocks=1, rng=rng)
+    if rng.integers(0, 4) == 0:
+        w = wl.with_fp8_cache(w)
+    cu = w.cu_seqlens_q
+    ends = np.concatenate([cu[:-1], cu[1:] - 1])
+    rows = np.unique(np.concatenate([ends, rng.choice(int(cu[-1]), min(int(cu[-1]), 160),
+                                                      replace=False)]))
+    _run(w, rows=rows)
