@@ -110,3 +110,34 @@ def test_mixed_rejects_bad_boundary_and_workspace(gpu):
     assert e.value.code == B.PKV_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool(torch.all(out == 7.0))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_mixed_random_shapes(gpu, seed):
+    """Random steps: 0..4 context sequences (context 0..1200, chunks 1..300) then 0..300
+    generation sequences of 1..6000 keys; GQA ratios, head_dim, pages, masks, spans and
+    dtypes drawn; sampled rows (every context chunk's first and last) against the oracle."""
+    rng = np.random.default_rng(900 + seed)
+    nc = int(rng.integers(0, 5))
+    ng = int(rng.choice([0, 1, 7, 64, 300])) if nc else int(rng.choice([1, 7, 64, 300]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([8, 16, 32]))
+    dtype = str(rng.choice(["bf16", "f16", "f32"]))
+    mask = int(rng.integers(0, 3))
+    ql = rng.integers(1, 301, size=nc)
+    ctx = rng.integers(0, 1201, size=nc)
+    # at most ~40M cached generation K elements so the host-side generation stays quick
+    gl = rng.integers(1, max(300, min(6000, 40_000_000 // (max(ng, 1) * Hkv * D))) + 1, size=ng)
+    lens = np.concatenate([ctx + ql, gl]).astype(np.int32)
+    qls = np.concatenate([ql, np.ones(ng, np.int64)]).astype(np.int32)
+    w = wl.build(f"rand_mixed_{seed}", 900 + seed, dtype, lens, qls, g * Hkv, Hkv, D, bs, mask,
+                 span_len=int(rng.choice([16, 48, 256])), scale=float(rng.uniform(0.05, 0.2)),
+                 rng=rng)
+    w.num_ctx_seqs = nc
+    cu = w.cu_seqlens_q
+    T = int(cu[-1])
+    ends = np.concatenate([cu[:nc], cu[1:nc + 1] - 1])
+    rows = np.unique(np.concatenate([ends, [T - 1], rng.choice(T, min(T, 200), replace=False)]))
+    _run(w, rows=rows.astype(np.int64))
