@@ -512,7 +512,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads",
                     default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal,mixed_spans,"
-                            "decode_batch_fp8,mixed_batch,smallseq_train")
+                            "decode_batch_fp8,decode_long_seq,mixed_batch,smallseq_train")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibration-copy", action="store_true",

@@ -311,6 +311,16 @@ def with_fp8_cache(w: Workload, k_scale: float = 0.0173, v_scale: float = 0.0211
     return w
 
 
+def decode_long_seq(seed: int = 7, length: int = 32768, dtype: str = "bf16",
+                    spare_blocks: int = 1) -> Workload:
+    """One sequence of 32768 keys decoding its next token (long-context batch-1 serving),
+    32 q / 8 kv heads, D 128, B 16."""
+    rng = np.random.default_rng(seed)
+    return build("decode_long_seq", seed, dtype, np.array([length], np.int32),
+                 np.ones(1, np.int32), 32, 8, 128, 16, MASK_NONE, spare_blocks=spare_blocks,
+                 decode=True, rng=rng)
+
+
 def decode_batch_fp8(seed: int = 1, **kw) -> Workload:
     """The decode batch (64 sequences, contexts U[256, 4096], 32 q / 8 kv heads, D 128,
     B 16) over an FP8 cache."""
@@ -351,6 +361,7 @@ CONFIGS = {
     "long_block_causal": long_block_causal,
     "mixed_spans": mixed_spans,
     "decode_batch_fp8": decode_batch_fp8,
+    "decode_long_seq": decode_long_seq,
     "long_block_causal_fp8": long_block_causal_fp8,
     "mixed_batch": mixed_batch,
     "smallseq_train": smallseq_train,
