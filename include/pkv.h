@@ -6,7 +6,8 @@
  * ---------------------------------------
  * - Every pointer argument named for a tensor is a DEVICE pointer owned by the
  *   caller.  The library allocates no device memory and keeps no state apart
- *   from a thread-local error string (pkv_last_error).
+ *   from a thread-local error string (pkv_last_error) and two device words of
+ *   the device-side checks.
  * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *   Every call only enqueues work on that stream: it never synchronises and
  *   never copies device memory to the host, so device-resident lengths and
@@ -46,6 +47,12 @@
  * - Precision: bf16/fp16 inputs, fp32 scores, softmax statistics and
  *   accumulators; probabilities are rounded to the input type for the
  *   probability-times-V products; output rounded to nearest even.
+ * - Non-finite inputs: cache slots a row cannot see (masked keys, unmapped
+ *   blocks, table tails, in-block tails) never enter its arithmetic, so they
+ *   may hold anything, NaN included.  A NaN or infinity in a query row or in a
+ *   key or value row that a query row does see gives that output row undefined
+ *   values on the MFMA prefill and mixed-batch kernels (they are compiled to
+ *   assume finite operands); the decode kernels give a NaN row.
  *
  * Device-content preconditions (not checked by default, undefined behaviour if
  * violated; pkv_set_device_checks(1) checks all but slot uniqueness on the GPU):
@@ -133,9 +140,10 @@ int pkv_kv_cache_write_fp8(const void* key, const void* value, int64_t kv_token_
                            float k_scale, float v_scale, pkv_dtype dtype, void* stream);
 
 /*
- * pkv_kv_cache_gather -- step 2 of the Spyre PR ("gather the relevant KV entries
- * from scattered blocks into compact tensors").  Test and debugging aid: the
- * attention kernels fuse this gather into their loads and never materialise it.
+ * pkv_kv_cache_gather -- step 2 of the Spyre PR ("Description"): the rows a
+ * sequence needs are read out of the scattered cache blocks through its block
+ * table and laid out contiguously.  Test and debugging aid: the attention
+ * kernels fuse this gather into their loads and never materialise it.
  *
  * cu_seq_lens     int32 [num_seqs+1], prefix sums of the sequence lengths.
  * key_out,
@@ -154,8 +162,9 @@ int pkv_kv_cache_gather(void* key_out, void* value_out, const int32_t* cu_seq_le
 /*
  * pkv_decode_workspace_size -- bytes of device workspace pkv_paged_attention_decode
  * needs for these sizes (0 when every sequence fits one split): fp32 partial
- * (output, max, sum) slots, plus, beyond 256 sequences, the tables a planning
- * kernel writes (8 bytes per sequence and 20 per key range).  The caller
+ * (output, max, sum) slots of (head_dim + 2) * 4 bytes each, plus, beyond 256
+ * sequences, the tables a planning kernel writes (8 bytes per sequence, 8 more,
+ * and 12 per key range).  The caller
  * allocates it ahead of time (ROCm TransformerEngine small-seq PR: workspace
  * and aux buffers are pre-allocated from host max sequence lengths).
  * Returns 0 for invalid sizes as well; the decode call then validates.
@@ -181,11 +190,12 @@ size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  * block_tables    int32 [num_seqs, max_blocks_per_seq] (row stride max_blocks_per_seq).
  * seq_lens        int32 [num_seqs]; 0 yields a zero output row.
  * max_seq_len     host hint >= every seq_lens[s]; sizes the split grid.
- * workspace       device buffer of at least pkv_decode_workspace_size(...) bytes
- *                 (may be NULL when that size is 0).  Contents need no
- *                 initialisation; calls sharing one workspace must be ordered.
- * Errors: INVALID_ARG (null pointers, num_heads % num_kv_heads != 0, sizes),
- * UNSUPPORTED (head_dim, dtype), WORKSPACE (too small).
+ * workspace       device buffer of at least pkv_decode_workspace_size(...) bytes,
+ *                 16-byte aligned (may be NULL when that size is 0).  Contents
+ *                 need no initialisation; calls sharing one workspace must be
+ *                 ordered.
+ * Errors: INVALID_ARG (null pointers, num_heads % num_kv_heads != 0, sizes, a
+ * misaligned workspace), UNSUPPORTED (head_dim, dtype), WORKSPACE (too small).
  */
 int pkv_paged_attention_decode(void* out, const void* query, const void* key_cache,
                                const void* value_cache, int64_t cache_block_stride,
@@ -283,7 +293,8 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* query, const int32_t*
  * seq_lens        int32 [num_seqs]; block_tables int32 [num_seqs, max_blocks_per_seq].
  * max_q_len       host hint >= every context chunk length (0 without context rows).
  * workspace       device buffer of pkv_mixed_workspace_size(num_seqs -
- *                 num_ctx_seqs, ...) bytes (may be NULL when that is 0).
+ *                 num_ctx_seqs, ...) bytes, 16-byte aligned (may be NULL when
+ *                 that is 0).
  *                 Contents need no initialisation; calls sharing one workspace
  *                 must be ordered.
  * bf16/fp16 with head_dim 64 or 128 and scale > 0 run as one launch; other

@@ -209,6 +209,10 @@ int decode_common(void* out, const void* query, const void* key_cache, const voi
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(PKV_ERR_WORKSPACE, "decode workspace of %zu bytes required (got %zu at %p)",
                 plan.workspace_bytes, workspace_bytes, workspace);
+  // the partials are stored as 16-byte vectors and the planning tables as int64
+  if (plan.workspace_bytes > 0 && !aligned(workspace, 16))
+    return fail(PKV_ERR_INVALID_ARG, "the decode workspace must be 16-byte aligned (got %p)",
+                workspace);
   pkv::AttnArgs a{};
   a.out = out;
   a.query = query;
@@ -631,6 +635,9 @@ int pkv_paged_attention_mixed(void* out, const void* query, const int32_t* cu_se
       (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(PKV_ERR_WORKSPACE, "mixed-batch workspace of %zu bytes required (got %zu at %p)",
                 plan.workspace_bytes, workspace_bytes, workspace);
+  if (num_gen > 0 && plan.workspace_bytes > 0 && !aligned(workspace, 16))
+    return fail(PKV_ERR_INVALID_ARG, "the mixed-batch workspace must be 16-byte aligned (got %p)",
+                workspace);
   const size_t eb = dtype == PKV_F32 ? 4 : 2;
   const size_t row_bytes = (size_t)num_heads * head_dim * eb;
   pkv::AttnArgs ctx{};

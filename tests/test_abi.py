@@ -97,6 +97,27 @@ def test_decode_rejections(lib):
     assert _decode(lib, S=0) == B.PKV_OK
 
 
+def test_decode_rejects_misaligned_workspace(lib):
+    """The partials are stored as 16-byte vectors and the planning tables as int64: a
+    workspace that is not 16-byte aligned is rejected on the host."""
+    need = lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 4096)
+    assert _decode(lib, ws=ctypes.c_void_p(0x1008), wsb=need) == B.PKV_ERR_INVALID_ARG
+    assert "aligned" in B.last_error()
+    # a plan without a workspace ignores the pointer
+    assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 256) == 0
+
+
+def test_mixed_rejects_misaligned_workspace(lib):
+    need = lib.pkv_mixed_workspace_size(64, 32, 8, 128, 16, 4096)
+    assert need > 0
+    rc = lib.pkv_paged_attention_mixed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16 * 8 * 128, FAKE, 256,
+                                       66, 64 + 100, 2, 100, 32, 8, 128, 9000, 16, 0.088,
+                                       B.PKV_MASK_CAUSAL, 0, 50, 4096, ctypes.c_void_p(0x1004),
+                                       need, B.PKV_BF16, NULL)
+    assert rc == B.PKV_ERR_INVALID_ARG
+    assert "aligned" in B.last_error()
+
+
 def test_decode_rejects_workspace_without_prefix_tables(lib):
     """Beyond 256 sequences a workspace sized for the partials alone is too small: the
     call fails on the host, before any launch."""
