@@ -6,8 +6,10 @@
  * ---------------------------------------
  * - Every pointer argument named for a tensor is a DEVICE pointer owned by the
  *   caller.  The library allocates no device memory and keeps no state apart
- *   from a thread-local error string (pkv_last_error) and two device words of
- *   the device-side checks.
+ *   from a thread-local error string (pkv_last_error), two device words of the
+ *   device-side checks, and the fixed scratch array of
+ *   pkv_paged_attention_decode_noalloc (one copy per GPU, part of the loaded
+ *   code object, held until the process ends).
  * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *   Every call only enqueues work on that stream: it never synchronises and
  *   never copies device memory to the host, so device-resident lengths and
@@ -205,6 +207,31 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
                                int32_t block_size, float scale, int32_t max_seq_len,
                                void* workspace, size_t workspace_bytes, pkv_dtype dtype,
                                void* stream);
+
+/*
+ * pkv_paged_attention_decode_noalloc -- pkv_paged_attention_decode for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments, results
+ * and kernels, without the workspace arguments.  The workspace is the
+ * library's own scratch array of PKV_DECODE_NOALLOC_MAX_WORKSPACE bytes, one per
+ * GPU (its address is looked up once per device, on the first call there); the
+ * call allocates and frees nothing.  Every call on one GPU shares that GPU's
+ * array, so calls that overlap on one GPU (concurrent streams, threads)
+ * race and give undefined results: order them.  Its contents need no
+ * clearing between calls (every partial is written before it is read).
+ * Errors: as pkv_paged_attention_decode, plus WORKSPACE when
+ * pkv_decode_workspace_size(...) for these sizes exceeds
+ * PKV_DECODE_NOALLOC_MAX_WORKSPACE, and LAUNCH when the array's device
+ * address cannot be obtained.
+ */
+#define PKV_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)16 << 20)
+int pkv_paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                       const void* value_cache, int64_t cache_block_stride,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t num_blocks, int32_t block_size, float scale,
+                                       int32_t max_seq_len, pkv_dtype dtype, void* stream);
 
 /*
  * pkv_paged_attention_decode_fp8 -- pkv_paged_attention_decode over FP8 caches

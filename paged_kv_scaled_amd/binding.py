@@ -32,6 +32,9 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32,
                                                   _I32, _I32, _I32, _I32, _F, _I32, _P, _SZ,
                                                   ctypes.c_int, _P]),
+    "pkv_paged_attention_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P,
+                                                          _I32, _I32, _I32, _I32, _I32, _I32, _F,
+                                                          _I32, ctypes.c_int, _P]),
     "pkv_paged_attention_decode_fp8": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
                                                       _I32, _I32, _I32, _I32, _I32, _F, _F, _F,
                                                       _I32, _P, _SZ, ctypes.c_int, _P]),
@@ -187,6 +190,21 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, seq
                                           block_tables.shape[1], _ptr(seq_lens), S, H, hkv, D, nb,
                                           bs, float(scale), int(max_seq_len), _ptr(workspace),
                                           ws_bytes, _dtype_code(query), _stream()))
+
+
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables, seq_lens,
+                                   scale: float, max_seq_len: int):
+    """paged_attention_decode with the library's own per-GPU scratch as workspace (the call
+    allocates nothing; calls that overlap on one GPU race)."""
+    lib = load()
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    S, H, D = query.shape
+    assert D == d and out.shape == query.shape and query.is_contiguous() and out.is_contiguous()
+    _check(lib.pkv_paged_attention_decode_noalloc(_ptr(out), _ptr(query), _ptr(key_cache),
+                                                  _ptr(value_cache), bstride, _ptr(block_tables),
+                                                  block_tables.shape[1], _ptr(seq_lens), S, H, hkv,
+                                                  D, nb, bs, float(scale), int(max_seq_len),
+                                                  _dtype_code(query), _stream()))
 
 
 def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables, seq_lens,

@@ -10,6 +10,9 @@
 #include "../../include/pkv.h"
 #include "kernels.h"
 
+static_assert(pkv::kDecodeScratchBytes == PKV_DECODE_NOALLOC_MAX_WORKSPACE,
+              "the scratch array and its documented size must agree");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -494,6 +497,41 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
                        max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
                        num_blocks, block_size, scale, false, 1.f, 1.f, max_seq_len, workspace,
                        workspace_bytes, dtype, stream, "pkv_paged_attention_decode");
+}
+
+int pkv_paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                       const void* value_cache, int64_t cache_block_stride,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t num_blocks, int32_t block_size, float scale,
+                                       int32_t max_seq_len, pkv_dtype dtype, void* stream) {
+  clear_error();
+  const char* what = "pkv_paged_attention_decode_noalloc";
+  int rc;
+  if ((rc = check_dtype(dtype)) != PKV_OK) return rc;
+  // the plan's workspace must fit the library's scratch array; checked before the lookup
+  // so that an oversized call touches no device state
+  if (num_seqs > 0 && num_heads > 0 && num_kv_heads > 0 && num_heads % num_kv_heads == 0 &&
+      PKV_HEAD_DIM_SUPPORTED(head_dim) && is_pow2_in(block_size, 1, 256) && max_seq_len >= 0) {
+    const size_t need = pkv::decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                         max_seq_len).workspace_bytes;
+    if (need > pkv::kDecodeScratchBytes)
+      return fail(PKV_ERR_WORKSPACE, "%s: these sizes need %zu bytes of decode workspace, more "
+                  "than the %zu bytes of the library's scratch; use pkv_paged_attention_decode "
+                  "with a caller workspace", what, need, (size_t)pkv::kDecodeScratchBytes);
+  }
+  void* ws = nullptr;
+  if (num_seqs > 0) {
+    const hipError_t e = pkv::decode_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(PKV_ERR_LAUNCH, "%s: the scratch array of the current device is unavailable: %s",
+                  what, hipGetErrorString(e));
+  }
+  return decode_common(out, query, key_cache, value_cache, cache_block_stride, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                       num_blocks, block_size, scale, false, 1.f, 1.f, max_seq_len, ws,
+                       ws ? pkv::kDecodeScratchBytes : 0, dtype, stream, what);
 }
 
 int pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,

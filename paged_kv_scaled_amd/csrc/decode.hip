@@ -1,10 +1,20 @@
 // Single-token decode: host side (plan and launches).  The kernels, and what they
 // compute, are in decode_device.h.
+#include <mutex>
+
 #include "decode_device.h"
 
 namespace pkv {
 
 namespace {
+
+// The decode workspace of the allocation-free entry point: a device array of the
+// library, one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel: it takes the device address that hipGetSymbolAddress gives
+// for the current device (decode_scratch) and passes that.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
 
 // ---- dispatch --------------------------------------------------------------------------
 
@@ -209,6 +219,27 @@ DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
     pl.workspace_bytes += ((size_t)num_seqs + 1 + pl.num_ranges) * sizeof(int64_t) +
                           (size_t)pl.num_ranges * sizeof(int32_t);
   return pl;
+}
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* table[kMaxScratchDevices] = {};
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (table[dev] == nullptr) {
+    // once per device, with that device current: its own copy of the array
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    table[dev] = p;
+  }
+  *ptr = table[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& pl, hipStream_t stream) {

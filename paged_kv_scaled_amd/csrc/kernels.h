@@ -147,6 +147,10 @@ hipError_t launch_kv_scatter_fp8(const ScatterArgs& a, float k_inv_scale, float 
                                  hipStream_t stream);
 hipError_t launch_kv_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, hipStream_t stream);
+// Size of the library's own decode workspace (the allocation-free decode entry point), and
+// its device address on the current device, looked up once per device.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr);
 // Returns hipErrorNotSupported when no MFMA variant covers the shape.
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_valu(const AttnArgs& a, hipStream_t stream);

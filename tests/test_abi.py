@@ -107,6 +107,31 @@ def test_decode_rejects_misaligned_workspace(lib):
     assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 256) == 0
 
 
+def _noalloc(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bstride=16 * 8 * 128, bt=FAKE, mb=256, sl=FAKE,
+             S=64, H=32, Hkv=8, D=128, nb=9000, bs=16, scale=0.088, maxL=4096, dt=B.PKV_BF16)
+    a.update(kw)
+    return lib.pkv_paged_attention_decode_noalloc(a["out"], a["q"], a["kc"], a["vc"], a["bstride"],
+                                                  a["bt"], a["mb"], a["sl"], a["S"], a["H"],
+                                                  a["Hkv"], a["D"], a["nb"], a["bs"], a["scale"],
+                                                  a["maxL"], a["dt"], NULL)
+
+
+def test_decode_noalloc_rejections(lib):
+    """The allocation-free decode rejects, before it looks up its scratch array, sizes
+    whose workspace exceeds that array, and every argument the plain decode rejects."""
+    limit = 16 << 20
+    # 2M sequences: 8.5 MB of partials plus 16 MB of planning tables
+    need = lib.pkv_decode_workspace_size(2_000_000, 64, 8, 128, 16, 5000)
+    assert need > limit
+    assert _noalloc(lib, S=2_000_000, H=64, maxL=5000, mb=400) == B.PKV_ERR_WORKSPACE
+    assert "scratch" in B.last_error()
+    # the decode batch fits
+    assert lib.pkv_decode_workspace_size(64, 32, 8, 128, 16, 4096) <= limit
+    assert _noalloc(lib, dt=7) == B.PKV_ERR_UNSUPPORTED
+    assert _noalloc(lib, S=0) == B.PKV_OK
+
+
 def test_mixed_rejects_misaligned_workspace(lib):
     need = lib.pkv_mixed_workspace_size(64, 32, 8, 128, 16, 4096)
     assert need > 0
