@@ -2,6 +2,7 @@
 // Every check runs before anything is enqueued, and a rejected call touches no memory
 // (CSA2 Vanilla golden PR, "Description": rejected before anything is written).
 #include <atomic>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -302,6 +303,25 @@ int smallseq_common(pkv::SmallArgs& a, const void* query, const void* key_cache,
 }  // namespace
 
 namespace pkv {
+
+DeviceShape device_shape() {
+  constexpr int kMaxDev = 64;
+  constexpr int kCusPerXcd = 32;
+  static std::mutex mu;
+  static DeviceShape table[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return DeviceShape{256, 8};
+  std::lock_guard<std::mutex> lock(mu);
+  DeviceShape& d = table[dev];
+  if (d.cus == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return DeviceShape{256, 8};
+    d.cus = cus;
+    d.xcds = cus >= kCusPerXcd ? cus / kCusPerXcd : 1;
+  }
+  return d;
+}
 
 // -1: not read yet; then 0 / 1 (PKV_LOG in the environment, or pkv_set_log)
 static std::atomic<int> g_log{-1};

@@ -62,8 +62,8 @@ bool launch_main_mfma(const DecodeParams& dp, const DecodePlan& pl, hipStream_t 
     if constexpr (mfma_stream_shape<T, D, HPW>()) {
       const int blocks = (int)((dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock);
       PKV_LOG_LAUNCH("decode_stream_kernel", blocks, kDecodeThreads,
-                     "core=mfma D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld", D, HPW, MS,
-                     dp.nranges, (long long)dp.total_items);
+                     "core=mfma D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld cus=%d", D,
+                     HPW, MS, dp.nranges, (long long)dp.total_items, device_shape().cus);
       if (pl.prefix)
         hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, MS, true, true>), dim3(blocks),
                            dim3(kDecodeThreads), 0, stream, dp);
@@ -99,8 +99,8 @@ void launch_main(const DecodeParams& dp, const DecodePlan& pl, hipStream_t strea
   if (pl.stream) {
     const int blocks = (int)((dp.total_items + kWavesPerBlock - 1) / kWavesPerBlock);
     PKV_LOG_LAUNCH("decode_stream_kernel", blocks, kDecodeThreads,
-                   "core=vector D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld", D, HPW, NS,
-                   dp.nranges, (long long)dp.total_items);
+                   "core=vector D=%d heads_per_wave=%d steps=%d ranges=%d items=%lld cus=%d", D,
+                   HPW, NS, dp.nranges, (long long)dp.total_items, device_shape().cus);
     if (pl.prefix)
       hipLaunchKernelGGL((decode_stream_kernel<T, D, HPW, NS, false, true>), dim3(blocks),
                          dim3(kDecodeThreads), 0, stream, dp);
@@ -208,7 +208,7 @@ DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
   // kStreamMaxSeqs generation sequences and takes split mode beyond.
   pl.stream = pl.num_splits > 1 && (!mixed || num_seqs <= kStreamMaxSeqs);
   pl.prefix = pl.stream && !mixed && num_seqs > kStreamScanSeqs;
-  const int waves = mixed ? kStreamWavesMixed : kStreamWaves;
+  const int waves = device_shape().cus * (mixed ? kStreamWavesPerCuMixed : kStreamWavesPerCu);
   pl.num_ranges = pl.stream ? (int)(waves / groups > 1 ? waves / groups : 1) : 0;
   // A workgroup per (sequence, head) merges where a sequence averages 16 ranges or more.
   pl.wide_merge = pl.stream && !mixed && (int64_t)num_seqs * 16 <= pl.num_ranges;

@@ -55,10 +55,10 @@ constexpr int kStreamScanSeqs = 256;   // plain decode: up to here every stream 
                                        // seq_lens, beyond the planning kernel's tables
 constexpr int kStreamMaxSeqs = 1024;   // mixed batch (no planning kernel): stream mode up to
                                        // here, scanned by every wave; split mode beyond
-constexpr int kStreamWaves = 1024;     // waves of the stream grid (all head groups): one wave
-                                       // per SIMD on 256 CUs
-constexpr int kStreamWavesMixed = 2048;   // the same inside the mixed-batch kernel, whose
-                                          // decode blocks hold 8 waves (two per SIMD)
+constexpr int kStreamWavesPerCu = 4;       // waves of the stream grid (all head groups): one
+                                           // wave per SIMD (1024 on a whole MI355X)
+constexpr int kStreamWavesPerCuMixed = 8;  // the same inside the mixed-batch kernel, whose
+                                           // decode blocks hold 8 waves (two per SIMD)
 constexpr int kStreamMinRange = 64;    // shortest range, keys
 
 template <typename T, int D>

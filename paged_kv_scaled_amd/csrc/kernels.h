@@ -110,6 +110,15 @@ struct DecodePlan {
 DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                        int block_size, int max_seq_len, bool mixed = false);
 
+// The current device's shape, read once per device from its properties: compute units,
+// and XCDs (chiplets of 32 CUs on gfx950, so 8 on a whole MI355X, fewer on a partition).
+// Without a device (host-only use, the workspace size queries) the whole chip is assumed.
+struct DeviceShape {
+  int cus;
+  int xcds;
+};
+DeviceShape device_shape();
+
 hipError_t launch_kv_scatter(const ScatterArgs& a, hipStream_t stream);
 // Launch log: with PKV_LOG=1 in the environment (read once), every kernel launch prints
 // one line to stderr -- the kernel, its grid and block, and the variant chosen.

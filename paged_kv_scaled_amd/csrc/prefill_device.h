@@ -55,6 +55,8 @@ struct PrefillParams {
   int32_t mb, S, H, Hkv, g, block_shift, mask, span;
   int32_t hw, rb_log2, head_groups, qtiles;   // WG tiling
   int32_t ngroups;                            // (sequence, kv head, head group) groups
+  int32_t nxcd;                               // XCDs of the device (workgroup dealing)
+  int32_t rank_items;                         // order each XCD's query tiles longest first
   float scale_log2;                           // scale * log2(e) (times k_scale for FP8)
   float out_scale;                            // v_scale for an FP8 cache, else 1
   const uint32_t* guard;                      // device error word when checks are on
@@ -131,22 +133,56 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   const int lc = lane & 31;           // lane column
 
   // ---- workgroup -> (sequence, kv head, head group, query tile) ----------------------
-  // Workgroups go to the 8 XCDs round-robin (XCD = blockIdx % 8).  Group u = (sequence,
-  // kv head, head group) is dealt to XCD u % 8, and all query tiles of a group stay on
+  // Workgroups go to the XCDs round-robin (XCD = blockIdx % nxcd).  Group u = (sequence,
+  // kv head, head group) is dealt to XCD u % nxcd, and all query tiles of a group stay on
   // its XCD (they read the same keys: one L2 holds them); the groups of one sequence
-  // spread over all XCDs, so a long sequence does not load one XCD only.  Inside a
-  // group the longest query tiles start first.
-  const int xcd = bid & 7;
-  const int slot = bid >> 3;
-  const int grp = (slot / p.qtiles) * 8 + xcd;
+  // spread over all XCDs, so a long sequence does not load one XCD only.
+  const int nx = p.nxcd;
+  const int xcd = bid % nx;
+  const int slot = bid / nx;
+  int grp, qt;
+  if (p.rank_items) {
+    // Few workgroups per CU: the order in which an XCD starts its query tiles sets the
+    // makespan (a long tile started late finishes last), so each XCD starts them longest
+    // first across all its groups.  Every wave ranks the XCD's (group, query tile) items,
+    // one per lane, by their key tiles, and the workgroup takes the item of rank `slot`.
+    const int items = ((p.ngroups + nx - 1) / nx) * p.qtiles;   // <= 64 (host)
+    int cnt = -2;                     // lanes past the items rank last
+    if (lane < items) {
+      cnt = -1;                       // an empty query tile ranks after every real one
+      const int g = (lane / p.qtiles) * nx + xcd;
+      if (g < p.ngroups) {
+        const int sq = g / (p.head_groups * p.Hkv);
+        const int c0 = p.cu_q[sq], n = p.cu_q[sq + 1] - c0;
+        const int r0 = (lane % p.qtiles) * (32 << p.rb_log2);
+        if (r0 < n) {
+          const int L = p.seq_lens[sq];
+          const int z0 = p.cu_spans ? p.cu_spans[sq] : 0, z1 = p.cu_spans ? p.cu_spans[sq + 1] : 0;
+          const int last = min(r0 + (32 << p.rb_log2), n) - 1;
+          cnt = (visible_end(p.mask, L - n + last, L, p.span, p.full_spans, z0, z1) + kBN - 1) / kBN;
+        }
+      }
+    }
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int cj = __builtin_amdgcn_readlane(cnt, j);
+      rank += (cj > cnt || (cj == cnt && j < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __ballot(rank == slot);
+    const int who = hit ? (int)__builtin_ctzll(hit) : 0;
+    grp = (who / p.qtiles) * nx + xcd;
+    qt = who % p.qtiles;
+  } else {
+    // inside a group the longest query tiles start first
+    grp = (slot / p.qtiles) * nx + xcd;
+    qt = p.qtiles - 1 - slot % p.qtiles;
+  }
   if (grp >= p.ngroups) return;
-  const int qt_rev = slot % p.qtiles;
   int rest = grp;
   const int hgrp = rest % p.head_groups;
   rest /= p.head_groups;
   const int kvh = rest % p.Hkv;
   const int s = rest / p.Hkv;
-  const int qt = p.qtiles - 1 - qt_rev;       // the longest tiles start first
   const int q0 = p.cu_q[s];
   const int qn = p.cu_q[s + 1] - q0;
   const int RB = 1 << p.rb_log2;
@@ -486,9 +522,16 @@ inline bool prefill_params(const AttnArgs& a, PrefillParams& p, int64_t& nb) {
   const int rows = 32 * (kWaves / hw);
   p.qtiles = (a.max_q_len + rows - 1) / rows;
   const int64_t ng = (int64_t)p.head_groups * p.Hkv * p.S;
-  nb = (ng + 7) / 8 * 8 * p.qtiles;     // 8 XCDs x groups per XCD x tiles
+  const int nx = device_shape().xcds;
+  nb = (ng + nx - 1) / nx * nx * p.qtiles;   // XCDs x groups per XCD x tiles
   if (nb > 0x7FFFFFFF) return false;
   p.ngroups = (int)ng;
+  p.nxcd = nx;
+  // rank the query tiles when an XCD's items fit one wave's lanes: a grid of at most
+  // 64 workgroups per XCD, where one workgroup per CU at a time leaves their order to
+  // decide the makespan
+  const int64_t items = (ng + nx - 1) / nx * p.qtiles;
+  p.rank_items = items <= 64 ? 1 : 0;
   p.scale_log2 = a.scale * (a.kv_fp8 ? a.k_scale : 1.f) * kLog2e;
   p.out_scale = a.kv_fp8 ? a.v_scale : 1.f;
   p.guard = a.guard;

@@ -40,6 +40,14 @@ def test_launch_log_names_the_chosen_kernels(gpu, capfd):
     # merges each (sequence, head)
     assert re.search(r"decode_merge_stream_wide_kernel grid=256 block=256 rows=256", err)
     assert re.search(r"prefill_mfma_kernel grid=\d+ block=512 D=128 heads_per_wg=4 rows_per_wg=64", err)
+    # the chip shape comes from the device: the CU count sizes the decode stream grid (one
+    # wave per SIMD) and the XCD count (32 CUs each) deals the prefill workgroups; this
+    # small prefill grid starts each XCD's query tiles longest first
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    m = re.search(r"decode_stream_kernel .* ranges=(\d+) items=(\d+) cus=(\d+)", err)
+    assert m and int(m.group(3)) == cus and int(m.group(2)) == 4 * cus, lines
+    m = re.search(r"prefill_mfma_kernel .* xcds=(\d+) ranked=(\d)", err)
+    assert m and int(m.group(1)) == max(1, cus // 32) and m.group(2) == "1", lines
     # switched off: nothing more
     d.decode()
     torch.cuda.synchronize()
