@@ -112,16 +112,17 @@ class Timer:
 
 
 def flush_llc(buf):
-    """Overwrite a 512 MB buffer so neither L2 nor the 256 MB MALL hold the inputs."""
-    buf.add_(1)
+    """Read a 512 MB buffer so that neither L2 nor the 256 MB MALL hold the inputs.  A read
+    (not a write) leaves clean lines behind: a rewrite would leave the caches full of dirty
+    lines whose write-back the next kernel would pay for."""
+    buf.sum()
 
 
 def run_decode_step_bench(w, steps, warmup):
     """The default step: scatter the new tokens, then decode."""
     import numpy as np
     import torch
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_helpers import Dev
+    from paged_kv_scaled_amd.harness import Dev
     from paged_kv_scaled_amd import binding as B
 
     d = Dev(w, fill="zero")
@@ -175,8 +176,7 @@ def run_decode_step_bench(w, steps, warmup):
 def run_attention_bench(w, kind, steps, warmup, flush=False):
     """Per-launch event timing of one attention entry point (cache written untimed)."""
     import torch
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_helpers import Dev
+    from paged_kv_scaled_amd.harness import Dev
     from paged_kv_scaled_amd import binding as B
 
     d = Dev(w, fill="zero")
@@ -205,13 +205,30 @@ def run_attention_bench(w, kind, steps, warmup, flush=False):
         call()
         tm.stop(e)
     ms = tm.ms()
+    if kind == "decode":
+        # the same launches back to back between one event pair (inputs may stay in the
+        # caches between launches: reported beside the flushed figure, not instead of it)
+        tb = Timer()
+        e = tb.start()
+        for _ in range(steps):
+            call()
+        tb.stop(e)
+        ms_b2b = tb.ms()[0] / steps
+        # an empty event pair: what the pair itself adds to a per-launch figure
+        te = Timer()
+        for _ in range(steps):
+            e = te.start()
+            te.stop(e)
+        ms_pair = med(te.ms())
+    else:
+        ms_b2b = ms_pair = None
     # scatter of the whole batch as its own HBM workload
     ts = Timer()
     for _ in range(max(3, steps // 4)):
         e = ts.start()
         d.write(d.key, d.value, d.slots)
         ts.stop(e)
-    return ms, ts.ms()
+    return ms, ts.ms(), ms_b2b, ms_pair
 
 
 def run_mixed_bench(w, steps, warmup):
@@ -220,8 +237,7 @@ def run_mixed_bench(w, steps, warmup):
     decode of the generation sequences), both per step between event pairs, with the
     caches flushed from L2 and MALL before each step."""
     import torch
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_helpers import Dev
+    from paged_kv_scaled_amd.harness import Dev
     from paged_kv_scaled_amd import binding as B
 
     d = Dev(w, fill="zero")
@@ -274,8 +290,7 @@ def run_train_bench(w, steps, warmup, max_kv=16):
     """Per-launch event timing of the small-seq forward and backward (cache written untimed)."""
     import numpy as np
     import torch
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_helpers import Dev
+    from paged_kv_scaled_amd.harness import Dev
     from paged_kv_scaled_amd import binding as B
 
     d = Dev(w, fill="zero")
@@ -307,46 +322,145 @@ def med(xs):
     return xs[len(xs) // 2]
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """The fp64 oracle as it stands, one BLAS thread, timed on the host cores.
+def visible_keys_per_row(w):
+    """Visible keys of every flat query row (the count the prefill flops are made of)."""
+    import numpy as np
+    out = np.zeros(w.num_tokens, np.int64)
+    for s in range(w.num_seqs):
+        L, q = int(w.seq_lens[s]), int(w.q_lens[s])
+        a = np.arange(L - q, L, dtype=np.int64)
+        if w.mask == 0:
+            vis = np.full(q, L, np.int64)
+        elif w.mask == 1:
+            vis = np.minimum(L, a + 1)
+        elif w.mask == 2:
+            vis = np.minimum(L, (a // w.span_len + 1) * w.span_len)
+        else:
+            vis = a + 1
+            for (b, e) in w.spans[s]:
+                vis = np.where((a >= b) & (a < e), e, vis)
+            vis = np.minimum(L, vis)
+        r0 = int(w.cu_seqlens_q[s])
+        out[r0:r0 + q] = vis
+    return out
 
-    The sample is whole passes over the decode batch (every sequence, every head), repeated
-    until about budget_s seconds of oracle work have run; the widening of the storage bits
-    to fp64 happens once, outside the timed region.  Bytes counted per pass are the same
-    algorithmic bytes as the GPU figure (K/V rows, Q, O)."""
+
+def _host_cpu():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, budget_s=8.0):
+    """The fp64 oracle as it stands, timed on the host cores of this machine.
+
+    BLAS threads = the affinity count (the oracle's matrix products); its visibility
+    matrices and per-row softmax are Python loops and run on one thread.  The widening
+    of the storage bits to fp64 happens outside the timed region.
+
+    Headline (the `value` of this entry, the unit of the benchmark's metric): whole passes
+    over the decode batch (every sequence, every head) for about budget_s seconds,
+    bytes counted as for the GPU figure.  per_config: the same oracle on the other
+    workloads, each on a bounded sample (named in its entry) scaled to the workload's
+    metric: the tiny prefill whole (and its brute-force scalar twin), sampled query rows
+    of the chunked and long block-causal prefills (TFLOP/s of their visible pairs), a
+    sample of the small-seq sequences (GB/s of their K/V, Q and O)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import reference as ref
+    from paged_kv_scaled_amd import workloads as wl
 
-    q = ref.widen(w.query, w.dtype)
-    k = ref.split_logical(ref.widen(w.key, w.dtype), w.cu_seq_lens)
-    v = ref.split_logical(ref.widen(w.value, w.dtype), w.cu_seq_lens)
+    cores = len(os.sched_getaffinity(0))
     eb = 2 if w.dtype != "f32" else 4
-    pass_bytes = (int(w.seq_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * eb * 2
-                  + 2 * w.num_tokens * w.num_heads * w.head_dim * eb)
-    passes = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
+    res = {"unit": "GB/s", "cores": cores, "kind": "oracle", "host_cpu": _host_cpu(),
+           "threads_note": f"BLAS threads = {cores} (affinity count); the oracle's Python "
+                           "loops (visibility, per-row softmax) run on one thread"}
+    with threadpool_limits(limits=cores):
+        # ---- decode batch (the headline): whole passes ------------------------------
+        q = ref.widen(w.query, w.dtype)
+        k = ref.split_logical(ref.widen(w.key, w.dtype), w.cu_seq_lens)
+        v = ref.split_logical(ref.widen(w.value, w.dtype), w.cu_seq_lens)
+        pass_bytes = (int(w.seq_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * eb * 2
+                      + 2 * w.num_tokens * w.num_heads * w.head_dim * eb)
+        passes, t0 = 0, time.perf_counter()
         while True:
             ref.paged_attention(q, k, v, w.cu_seqlens_q, w.seq_lens, w.num_kv_heads, w.scale,
                                 w.mask, w.span_len)
             passes += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
-    el = time.perf_counter() - t0
-    model = None
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return dict(value=round(passes * pass_bytes / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                host_cpu=model, host_cores_available=len(os.sched_getaffinity(0)),
-                sample=f"{passes} full passes over the decode batch ({w.num_seqs} sequences, "
-                       f"{w.num_heads} heads), fp64 numpy, 1 BLAS thread, {el:.1f} s",
-                seconds=round(el, 2))
+        el = time.perf_counter() - t0
+        res.update(value=round(passes * pass_bytes / el / 1e9, 4),
+                   sample=f"{passes} full passes over the decode batch ({w.num_seqs} sequences, "
+                          f"{w.num_heads} heads), fp64 numpy, {el:.1f} s",
+                   seconds=round(el, 2))
+        per = {}
+        # ---- tiny prefill: whole, and the brute-force twin ---------------------------
+        t = wl.tiny_prefill()
+        tq = ref.widen(t.query, t.dtype)
+        tk = ref.split_logical(ref.widen(t.key, t.dtype), t.cu_seq_lens)
+        tv = ref.split_logical(ref.widen(t.value, t.dtype), t.cu_seq_lens)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            ref.paged_attention(tq, tk, tv, t.cu_seqlens_q, t.seq_lens, t.num_kv_heads, t.scale, t.mask,
+                                t.span_len)
+            reps += 1
+        vec_ms = (time.perf_counter() - t0) / reps * 1e3
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            ref.brute_force(tq, tk, tv, t.cu_seqlens_q, t.seq_lens, t.num_kv_heads, t.scale, t.mask,
+                            t.span_len)
+            reps += 1
+        bf_ms = (time.perf_counter() - t0) / reps * 1e3
+        per["tiny_prefill"] = {"value": round(vec_ms, 3), "unit": "ms per call",
+                               "brute_force_ms": round(bf_ms, 3), "sample": "the whole workload"}
+        # ---- prefill workloads: sampled query rows ----------------------------------
+        for name, gen in (("chunked_prefill", wl.chunked_prefill), ("long_block_causal", wl.long_block_causal)):
+            pw = gen()
+            pq = ref.widen(pw.query, pw.dtype)
+            pk = ref.split_logical(ref.widen(pw.key, pw.dtype), pw.cu_seq_lens)
+            pv = ref.split_logical(ref.widen(pw.value, pw.dtype), pw.cu_seq_lens)
+            vis = visible_keys_per_row(pw)
+            rng = np.random.default_rng(11)
+            n, spent, flops, rows_done = 8, 0.0, 0.0, 0
+            while spent < budget_s / 2 and rows_done < pw.num_tokens:
+                rows = np.sort(rng.choice(pw.num_tokens, min(n, pw.num_tokens), replace=False))
+                t0 = time.perf_counter()
+                ref.paged_attention(pq, pk, pv, pw.cu_seqlens_q, pw.seq_lens, pw.num_kv_heads, pw.scale,
+                                    pw.mask, pw.span_len, rows=rows)
+                spent += time.perf_counter() - t0
+                flops += 4.0 * pw.head_dim * pw.num_heads * float(vis[rows].sum())
+                rows_done += len(rows)
+                n *= 2
+            per[name] = {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s",
+                         "sample": f"{rows_done} random query rows (all heads) of {pw.num_tokens}, "
+                                   f"{spent:.1f} s", "seconds": round(spent, 2)}
+            del pq, pk, pv
+        # ---- small-seq: the first sequences ----------------------------------------
+        sw = wl.smallseq_varlen()
+        n, spent, by, seqs_done = 64, 0.0, 0, 0
+        while spent < budget_s / 2 and seqs_done < sw.num_seqs:
+            s0, s1 = seqs_done, min(seqs_done + n, sw.num_seqs)
+            k0, k1 = int(sw.cu_seq_lens[s0]), int(sw.cu_seq_lens[s1])
+            sq = ref.widen(sw.query[s0:s1], sw.dtype)
+            sk = ref.split_logical(ref.widen(sw.key[k0:k1], sw.dtype), sw.cu_seq_lens[s0:s1 + 1] - k0)
+            sv = ref.split_logical(ref.widen(sw.value[k0:k1], sw.dtype), sw.cu_seq_lens[s0:s1 + 1] - k0)
+            t0 = time.perf_counter()
+            ref.paged_attention(sq, sk, sv, np.arange(s1 - s0 + 1, dtype=np.int32), sw.seq_lens[s0:s1],
+                                sw.num_kv_heads, sw.scale, sw.mask, sw.span_len)
+            spent += time.perf_counter() - t0
+            by += (k1 - k0) * sw.num_kv_heads * sw.head_dim * 2 * 2 + 2 * (s1 - s0) * sw.num_heads * sw.head_dim * 2
+            seqs_done = s1
+            n *= 2
+        per["smallseq_varlen"] = {"value": round(by / spent / 1e9, 4), "unit": "GB/s",
+                                  "sample": f"the first {seqs_done} of {sw.num_seqs} sequences, {spent:.1f} s",
+                                  "seconds": round(spent, 2)}
+        res["per_config"] = per
+    return res
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
@@ -368,46 +482,84 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def gemm_ceiling(n=8192, reps=5):
-    """Achievable dense bf16 MFMA rate on this GPU: torch.matmul (hipBLASLt) on n x n x n
-    bf16, median of `reps` launches.  Context for the prefill fractions, not a target."""
+def _ceilings_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_scaled_amd", "libpkv_ceilings.so"))
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.pkv_ceiling_stream_read.argtypes = [P, SZ, P, I, I, P]
+    lib.pkv_ceiling_mfma.argtypes = [I, I, P, P, P]
+    return lib
+
+
+def stream_read_ceiling(nbytes=4 << 30, reps=4):
+    """Achievable HBM read rate: the ceiling kernel streams a 4 GiB buffer (16x the MALL)
+    with a small sweep of grid sizes and loads in flight; the best median is reported."""
+    import ctypes
     import torch
-    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
-    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
-    for _ in range(2):
-        torch.matmul(a, b)
-    tm = Timer()
-    for _ in range(reps):
-        e = tm.start()
-        torch.matmul(a, b)
-        tm.stop(e)
-    ms = med(tm.ms())
-    del a, b
+    lib = _ceilings_lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(7)
+    best = None
+    for blocks in (2048, 4096, 8192):
+        for unroll in (4, 8):
+            sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+            tm = Timer()
+            for _ in range(reps):
+                e = tm.start()
+                rc = lib.pkv_ceiling_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes // 16,
+                                                 ctypes.c_void_p(sink.data_ptr()), blocks, unroll, st)
+                tm.stop(e)
+                assert rc == 0, rc
+            gbs = nbytes / (med(tm.ms()) * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, blocks, unroll)
+    del buf
     torch.cuda.empty_cache()
-    return round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    return {"GBps": round(best[0], 1), "blocks": best[1], "loads_in_flight": best[2],
+            "note": "plain streaming read of 4 GiB (16-byte nontemporal loads), best of a grid sweep"}
+
+
+def mfma_ceiling(iters=4000, reps=3):
+    """Achievable bf16 MFMA rate: back-to-back v_mfma_f32_32x32x16_bf16 on four independent
+    accumulators, one workgroup of 4 waves per 256 threads; also the shader clock during
+    the loop (its clock counter against the 100 MHz constant counter)."""
+    import ctypes
+    import torch
+    lib = _ceilings_lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = None
+    for blocks in (256, 512):   # one and two waves per SIMD
+        sink = torch.zeros(blocks * 4, dtype=torch.float32, device="cuda")
+        clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+        tm = Timer()
+        for _ in range(reps):
+            e = tm.start()
+            rc = lib.pkv_ceiling_mfma(blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                      ctypes.c_void_p(clk.data_ptr()), st)
+            tm.stop(e)
+            assert rc == 0, rc
+        ms = med(tm.ms())
+        ticks, ref = (int(x) for x in clk.cpu().tolist())
+        tf = blocks * 4 * iters * 4 * 32768.0 / (ms * 1e-3) / 1e12
+        if best is None or tf > best[0]:
+            best = (tf, blocks, ticks, ref)
+    tf, blocks, ticks, ref = best
+    ghz = ticks / (ref / 100e6) / 1e9 if ref > 0 else None
+    return {"TFLOPs": round(tf, 1), "clock_GHz_during_loop": round(ghz, 3) if ghz else None,
+            "cycles_per_mfma": round(ticks / (iters * 4), 2) if ticks else None,
+            "TFLOPs_at_2.4GHz_equivalent": round(tf * 2.4 / ghz, 1) if ghz else None,
+            "note": f"back-to-back 32x32x16 bf16 MFMAs, 4 accumulators per wave, {blocks} "
+                    "workgroups of 4 waves (best of 1 and 2 waves per SIMD)"}
 
 
 def device_info():
-    """What the run was measured on: device properties, and the current core and memory
-    clock levels from the driver's sysfs DPM tables (files only: no helper program is
-    started from this GPU process)."""
-    import glob
+    """What the run was measured on (device properties; the clock under load is measured
+    by the MFMA ceiling loop, not read from an idle DPM level)."""
     import torch
     pr = torch.cuda.get_device_properties(0)
-    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
-            "memory_GB": round(pr.total_memory / 1e9, 1)}
-    clocks = {}
-    for kind in ("sclk", "mclk"):
-        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}")):
-            try:
-                cur = [l.strip() for l in open(f) if l.strip().endswith("*")]
-            except OSError:
-                continue
-            if cur:
-                clocks[kind] = cur[0]
-                break
-    info["clocks"] = clocks or None
-    return info
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None),
+            "compute_units": pr.multi_processor_count, "memory_GB": round(pr.total_memory / 1e9, 1)}
 
 
 DECODE_SOURCES = ("decode_device.h", "decode_mfma.h", "decode.hip", "common.h")
@@ -480,15 +632,20 @@ def run_workloads(args, names):
             torch.cuda.empty_cache()
             continue
         kind = "decode" if wk.decode else "prefill"
-        flush = kind == "prefill"
-        ms, sc_ms = run_attention_bench(wk, kind, args.steps, args.warmup, flush=flush)
+        # every launch timed after a 512 MB rewrite, so that neither L2 nor the MALL
+        # holds its inputs
+        ms, sc_ms, ms_b2b, ms_pair = run_attention_bench(wk, kind, args.steps, args.warmup, flush=True)
         m = med(ms)
-        entry = {"launch_us_median": round(m * 1e3, 2), "launch_us_min": round(min(ms) * 1e3, 2)}
+        entry = {"launch_us_median": round(m * 1e3, 2), "launch_us_min": round(min(ms) * 1e3, 2),
+                 "flushed": True}
         if kind == "decode":
             by = decode_bytes(wk)
             entry.update(metric="decode attn HBM GB/s", value=round(by / (m * 1e-3) / 1e9, 1),
                          unit="GB/s", frac_of_peak=round(by / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         bytes_per_launch=by)
+                         bytes_per_launch=by,
+                         event_pair_us=round(ms_pair * 1e3, 2),
+                         back_to_back_us=round(ms_b2b * 1e3, 2),
+                         back_to_back_GBps=round(by / (ms_b2b * 1e-3) / 1e9, 1))
         else:
             fl = prefill_flops(wk)
             tf = fl / (m * 1e-3) / 1e12
@@ -514,12 +671,12 @@ def main():
                     default="decode_batch,smallseq_varlen,chunked_prefill,long_block_causal,mixed_spans,"
                             "decode_batch_fp8,decode_long_seq,mixed_batch,smallseq_train")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--calibration-copy", action="store_true",
                     help="kept for old command lines: the 1 GiB device copy (the reference kernel "
                          "of the counter passes) now always runs")
     ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the measured copy and GEMM ceilings")
+                    help="skip the measured streaming-read and MFMA-loop ceilings")
     ap.add_argument("--workloads-only", action="store_true",
                     help="profiling runs: skip the default decode step (and the ceilings and "
                          "the CPU baseline) and print only the per-workload entries")
@@ -567,17 +724,26 @@ def main():
     result_wl = run_workloads(args, names)
 
     copy_gbs = copy_calibration()
-    gemm_tf = None if args.no_ceilings else gemm_ceiling()
-    roofline["frac_of_measured_copy_ceiling"] = round(achieved / copy_gbs, 4) if copy_gbs else None
-    for name, e in result_wl.items():
-        if e.get("unit") == "TFLOP/s" and gemm_tf:
-            e["frac_of_measured_gemm_ceiling"] = round(e["value"] / gemm_tf, 4)
+    ceil = None
+    if not args.no_ceilings:
+        log("measuring the ceilings")
+        ceil = {"hbm_read": stream_read_ceiling(), "mfma_bf16": mfma_ceiling()}
+        roofline["frac_of_measured_read_ceiling"] = round(achieved / ceil["hbm_read"]["GBps"], 4)
+        for name, e in result_wl.items():
+            if e.get("unit") == "TFLOP/s":
+                e["frac_of_measured_mfma_ceiling"] = round(e["value"] / ceil["mfma_bf16"]["TFLOPs"], 4)
+            elif e.get("metric", "").startswith("decode") and e.get("value"):
+                e["frac_of_measured_read_ceiling"] = round(e["value"] / ceil["hbm_read"]["GBps"], 4)
 
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
         cpu = cpu_baseline(w, args.cpu_seconds)
         cpu["gpu_over_cpu"] = round(value / cpu["value"], 1) if cpu["value"] > 0 else None
+        for name, e in cpu["per_config"].items():
+            g = result_wl.get(name)
+            if g and g.get("unit") == e["unit"] and e["value"] > 0:
+                e["gpu_over_cpu"] = round(g["value"] / e["value"], 1)
 
     line = {
         "metric": METRIC,
@@ -602,9 +768,10 @@ def main():
         "workloads": result_wl,
         "step_us_event_median": round(med(r["step_ms"]) * 1e3, 2),
     }
-    line["ceilings"] = {"copy_GBps": copy_gbs, "copy_note": "1 GiB device copy, read + write bytes",
-                        "bf16_gemm_TFLOPs": gemm_tf, "gemm_note": "torch.matmul 8192^3 bf16 (hipBLASLt)",
-                        "hbm_spec_GBps": HBM_PEAK_GBS, "bf16_spec_TFLOPs": BF16_PEAK_TFLOPS}
+    line["ceilings"] = dict(ceil or {}, hbm_spec_GBps=HBM_PEAK_GBS, bf16_spec_TFLOPs=BF16_PEAK_TFLOPS,
+                            counter_calibration_copy_GBps=copy_gbs,
+                            counter_calibration_note="1 GiB device copy (read + write bytes): the "
+                            "reference kernel of the FETCH_SIZE / WRITE_SIZE calibration")
     line["device"] = device_info()
     print(json.dumps(line), flush=True)
 
