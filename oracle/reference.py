@@ -199,15 +199,28 @@ def span_visible(p: int, a: int, seq_len: int, full_spans) -> bool:
 def visibility_matrix(positions: np.ndarray, seq_len: int, mask: int, span_len: int,
                       full_spans=None):
     """Boolean [len(positions), seq_len] matrix of is_visible (or, for SPANS, of
-    span_visible over this sequence's full spans), built entry by entry."""
-    vis = np.zeros((len(positions), seq_len), bool)
-    for i, a in enumerate(positions):
-        for p in range(seq_len):
-            if mask == MASK_SPANS:
-                vis[i, p] = span_visible(p, int(a), seq_len, full_spans)
-            else:
-                vis[i, p] = is_visible(p, int(a), seq_len, mask, span_len)
-    return vis
+    span_visible over this sequence's full spans).
+
+    The same rules as is_visible / span_visible, written over whole index grids (query
+    position a down the rows, key position p across the columns) so that long sequences
+    are feasible: NONE every p < L; CAUSAL p <= a; BLOCK_CAUSAL p <= a or p // span ==
+    a // span (the piecewise PR's dense reference); SPANS p <= a, or p and a inside the
+    same full span.  tests/test_oracle_pins.py holds it equal to the scalar rules entry
+    by entry."""
+    a = np.asarray(positions, np.int64).reshape(-1, 1)
+    p = np.arange(seq_len, dtype=np.int64).reshape(1, -1)
+    if mask == MASK_NONE:
+        return np.ones((a.shape[0], seq_len), bool)
+    if mask == MASK_CAUSAL:
+        return p <= a
+    if mask == MASK_BLOCK_CAUSAL:
+        return (p <= a) | ((p // span_len) == (a // span_len))
+    if mask == MASK_SPANS:
+        vis = p <= a
+        for (b, e) in (full_spans or []):
+            vis |= ((a >= b) & (a < e)) & ((p >= b) & (p < e))
+        return vis
+    raise ValueError(mask)
 
 
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray, scale: float):

@@ -469,41 +469,69 @@ def test_planted_wrong_gqa_head_map_is_caught(monkeypatch):
     assert _caught(test_full_prefill_equals_sdpa, ref.MASK_CAUSAL)
 
 
-def test_planted_top_left_causal_is_caught(monkeypatch):
-    orig = ref.is_visible
+def test_visibility_matrix_equals_the_scalar_rules():
+    """The grid form of the masks equals is_visible / span_visible entry by entry: every
+    mask, random chunk offsets, spans and lengths (including spans past the sequence)."""
+    rng = np.random.default_rng(77)
+    for _ in range(60):
+        L = int(rng.integers(1, 70))
+        q = int(rng.integers(1, L + 1))
+        pos = np.arange(L - q, L)
+        for mask in (ref.MASK_NONE, ref.MASK_CAUSAL, ref.MASK_BLOCK_CAUSAL, ref.MASK_SPANS):
+            span = int(rng.integers(1, 20))
+            spans = None
+            if mask == ref.MASK_SPANS:
+                cuts = np.sort(rng.choice(np.arange(0, L + 10), size=4, replace=False))
+                spans = [(int(cuts[0]), int(cuts[1])), (int(cuts[2]), int(cuts[3]))]
+            got = ref.visibility_matrix(pos, L, mask, span, spans)
+            want = np.zeros((q, L), bool)
+            for i, a in enumerate(pos):
+                for k in range(L):
+                    want[i, k] = (ref.span_visible(k, int(a), L, spans) if mask == ref.MASK_SPANS
+                                  else ref.is_visible(k, int(a), L, mask, span))
+            assert np.array_equal(got, want), (L, q, mask, span, spans)
 
-    def top_left(p, a, L, mask, span):
+
+def test_planted_top_left_causal_is_caught(monkeypatch):
+    orig = ref.visibility_matrix
+
+    def top_left(positions, L, mask, span, spans=None):
         # a chunk's row index instead of its absolute position: top-left alignment
-        if mask == ref.MASK_CAUSAL:
-            return p < L and p <= a - (L - 19 if L == 23 else 0)
-        return orig(p, a, L, mask, span)
-    monkeypatch.setattr(ref, "is_visible", top_left)
+        if mask == ref.MASK_CAUSAL and L == 23:
+            return orig(np.asarray(positions) - (L - 19), L, mask, span, spans)
+        return orig(positions, L, mask, span, spans)
+    monkeypatch.setattr(ref, "visibility_matrix", top_left)
     assert _caught(test_chunked_causal_is_bottom_right, 19)
 
 
 def test_planted_block_rule_off_by_one_is_caught(monkeypatch):
-    orig = ref.is_visible
+    orig = ref.visibility_matrix
 
-    def wrong(p, a, L, mask, span):
+    def wrong(positions, L, mask, span, spans=None):
         if mask == ref.MASK_BLOCK_CAUSAL:
-            return p < L and (p <= a or (p // span) == (a // span) + 1)
-        return orig(p, a, L, mask, span)
-    monkeypatch.setattr(ref, "is_visible", wrong)
+            a = np.asarray(positions).reshape(-1, 1)
+            p = np.arange(L).reshape(1, -1)
+            return (p <= a) | ((p // span) == (a // span) + 1)
+        return orig(positions, L, mask, span, spans)
+    monkeypatch.setattr(ref, "visibility_matrix", wrong)
     assert _caught(test_block_causal_equals_piecewise_segments)
 
 
 def test_planted_span_end_off_by_one_is_caught(monkeypatch):
-    orig = ref.full_span_of
+    orig = ref.visibility_matrix
 
-    def inclusive_end(pos, full_spans):
+    def inclusive_end(positions, L, mask, span, spans=None):
         # the span end taken as inclusive: one key past each image block leaks in
-        for i, (s, e) in enumerate(full_spans):
-            if s <= pos <= e:
-                return i
-        return None
-    monkeypatch.setattr(ref, "full_span_of", inclusive_end)
+        if mask == ref.MASK_SPANS:
+            a = np.asarray(positions).reshape(-1, 1)
+            p = np.arange(L).reshape(1, -1)
+            vis = p <= a
+            for (b, e) in spans or []:
+                vis |= ((a >= b) & (a <= e)) & ((p >= b) & (p <= e))
+            return vis
+        return orig(positions, L, mask, span, spans)
+    monkeypatch.setattr(ref, "visibility_matrix", inclusive_end)
     assert _caught(test_spans_equal_piecewise_segments, 0)
-    monkeypatch.setattr(ref, "full_span_of", orig)
 
 
 def test_planted_missing_scale_and_unstable_softmax_are_caught(monkeypatch):
