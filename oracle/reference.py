@@ -226,26 +226,29 @@ def visibility_matrix(positions: np.ndarray, seq_len: int, mask: int, span_len: 
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray, scale: float):
     """One sequence, one query head: q [n, D], k/v [L, D], vis [n, L] -> out [n, D], lse [n].
 
-    z = scale * q k^T (a matmul as a library step), excluded keys dropped, then the
-    stable softmax: subtract the row max, exponentiate, normalise.  A row with no
-    visible key gives zeros and lse = -inf (reading A6).
+    Only the keys some row sees and the rows that see some key take part (a key no row
+    sees is dropped whatever it holds).  z = scale * q k^T over them (a matmul as a
+    library step); a key a row cannot see gets -inf, so its weight below is exactly 0;
+    then the stable softmax row by row: subtract the row max over the visible keys,
+    exponentiate, normalise, and the weighted sum of the value rows (a matmul).  A row
+    with no visible key gives zeros and lse = -inf (reading A6).
     """
     n, D = q.shape
     out = np.zeros((n, v.shape[1]), np.float64)
     lse = np.full(n, -np.inf)
     if n == 0 or k.shape[0] == 0:
         return out, lse
-    z = scale * (q @ k.T)
-    for i in range(n):
-        sel = vis[i]
-        if not sel.any():
-            continue
-        zi = z[i, sel]
-        m = zi.max()
-        w = np.exp(zi - m)
-        l = w.sum()
-        out[i] = (w @ v[sel]) / l
-        lse[i] = m + math.log(l)
+    rows = vis.any(axis=1)
+    cols = vis.any(axis=0)
+    if not rows.any():
+        return out, lse
+    sub = vis[rows][:, cols]
+    z = np.where(sub, scale * (q[rows] @ k[cols].T), -np.inf)
+    m = z.max(axis=1, keepdims=True)
+    w = np.exp(z - m)                 # exp(-inf) = 0: keys the row cannot see weigh nothing
+    l = w.sum(axis=1)
+    out[rows] = (w @ v[cols]) / l[:, None]
+    lse[rows] = m[:, 0] + np.log(l)
     return out, lse
 
 
