@@ -429,7 +429,8 @@ int pkv_paged_attention_prefill_spans(void* out, const void* query, const int32_
  * extents.  The word stays set until pkv_check_device_error reads it.
  * (Spyre paged-attention PR: no host syncs in the forward, hence the checks run
  * on the device; CSA2 Vanilla golden PR: a failed call writes nothing.)
- * Duplicate slots within one kv_cache_write call are not detected. */
+ * Duplicate slots within one kv_cache_write call are detected by
+ * pkv_check_slots_unique (below), which needs a caller-owned bitmap. */
 typedef enum {
   PKV_CHECK_SLOT_RANGE = 1,  /* a slot >= num_blocks * block_size                    */
   PKV_CHECK_SEQ_LEN = 2,     /* seq_lens[s] < 0, > max_seq_len, or > max_blocks*B;   */
@@ -438,10 +439,33 @@ typedef enum {
   PKV_CHECK_TABLE = 4,       /* a used block_tables entry outside [0, num_blocks)    */
   PKV_CHECK_CU_Q = 8,        /* cu_seqlens_q: not from 0, decreasing, not ending at  */
                              /* num_tokens, or q_s > min(seq_lens[s], max_q_len)     */
-  PKV_CHECK_SPANS = 16       /* span lists: cu_spans not from 0 / decreasing / not   */
+  PKV_CHECK_SPANS = 16,      /* span lists: cu_spans not from 0 / decreasing / not   */
                              /* ending at num_spans, or a sequence's spans unsorted, */
                              /* overlapping, empty or starting below 0               */
+  PKV_CHECK_DUP_SLOT = 32    /* two tokens of one slot_mapping share a slot          */
 } pkv_check_bits;
+
+/* pkv_check_slots_unique -- the uniqueness precondition of pkv_kv_cache_write
+ * (two tokens of one call with the same slot race; the Spyre paged-attention PR,
+ * "Description", step 1, scatters each new token to its own slot).  Enqueues, on
+ * `stream`, a pass that sets one bit per valid slot of slot_mapping in `marks` and
+ * ORs PKV_CHECK_DUP_SLOT into the device error word when a bit was already set, then
+ * a pass that clears those bits again.  Run it before the kv_cache_write call it
+ * checks, on the same stream: with device checks on (pkv_set_device_checks) that
+ * write and every later call then write nothing until pkv_check_device_error reads
+ * the word; with checks off the bit still waits there for pkv_check_device_error.
+ *
+ * slot_mapping    int64 [num_tokens], as given to pkv_kv_cache_write; negative and
+ *                 out-of-range slots are skipped (the range check reports the latter).
+ * marks           device bitmap of at least ((num_blocks*block_size + 31) / 32) uint32
+ *                 words, 4-byte aligned, owned by the caller, ALL ZERO before the first
+ *                 call (for instance from hipMemset once); every call leaves it all zero.
+ *                 Calls sharing one bitmap must be ordered.
+ * Errors: INVALID_ARG for null pointers, num_tokens < 0, num_blocks or block_size out
+ * of range, or a bitmap that is too small or misaligned; LAUNCH if the device error
+ * word is unavailable.  num_tokens == 0 is a successful no-op. */
+int pkv_check_slots_unique(const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                           int32_t block_size, void* marks, size_t marks_bytes, void* stream);
 
 /* Turn the device-side checks on (enable != 0) or off for every later call in
  * this process.  Checks cost one small kernel per call.  Returns PKV_OK. */

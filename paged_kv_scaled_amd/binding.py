@@ -18,6 +18,7 @@ PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_LAU
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 PKV_MASK_NONE, PKV_MASK_CAUSAL, PKV_MASK_BLOCK_CAUSAL = 0, 1, 2
 PKV_CHECK_SLOT_RANGE, PKV_CHECK_SEQ_LEN, PKV_CHECK_TABLE, PKV_CHECK_CU_Q, PKV_CHECK_SPANS = 1, 2, 4, 8, 16
+PKV_CHECK_DUP_SLOT = 32
 
 # Every symbol include/pkv.h declares, with its ctypes signature.
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -61,6 +62,7 @@ SIGNATURES = {
                                                          _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                          _F, _P, _P, _I32, _I32, _I32,
                                                          ctypes.c_int, _P]),
+    "pkv_check_slots_unique": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _SZ, _P]),
     "pkv_set_device_checks": (ctypes.c_int, [ctypes.c_int]),
     "pkv_set_log": (ctypes.c_int, [ctypes.c_int]),
     "pkv_check_device_error": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32)]),
@@ -158,6 +160,16 @@ def kv_cache_write_fp8(key, value, slot_mapping, key_cache, value_cache, k_scale
                                       T, _ptr(key_cache), _ptr(value_cache), bstride, nb, bs, hkv,
                                       d, float(k_scale), float(v_scale), _dtype_code(key),
                                       _stream()))
+
+
+def check_slots_unique(slot_mapping, num_blocks: int, block_size: int, marks):
+    """Flag (in the device error word) a slot that slot_mapping holds twice.  marks: a
+    device bitmap of >= ceil(num_blocks * block_size / 32) int32 words, zero on entry and
+    left zero."""
+    lib = load()
+    _check(lib.pkv_check_slots_unique(_ptr(slot_mapping), slot_mapping.shape[0], num_blocks,
+                                      block_size, _ptr(marks),
+                                      marks.numel() * marks.element_size(), _stream()))
 
 
 def kv_cache_gather(key_out, value_out, cu_seq_lens, key_cache, value_cache, block_tables,

@@ -381,13 +381,37 @@ int pkv_check_device_error(void* stream, uint32_t* bits) {
       {PKV_CHECK_SEQ_LEN, "sequence length outside [0, min(max_seq_len, max_blocks_per_seq*block_size)]"},
       {PKV_CHECK_TABLE, "block_tables entry outside [0, num_blocks)"},
       {PKV_CHECK_CU_Q, "cu_seqlens_q inconsistent"},
-      {PKV_CHECK_SPANS, "span lists inconsistent"}};
+      {PKV_CHECK_SPANS, "span lists inconsistent"},
+      {PKV_CHECK_DUP_SLOT, "slot_mapping holds a slot twice"}};
   for (const auto& n : names) {
     if (!(v & n.bit)) continue;
     if (list[0]) strncat(list, "; ", sizeof(list) - strlen(list) - 1);
     strncat(list, n.name, sizeof(list) - strlen(list) - 1);
   }
   return fail(PKV_ERR_INVALID_ARG, "device checks failed (bits 0x%x): %s", v, list);
+}
+
+int pkv_check_slots_unique(const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                           int32_t block_size, void* marks, size_t marks_bytes, void* stream) {
+  clear_error();
+  const char* what = "pkv_check_slots_unique";
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "%s: num_tokens must be >= 0 (got %d)", what, num_tokens);
+  if (num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "%s: num_blocks must be > 0 (got %d)", what, num_blocks);
+  if (!is_pow2_in(block_size, 1, 256))
+    return fail(PKV_ERR_INVALID_ARG, "%s: block_size must be a power of two in [1, 256] (got %d)",
+                what, block_size);
+  if (num_tokens == 0) return PKV_OK;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  const size_t need = (size_t)((num_slots + 31) / 32) * sizeof(uint32_t);
+  if (!slot_mapping || !marks)
+    return fail(PKV_ERR_INVALID_ARG, "%s: slot_mapping and marks must not be NULL", what);
+  if (marks_bytes < need || !aligned(marks, 4))
+    return fail(PKV_ERR_INVALID_ARG, "%s: marks must be a 4-byte aligned bitmap of at least %zu "
+                "bytes (got %zu at %p)", what, need, marks_bytes, marks);
+  return launched(pkv::launch_check_duplicate_slots(slot_mapping, num_tokens, num_slots,
+                                                    static_cast<uint32_t*>(marks),
+                                                    (hipStream_t)stream),
+                  what);
 }
 
 int pkv_kv_cache_write(const void* key, const void* value, int64_t kv_token_stride,

@@ -80,6 +80,36 @@ check_seqs_kernel(const CheckSeqArgs a, uint32_t* word) {
   if (bits != 0 && lane == 0) atomicOr(word, bits);
 }
 
+// Duplicate slots of one kv_cache_write call (two tokens with one slot race in the
+// scatter): one bit per cache slot in a caller-owned bitmap, all clear between calls.
+// Pass 1 sets each valid slot's bit and flags a bit that was already set; pass 2, a
+// separate launch on the same stream, clears the bits again.  Negative and
+// out-of-range slots are skipped (the range check covers the latter).
+__global__ void __launch_bounds__(kCheckThreads)
+mark_slots_kernel(const int64_t* __restrict__ slots, int32_t n, int64_t num_slots,
+                  uint32_t* __restrict__ marks, uint32_t* word) {
+  bool dup = false;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) {
+    const int64_t sl = slots[i];
+    if (sl < 0 || sl >= num_slots) continue;
+    const uint32_t bit = 1u << (sl & 31);
+    dup |= (atomicOr(marks + (sl >> 5), bit) & bit) != 0u;
+  }
+  if (__any(dup) && (threadIdx.x & (kWave - 1)) == 0) atomicOr(word, (uint32_t)PKV_CHECK_DUP_SLOT);
+}
+
+__global__ void __launch_bounds__(kCheckThreads)
+clear_slots_kernel(const int64_t* __restrict__ slots, int32_t n, int64_t num_slots,
+                   uint32_t* __restrict__ marks) {
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) {
+    const int64_t sl = slots[i];
+    if (sl < 0 || sl >= num_slots) continue;
+    atomicAnd(marks + (sl >> 5), ~(1u << (sl & 31)));
+  }
+}
+
 // Move the word into g_check_taken and clear it, in one atomic step.
 __global__ void take_word_kernel(uint32_t* word, uint32_t* taken) {
   if (threadIdx.x == 0) *taken = atomicExch(word, 0u);
@@ -135,6 +165,22 @@ hipError_t launch_check_seqs(const CheckSeqArgs& a, hipStream_t stream) {
   const int per_block = kCheckThreads / kWave;
   const int blocks = (a.num_seqs + per_block - 1) / per_block;
   hipLaunchKernelGGL(check_seqs_kernel, dim3(blocks), dim3(kCheckThreads), 0, stream, a, s.word);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_duplicate_slots(const int64_t* slots, int32_t n, int64_t num_slots,
+                                        uint32_t* marks, hipStream_t stream) {
+  Symbols s;
+  if (!symbols(s)) return hipErrorInvalidSymbol;
+  if (n <= 0) return hipSuccess;
+  const int64_t want = ((int64_t)n + kCheckThreads - 1) / kCheckThreads;
+  const int blocks = (int)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(mark_slots_kernel, dim3(blocks), dim3(kCheckThreads), 0, stream, slots, n,
+                     num_slots, marks, s.word);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(clear_slots_kernel, dim3(blocks), dim3(kCheckThreads), 0, stream, slots, n,
+                     num_slots, marks);
   return hipGetLastError();
 }
 

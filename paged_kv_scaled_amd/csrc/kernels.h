@@ -87,6 +87,10 @@ const uint32_t* check_guard();
 hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t num_slots, hipStream_t stream);
 hipError_t launch_check_seqs(const CheckSeqArgs& a, hipStream_t stream);
 hipError_t take_check_word(hipStream_t stream, uint32_t* bits);
+// Duplicate-slot check of one slot_mapping over a caller bitmap of ceil(num_slots / 32)
+// words that is all zero on entry and left all zero (two launches).
+hipError_t launch_check_duplicate_slots(const int64_t* slots, int32_t n, int64_t num_slots,
+                                        uint32_t* marks, hipStream_t stream);
 
 // Decode split plan: a pure function of the sizes, shared by the workspace query
 // and the launch so that both agree.

@@ -71,6 +71,30 @@ def test_write_rejections(lib):
     assert B.last_error() == ""
 
 
+def _slots_unique(lib, **kw):
+    a = dict(slots=FAKE, T=4, nb=8, bs=16, marks=FAKE, mbytes=16)
+    a.update(kw)
+    return lib.pkv_check_slots_unique(a["slots"], a["T"], a["nb"], a["bs"], a["marks"],
+                                      a["mbytes"], NULL)
+
+
+def test_slots_unique_rejections(lib):
+    """Argument checks of the duplicate-slot check (8 blocks of 16 slots -> 4 words, 16 bytes)."""
+    assert _slots_unique(lib, slots=NULL) == B.PKV_ERR_INVALID_ARG
+    assert "NULL" in B.last_error()
+    assert _slots_unique(lib, marks=NULL) == B.PKV_ERR_INVALID_ARG
+    assert _slots_unique(lib, mbytes=15) == B.PKV_ERR_INVALID_ARG
+    assert "16 bytes" in B.last_error()
+    assert _slots_unique(lib, nb=9) == B.PKV_ERR_INVALID_ARG       # 144 slots need 20 bytes
+    assert _slots_unique(lib, marks=ctypes.c_void_p(FAKE.value + 2)) == B.PKV_ERR_INVALID_ARG
+    assert "aligned" in B.last_error()
+    assert _slots_unique(lib, bs=12) == B.PKV_ERR_INVALID_ARG
+    assert _slots_unique(lib, nb=0) == B.PKV_ERR_INVALID_ARG
+    assert _slots_unique(lib, T=-1) == B.PKV_ERR_INVALID_ARG
+    assert _slots_unique(lib, T=0, slots=NULL, marks=NULL) == B.PKV_OK
+    assert B.last_error() == ""
+
+
 def _decode(lib, **kw):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bstride=16 * 8 * 128, bt=FAKE, mb=256, sl=FAKE,
              S=64, H=32, Hkv=8, D=128, nb=9000, bs=16, scale=0.088, maxL=4096, ws=FAKE, wsb=0,

@@ -242,3 +242,34 @@ def test_checks_cover_smallseq_backward(checks):
     assert bits == B.PKV_CHECK_SEQ_LEN
     torch.cuda.synchronize()
     assert bool(torch.all(dq == 8.0)) and bool(torch.all(dk == 8.0)) and bool(torch.all(dv == 8.0))
+
+
+def test_checks_flag_duplicate_slot(checks):
+    """pkv_check_slots_unique before a write: unique slots (one padding token, slot -1) leave
+    no bit; a slot held twice sets PKV_CHECK_DUP_SLOT and the guarded write after it writes
+    nothing.  Every call leaves the bitmap all zero."""
+    w = wl.random_small(5, "bf16", head_dim=64)
+    d = Dev(w)
+    nslots = w.num_blocks * w.block_size
+    marks = torch.zeros((nslots + 31) // 32 + 3, dtype=torch.int32, device="cuda")
+    slots = d.slots.clone()
+    slots[0] = -1
+    B.check_slots_unique(slots, w.num_blocks, w.block_size, marks)
+    assert B.check_device_error() == (0, "")
+    assert int(marks.count_nonzero()) == 0
+    slots = d.slots.clone()
+    slots[-1] = slots[len(slots) // 2]
+    B.check_slots_unique(slots, w.num_blocks, w.block_size, marks)
+    B.kv_cache_write(d.key, d.value, slots, d.kc, d.vc)
+    bits, msg = B.check_device_error()
+    assert bits == B.PKV_CHECK_DUP_SLOT and "twice" in msg
+    torch.cuda.synchronize()
+    assert int(marks.count_nonzero()) == 0
+    assert torch.isnan(d.kc).all() and torch.isnan(d.vc).all()        # nothing written
+    # with checks off the bit is still recorded, and read once
+    B.set_device_checks(False)
+    B.check_slots_unique(slots, w.num_blocks, w.block_size, marks)
+    bits, _ = B.check_device_error()
+    assert bits == B.PKV_CHECK_DUP_SLOT
+    assert B.check_device_error() == (0, "")
+    assert int(marks.count_nonzero()) == 0
