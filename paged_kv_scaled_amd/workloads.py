@@ -264,11 +264,13 @@ def smallseq_train(seed: int = 7, num_seqs: int = 30720, dtype: str = "bf16",
 
 
 def long_block_causal(seed: int = 4, num_seqs: int = 4, seq_len: int = 8192, dtype: str = "bf16",
-                      num_heads: int = 64, spare_blocks: int = 1) -> Workload:
-    """4 x 8192 tokens, 64 q heads / 8 kv heads, D 128, B 16, block-causal spans of 2048."""
+                      num_heads: int = 64, spare_blocks: int = 1, num_kv_heads: int = 8) -> Workload:
+    """4 x 8192 tokens, 64 q heads / 8 kv heads, D 128, B 16, block-causal spans of 2048.
+    (num_heads = 8, num_kv_heads = 1 is one GPU's share when the kv heads are split over
+    eight GPUs.)"""
     rng = np.random.default_rng(seed)
     lens = np.full(num_seqs, seq_len, np.int32)
-    return build("long_block_causal", seed, dtype, lens, lens, num_heads, 8, 128, 16,
+    return build("long_block_causal", seed, dtype, lens, lens, num_heads, num_kv_heads, 128, 16,
                  MASK_BLOCK_CAUSAL, span_len=2048, spare_blocks=spare_blocks, rng=rng)
 
 

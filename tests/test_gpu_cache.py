@@ -106,3 +106,33 @@ def test_scatter_full_size_smallseq(gpu):
     free = [b for b in range(w.num_blocks) if b not in used]
     for b in free:
         assert np.all(bits_of(d.kc[b]) == wl.nan_bits("bf16"))
+
+
+FULL = {
+    "decode_batch": wl.decode_batch,
+    "chunked_prefill": wl.chunked_prefill,
+    "long_block_causal": wl.long_block_causal,
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_scatter_and_gather_full_size_bit_exact(gpu, name):
+    """The full decode batch (about 140k tokens), chunked prefill and long block-causal
+    (32768 tokens x 8 kv heads) caches: every byte of both caches equals the oracle's
+    scatter model (written rows and the untouched NaN sentinels alike), and the exported
+    gather of every sequence returns the generator's logical rows bit for bit."""
+    w = FULL[name]()
+    print(f"full-size scatter/gather: {name} tokens={w.key.shape[0]}", flush=True)
+    d = Dev(w)
+    d.write_all()
+    torch.cuda.synchronize()
+    ek, ev = _expected_cache(w)
+    assert np.array_equal(bits_of(d.kc), ek)
+    assert np.array_equal(bits_of(d.vc), ev)
+    del ek, ev
+    ko = torch.zeros_like(d.key)
+    vo = torch.zeros_like(d.value)
+    B.kv_cache_gather(ko, vo, d.cu_k, d.kc, d.vc, d.tables, w.max_seq_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(ko), w.key)
+    assert np.array_equal(bits_of(vo), w.value)

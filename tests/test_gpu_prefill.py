@@ -75,6 +75,16 @@ def test_long_block_causal_sampled(gpu):
     _run(w, rows=np.array(sorted(set(rows))), heads=heads)
 
 
+@pytest.mark.timeout(600)
+def test_long_block_causal_one_gpu_share_every_row(gpu):
+    """One GPU's share of the long block-causal prefill when its 8 kv heads are split over
+    eight GPUs: 4 x 8192 tokens, 8 q heads / 1 kv head, spans of 2048 (the same kernel at
+    the per-GPU shape).  Every output row and head is compared with the oracle."""
+    w = wl.long_block_causal(num_heads=8, num_kv_heads=1)
+    print(f"long block-causal per-GPU share: tokens={w.num_tokens} heads={w.num_heads}", flush=True)
+    _run(w)
+
+
 def test_block_causal_span_one_equals_causal(gpu):
     w = wl.chunked_prefill(seed=40, num_seqs=3, ctx_hi=100, q_lo=5, q_hi=90)
     d = Dev(w)
