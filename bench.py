@@ -232,10 +232,11 @@ def run_attention_bench(w, kind, steps, warmup, flush=False):
 
 
 def run_mixed_bench(w, steps, warmup):
-    """The mixed batch through paged_attention_mixed (one attention launch plus the split
-    merge) against the same rows as two calls (prefill of the context sequences, then
-    decode of the generation sequences), both per step between event pairs, with the
-    caches flushed from L2 and MALL before each step."""
+    """The mixed batch through paged_attention_mixed (one call: the prefill launch over the
+    context rows, then the decode launches over the generation rows) against the same rows
+    as two calls (prefill of the context sequences, then decode of the generation
+    sequences), both per step between event pairs, with the caches flushed from L2 and
+    MALL before each step."""
     import torch
     from paged_kv_scaled_amd.harness import Dev
     from paged_kv_scaled_amd import binding as B

@@ -300,10 +300,10 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* query, const int32_t*
 
 /*
  * Mixed batch -- one step's context rows (prefill / chunked prefill) and
- * generation rows (single-token decode) in one call and one attention launch
- * (plus a small merge launch when a generation sequence is cut into several
- * pieces).  The launch's first blocks are prefill workgroups and the rest
- * decode waves, so the decode work starts on the CUs the prefill tail frees.
+ * generation rows (single-token decode) in one call: the prefill kernel over
+ * the context rows, then the decode kernels over the generation rows, enqueued
+ * on `stream` in that order (results and speed equal to the two calls
+ * pkv_paged_attention_prefill + pkv_paged_attention_decode on the two parts).
  * The Spyre paged-attention PR ("Description") sends the prefill and decode
  * sequences of a step through one attention call; the CSA2 Vanilla golden PR
  * ("Description") orders a batch context first, generation after, and keeps
@@ -320,13 +320,12 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* query, const int32_t*
  * seq_lens        int32 [num_seqs]; block_tables int32 [num_seqs, max_blocks_per_seq].
  * max_q_len       host hint >= every context chunk length (0 without context rows).
  * workspace       device buffer of pkv_mixed_workspace_size(num_seqs -
- *                 num_ctx_seqs, ...) bytes, 16-byte aligned (may be NULL when
- *                 that is 0).
+ *                 num_ctx_seqs, ...) bytes (the decode workspace of the
+ *                 generation rows, pkv_decode_workspace_size of the same
+ *                 arguments), 16-byte aligned (may be NULL when that is 0).
  *                 Contents need no initialisation; calls sharing one workspace
  *                 must be ordered.
- * bf16/fp16 with head_dim 64 or 128 and scale > 0 run as one launch; other
- * cases run the vector-ALU prefill and then the decode (same results, two
- * launches).  Errors: as pkv_paged_attention_prefill and
+ * Errors: as pkv_paged_attention_prefill and
  * pkv_paged_attention_decode, plus INVALID_ARG for an inconsistent boundary.
  */
 size_t pkv_mixed_workspace_size(int32_t num_gen_seqs, int32_t num_heads, int32_t num_kv_heads,

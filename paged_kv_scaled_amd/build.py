@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 LIB_CEILINGS = os.path.join(PKG, "libpkv_ceilings.so")
 CEILING_SOURCES = ["ceilings.hip"]
 
-SOURCES = ["api.cpp", "scatter.hip", "decode.hip", "prefill_valu.hip", "prefill_mfma.hip", "mixed.hip",
+SOURCES = ["api.cpp", "scatter.hip", "decode.hip", "prefill_valu.hip", "prefill_mfma.hip",
            "smallseq.hip", "checks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

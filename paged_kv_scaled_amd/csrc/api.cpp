@@ -651,7 +651,7 @@ size_t pkv_mixed_workspace_size(int32_t num_gen_seqs, int32_t num_heads, int32_t
       !PKV_HEAD_DIM_SUPPORTED(head_dim) || !is_pow2_in(block_size, 1, 256) || max_seq_len < 0)
     return 0;
   return pkv::decode_plan(num_gen_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                          max_seq_len, true)
+                          max_seq_len)
       .workspace_bytes;
 }
 
@@ -711,8 +711,7 @@ int pkv_paged_attention_mixed(void* out, const void* query, const int32_t* cu_se
                                  dtype == PKV_F32 ? 4 : 2)) != PKV_OK)
     return rc;
   const pkv::DecodePlan plan = pkv::decode_plan(num_gen > 0 ? num_gen : 1, num_heads,
-                                                num_kv_heads, head_dim, block_size, max_seq_len,
-                                                true);
+                                                num_kv_heads, head_dim, block_size, max_seq_len);
   if (num_gen > 0 && plan.workspace_bytes > 0 &&
       (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(PKV_ERR_WORKSPACE, "mixed-batch workspace of %zu bytes required (got %zu at %p)",
@@ -771,12 +770,14 @@ int pkv_paged_attention_mixed(void* out, const void* query, const int32_t* cu_se
       if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream), what)) != PKV_OK) return rc;
     }
   }
-  if (pkv::mixed_fused_supported((int)dtype, head_dim, scale, false))
-    return launched(pkv::launch_mixed(ctx, gen, plan, (hipStream_t)stream), what);
-  // fp32 or head_dim 16: the vector-ALU prefill, then split-mode decode (two launches)
-  if (num_ctx_seqs > 0 && num_ctx_tokens > 0 &&
-      (rc = launched(pkv::launch_prefill_valu(ctx, (hipStream_t)stream), what)) != PKV_OK)
-    return rc;
+  // the context rows through the prefill kernel, then the generation rows through the
+  // decode kernels, on the caller's stream
+  if (num_ctx_seqs > 0 && num_ctx_tokens > 0) {
+    const hipError_t e = pkv::prefill_mfma_supported((int)dtype, head_dim, scale)
+                             ? pkv::launch_prefill_mfma(ctx, (hipStream_t)stream)
+                             : pkv::launch_prefill_valu(ctx, (hipStream_t)stream);
+    if ((rc = launched(e, what)) != PKV_OK) return rc;
+  }
   if (num_gen > 0) return launched(pkv::launch_decode(gen, plan, (hipStream_t)stream), what);
   return PKV_OK;
 }

@@ -181,11 +181,10 @@ void launch_all(const DecodeParams& dp, const DecodePlan& pl, int d, bool merge,
 }  // namespace
 
 DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                       int block_size, int max_seq_len, bool mixed) {
+                       int block_size, int max_seq_len) {
   DecodePlan pl{};
   const int g = num_kv_heads > 0 ? num_heads / num_kv_heads : 1;
   pl.heads_per_wave = heads_per_wave(g);
-  if (mixed && pl.heads_per_wave > 4) pl.heads_per_wave = 4;
   pl.groups_per_kv = (g + pl.heads_per_wave - 1) / pl.heads_per_wave;
   const int64_t groups = (int64_t)num_kv_heads * pl.groups_per_kv;
   // Split mode: splits of >= 256 keys within 64 blocks, lengthened until the item count
@@ -203,15 +202,13 @@ DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
   // sequences every wave scans the lengths itself; beyond, a planning kernel writes
   // prefix sums and range starts for the waves to read.  Measured (interleaved A/B, 32 q
   // / 8 kv heads, D 128): 1024 sequences of <= 1024 keys 5.26 -> 5.92 TB/s and 512 of
-  // <= 2048 keys 5.97 -> 6.16 TB/s with the tables; 256 sequences equal either way.  A
-  // mixed batch, whose one launch leaves no room for the planning kernel, scans up to
-  // kStreamMaxSeqs generation sequences and takes split mode beyond.
-  pl.stream = pl.num_splits > 1 && (!mixed || num_seqs <= kStreamMaxSeqs);
-  pl.prefix = pl.stream && !mixed && num_seqs > kStreamScanSeqs;
-  const int waves = device_shape().cus * (mixed ? kStreamWavesPerCuMixed : kStreamWavesPerCu);
+  // <= 2048 keys 5.97 -> 6.16 TB/s with the tables; 256 sequences equal either way.
+  pl.stream = pl.num_splits > 1;
+  pl.prefix = pl.stream && num_seqs > kStreamScanSeqs;
+  const int waves = device_shape().cus * kStreamWavesPerCu;
   pl.num_ranges = pl.stream ? (int)(waves / groups > 1 ? waves / groups : 1) : 0;
   // A workgroup per (sequence, head) merges where a sequence averages 16 ranges or more.
-  pl.wide_merge = pl.stream && !mixed && (int64_t)num_seqs * 16 <= pl.num_ranges;
+  pl.wide_merge = pl.stream && (int64_t)num_seqs * 16 <= pl.num_ranges;
   const size_t slots = pl.stream ? (size_t)num_heads * pl.num_ranges * 2
                                  : (pl.num_splits > 1 ? (size_t)num_seqs * num_heads * pl.num_splits : 0);
   pl.workspace_bytes = slots * (size_t)head_dim * sizeof(float) + slots * 2 * sizeof(float);

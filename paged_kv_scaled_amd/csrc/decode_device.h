@@ -30,10 +30,9 @@
 //    leaves (acc, m, l) partials that the merge kernel combines.  Up to kStreamScanSeqs
 //    sequences each wave finds its range's first sequence by scanning the lengths;
 //    beyond, a one-block planning kernel writes the length prefix sums and every range's
-//    first sequence into the workspace, and the waves read them (a mixed batch, which
-//    has no room for the planning launch, scans up to kStreamMaxSeqs);
-//  * split mode (every sequence within one split, or the generation rows of a mixed
-//    batch beyond kStreamMaxSeqs): fixed splits of split_len keys per sequence, waves
+//    first sequence into the workspace, and the waves read them;
+//  * split mode (every sequence within one split): fixed splits of split_len keys per
+//    sequence, waves
 //    walk (sequence, split, head group) items in a grid-stride loop; sequences with one
 //    split are written directly.
 // The merge combines one (sequence, head)'s partials by their log-sum-exp weights: one wave
@@ -53,12 +52,8 @@ constexpr int kWavesPerBlock = kDecodeThreads / kWave;
 constexpr float kLazyRescale = 8.0f;   // log2 units
 constexpr int kStreamScanSeqs = 256;   // plain decode: up to here every stream wave scans
                                        // seq_lens, beyond the planning kernel's tables
-constexpr int kStreamMaxSeqs = 1024;   // mixed batch (no planning kernel): stream mode up to
-                                       // here, scanned by every wave; split mode beyond
 constexpr int kStreamWavesPerCu = 4;       // waves of the stream grid (all head groups): one
                                            // wave per SIMD (1024 on a whole MI355X)
-constexpr int kStreamWavesPerCuMixed = 8;  // the same inside the mixed-batch kernel, whose
-                                           // decode blocks hold 8 waves (two per SIMD)
 constexpr int kStreamMinRange = 64;    // shortest range, keys
 
 template <typename T, int D>

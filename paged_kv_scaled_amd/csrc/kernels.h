@@ -109,10 +109,8 @@ struct DecodePlan {
   int max_seq_len;
   size_t workspace_bytes;
 };
-// mixed: the plan of the decode rows of a mixed batch -- at most 4 heads per wave (they run
-// inside the prefill kernel's register budget).
 DecodePlan decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                       int block_size, int max_seq_len, bool mixed = false);
+                       int block_size, int max_seq_len);
 
 // The current device's shape, read once per device from its properties: compute units,
 // and XCDs (chiplets of 32 CUs on gfx950, so 8 on a whole MI355X, fewer on a partition).
@@ -168,11 +166,5 @@ hipError_t decode_scratch(void** ptr);
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_valu(const AttnArgs& a, hipStream_t stream);
 bool prefill_mfma_supported(int dtype, int head_dim, float scale);
-// Mixed batch in one launch (plus the split merge): ctx holds the context sequences (THD
-// rows from 0), gen the generation sequences (one row each, pointers already offset);
-// plan from decode_plan(..., mixed = true) for gen.
-bool mixed_fused_supported(int dtype, int head_dim, float scale, bool kv_fp8);
-hipError_t launch_mixed(const AttnArgs& ctx, const AttnArgs& gen, const DecodePlan& plan,
-                        hipStream_t stream);
 
 }  // namespace pkv
