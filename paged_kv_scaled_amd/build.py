@@ -42,7 +42,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
 _MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]
 # The decode kernels' matrix-core core keeps its accumulators in VGPRs for the same reason,
 # but stays in IEEE mode: decode results with NaN inputs are defined (NaN rows).
-EXTRA = {"prefill_mfma.hip": _MFMA_FLAGS, "mixed.hip": _MFMA_FLAGS,
+EXTRA = {"prefill_mfma.hip": _MFMA_FLAGS,
          "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

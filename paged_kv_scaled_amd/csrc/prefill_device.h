@@ -40,6 +40,7 @@ constexpr int kWaves = 8;          // waves per workgroup: 2 per SIMD
 constexpr int kBN = 64;            // keys per tile
 constexpr int kTableChunk = 1024;  // page ids staged in LDS at a time
 constexpr float kLazy = 8.0f;
+static_assert(kTableChunk % (kWaves * 64) == 0, "page-id staging: whole loads per thread");
 
 struct PrefillParams {
   void* out;
@@ -57,6 +58,7 @@ struct PrefillParams {
   int32_t ngroups;                            // (sequence, kv head, head group) groups
   int32_t nxcd;                               // XCDs of the device (workgroup dealing)
   int32_t rank_items;                         // order each XCD's query tiles longest first
+  int32_t rank_bits;                          // bits of (key tiles per query tile + 2)
   float scale_log2;                           // scale * log2(e) (times k_scale for FP8)
   float out_scale;                            // v_scale for an FP8 cache, else 1
   const uint32_t* guard;                      // device error word when checks are on
@@ -141,6 +143,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   const int xcd = bid % nx;
   const int slot = bid / nx;
   int grp, qt;
+  int q0 = 0, qn = 0, Ls = 0;   // the sequence's first query row, chunk length, key count
+  bool have_lens = false;
   if (p.rank_items) {
     // Few workgroups per CU: the order in which an XCD starts its query tiles sets the
     // makespan (a long tile started late finishes last), so each XCD starts them longest
@@ -148,30 +152,47 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
     // one per lane, by their key tiles, and the workgroup takes the item of rank `slot`.
     const int items = ((p.ngroups + nx - 1) / nx) * p.qtiles;   // <= 64 (host)
     int cnt = -2;                     // lanes past the items rank last
+    int c0 = 0, n = 0, L = 0;
     if (lane < items) {
       cnt = -1;                       // an empty query tile ranks after every real one
       const int g = (lane / p.qtiles) * nx + xcd;
       if (g < p.ngroups) {
         const int sq = g / (p.head_groups * p.Hkv);
-        const int c0 = p.cu_q[sq], n = p.cu_q[sq + 1] - c0;
+        c0 = p.cu_q[sq];
+        n = p.cu_q[sq + 1] - c0;
+        L = p.seq_lens[sq];
         const int r0 = (lane % p.qtiles) * (32 << p.rb_log2);
         if (r0 < n) {
-          const int L = p.seq_lens[sq];
           const int z0 = p.cu_spans ? p.cu_spans[sq] : 0, z1 = p.cu_spans ? p.cu_spans[sq + 1] : 0;
           const int last = min(r0 + (32 << p.rb_log2), n) - 1;
           cnt = (visible_end(p.mask, L - n + last, L, p.span, p.full_spans, z0, z1) + kBN - 1) / kBN;
         }
       }
     }
+    // rank = lanes with a larger count, plus lanes with an equal count and a lower index
+    // (a permutation of 0..63), by a most-significant-bit-first radix pass over ballots:
+    // `eq` keeps the lanes whose count agrees with this lane's on the bits seen so far
+    const uint32_t key = (uint32_t)(cnt + 2);
+    uint64_t eq = ~0ull;
     int rank = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int cj = __builtin_amdgcn_readlane(cnt, j);
-      rank += (cj > cnt || (cj == cnt && j < lane)) ? 1 : 0;
+    for (int b = p.rank_bits - 1; b >= 0; --b) {
+      const bool bit = (key >> b) & 1u;
+      const uint64_t ones = __ballot(bit);
+      const uint64_t agree = bit ? (eq & ones) : (eq & ~ones);
+      if (!bit) rank += __builtin_popcountll(eq & ones);
+      eq = agree;
     }
+    rank += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
     const uint64_t hit = __ballot(rank == slot);
     const int who = hit ? (int)__builtin_ctzll(hit) : 0;
     grp = (who / p.qtiles) * nx + xcd;
     qt = who % p.qtiles;
+    // the lane that ranked the item already holds its sequence's lengths
+    q0 = __builtin_amdgcn_readlane(c0, who);
+    qn = __builtin_amdgcn_readlane(n, who);
+    Ls = __builtin_amdgcn_readlane(L, who);
+    have_lens = true;
   } else {
     // inside a group the longest query tiles start first
     grp = (slot / p.qtiles) * nx + xcd;
@@ -183,13 +204,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   rest /= p.head_groups;
   const int kvh = rest % p.Hkv;
   const int s = rest / p.Hkv;
-  const int q0 = p.cu_q[s];
-  const int qn = p.cu_q[s + 1] - q0;
+  if (!have_lens) {
+    q0 = p.cu_q[s];
+    qn = p.cu_q[s + 1] - q0;
+    Ls = p.seq_lens[s];
+  }
   const int RB = 1 << p.rb_log2;
   const int wg_rows = 32 * RB;
   const int row0 = qt * wg_rows;
   if (row0 >= qn) return;
-  const int Ls = p.seq_lens[s];
   const int ctx = Ls - qn;
   const int sp0 = p.cu_spans ? p.cu_spans[s] : 0, sp1 = p.cu_spans ? p.cu_spans[s + 1] : 0;
 
@@ -212,15 +235,24 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   // no row of the wave sees are still computed: their probabilities are exactly 0
   // (every row saw key 0 in the first tile, so the running max is finite), and the
   // accumulators stay free of branch copies.
+  // (the visible end never decreases with the row, so it is lane 0's: the wave's first row)
   int wmin = vis[0];
 #pragma unroll
   for (int j = 1; j < NCB; ++j) wmin = min(wmin, vis[j]);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) wmin = min(wmin, __shfl_xor(wmin, off, 64));
   wmin = __builtin_amdgcn_readfirstlane(wmin);
   // keys the whole workgroup needs: the last row of its tile sees the most
   const int last_row = min(row0 + wg_rows, qn) - 1;
   const int kv_end = visible_end(p.mask, ctx + last_row, Ls, p.span, p.full_spans, sp0, sp1);
+
+  // ---- page ids of this sequence, loaded first: the K / V gather waits on them, while
+  // the Q fragments below are needed one step later (by the first tile's MFMAs) ------
+  const int32_t* table = p.block_tables + (int64_t)s * p.mb;
+  const int last_page = (kv_end - 1) >> p.block_shift;
+  int tbl_base = 0;
+  constexpr int kTblPer = kTableChunk / NT;
+  int32_t tv[kTblPer];
+#pragma unroll
+  for (int k = 0; k < kTblPer; ++k) tv[k] = table[min(tid + k * NT, last_page)];
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[row lc][dims ks*16+hl*8..+8]
   using S = typename T::storage;
@@ -234,11 +266,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
     for (int ks = 0; ks < KS; ++ks) qf[j][ks] = qp[ks * 2 + hl];
   }
 
-  // ---- page ids of this sequence, staged in LDS ------------------------------------
-  const int32_t* table = p.block_tables + (int64_t)s * p.mb;
-  const int last_page = (kv_end - 1) >> p.block_shift;
-  int tbl_base = 0;
-  for (int i = tid; i < kTableChunk; i += NT) s_tbl[i] = table[min(i, last_page)];
+  // ---- page ids staged in LDS ------------------------------------------------------
+#pragma unroll
+  for (int k = 0; k < kTblPer; ++k) s_tbl[tid + k * NT] = tv[k];
   __syncthreads();
 
   // ---- K / V tile loads into registers (clamped to the last key: finite data) -------
@@ -532,6 +562,11 @@ inline bool prefill_params(const AttnArgs& a, PrefillParams& p, int64_t& nb) {
   // decide the makespan
   const int64_t items = (ng + nx - 1) / nx * p.qtiles;
   p.rank_items = items <= 64 ? 1 : 0;
+  // a query tile's key tiles never exceed ceil(max_seq_len / kBN); the rank compares
+  // count + 2 (empty and absent items rank last) over that many bits
+  const int64_t max_key = ((int64_t)a.max_seq_len + kBN - 1) / kBN + 2;
+  p.rank_bits = 1;
+  while (((int64_t)1 << p.rank_bits) <= max_key) ++p.rank_bits;
   p.scale_log2 = a.scale * (a.kv_fp8 ? a.k_scale : 1.f) * kLog2e;
   p.out_scale = a.kv_fp8 ? a.v_scale : 1.f;
   p.guard = a.guard;
