@@ -204,6 +204,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   rest /= p.head_groups;
   const int kvh = rest % p.Hkv;
   const int s = rest / p.Hkv;
+  // ---- page ids of this sequence, loaded first: they need only the sequence index, and
+  // the K / V gather waits on them.  The first window is the row's first kTableChunk
+  // entries (clamped to the row); entries past the sequence's last page are never used.
+  const int32_t* table = p.block_tables + (int64_t)s * p.mb;
+  constexpr int kTblPer = kTableChunk / NT;
+  int32_t tv[kTblPer];
+#pragma unroll
+  for (int k = 0; k < kTblPer; ++k) tv[k] = table[min(tid + k * NT, p.mb - 1)];
   if (!have_lens) {
     q0 = p.cu_q[s];
     qn = p.cu_q[s + 1] - q0;
@@ -244,15 +252,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   const int last_row = min(row0 + wg_rows, qn) - 1;
   const int kv_end = visible_end(p.mask, ctx + last_row, Ls, p.span, p.full_spans, sp0, sp1);
 
-  // ---- page ids of this sequence, loaded first: the K / V gather waits on them, while
-  // the Q fragments below are needed one step later (by the first tile's MFMAs) ------
-  const int32_t* table = p.block_tables + (int64_t)s * p.mb;
   const int last_page = (kv_end - 1) >> p.block_shift;
   int tbl_base = 0;
-  constexpr int kTblPer = kTableChunk / NT;
-  int32_t tv[kTblPer];
-#pragma unroll
-  for (int k = 0; k < kTblPer; ++k) tv[k] = table[min(tid + k * NT, last_page)];
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[row lc][dims ks*16+hl*8..+8]
   using S = typename T::storage;
