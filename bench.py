@@ -426,10 +426,11 @@ def cpu_baseline(w, budget_s=8.0):
             pk = ref.split_logical(ref.widen(pw.key, pw.dtype), pw.cu_seq_lens)
             pv = ref.split_logical(ref.widen(pw.value, pw.dtype), pw.cu_seq_lens)
             vis = visible_keys_per_row(pw)
-            rng = np.random.default_rng(11)
+            # distinct random rows: a fixed permutation taken in growing chunks
+            order = np.random.default_rng(11).permutation(pw.num_tokens)
             n, spent, flops, rows_done = 8, 0.0, 0.0, 0
             while spent < budget_s / 2 and rows_done < pw.num_tokens:
-                rows = np.sort(rng.choice(pw.num_tokens, min(n, pw.num_tokens), replace=False))
+                rows = np.sort(order[rows_done:rows_done + n])
                 t0 = time.perf_counter()
                 ref.paged_attention(pq, pk, pv, pw.cu_seqlens_q, pw.seq_lens, pw.num_kv_heads, pw.scale,
                                     pw.mask, pw.span_len, rows=rows)
