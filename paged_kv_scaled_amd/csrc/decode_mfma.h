@@ -320,8 +320,13 @@ __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s
       const int last_group = (hi - 1) & ~(kMGroup - 1);
       auto load = [&](MStep<T, D> (&b)[NSTEP], int base) {
         const int need = (min(base + BATCH, hi) - 1) >> p.block_shift;
-        if (need >= tw.chunk_base + kWave)
+        if (need >= tw.chunk_base + kWave) {
           table_window_load(tw, table, min(base, last_group) >> p.block_shift, last_page, lane);
+          // wait for the new page ids here, on this rare path: a wait after the branch
+          // would be one for every load in flight (the counter is in order) on every batch,
+          // and the other buffer's loads would never overlap this batch's
+          asm volatile("" ::"v"(tw.ids));
+        }
 #pragma unroll
         for (int k = 0; k < NSTEP; ++k)
           mload_step<T, D>(b[k], p, tw, head_off, base + k * kMStep, hi, a, n);
