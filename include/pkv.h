@@ -53,11 +53,13 @@
  *   blocks, table tails, in-block tails) never enter its arithmetic, so they
  *   may hold anything, NaN included.  A NaN or infinity in a query row or in a
  *   key or value row that a query row does see gives that output row undefined
- *   values on the MFMA prefill and mixed-batch kernels (they are compiled to
- *   assume finite operands); the decode kernels give a NaN row.
+ *   values on the MFMA prefill kernel, which the prefill, span-list, FP8
+ *   prefill and mixed-batch calls use (it is compiled to assume finite
+ *   operands); the decode kernels give a NaN row.
  *
  * Device-content preconditions (not checked by default, undefined behaviour if
- * violated; pkv_set_device_checks(1) checks all but slot uniqueness on the GPU):
+ * violated; pkv_set_device_checks(1) checks them on the GPU, slot uniqueness
+ * through pkv_check_slots_unique):
  *   slots in [0, num_blocks*block_size) or negative, unique within one call;
  *   block_tables entries in [0, num_blocks) for the blocks a sequence uses;
  *   seq_lens[s] <= max_blocks_per_seq*block_size and <= max_seq_len;
