@@ -32,8 +32,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-# Per-file code-generation options.  The MFMA prefill kernel (also inside the mixed-batch
-# kernel) keeps its accumulators in
+# Per-file code-generation options.  The MFMA prefill kernel keeps its accumulators in
 # VGPRs (VGPR-form MFMA): with the default AGPR form the compiler copies the output
 # accumulator between register files on every key tile.  It also runs with the IEEE mode
 # bit off and NaN-free inputs assumed: in IEEE mode every fmax operand that comes out of an
