@@ -178,7 +178,7 @@ int prefill_common(void* out, const void* query, const int32_t* cu_seqlens_q,
                         max_seq_len, max_q_len, num_tokens, 0};
     if ((rc = launched(pkv::launch_check_seqs(c, (hipStream_t)stream), what)) != PKV_OK) return rc;
   }
-  if (pkv::prefill_mfma_supported((int)dtype, head_dim, scale))
+  if (pkv::prefill_mfma_supported(a))
     return launched(pkv::launch_prefill_mfma(a, (hipStream_t)stream), what);
   return launched(pkv::launch_prefill_valu(a, (hipStream_t)stream), what);
 }
@@ -773,7 +773,7 @@ int pkv_paged_attention_mixed(void* out, const void* query, const int32_t* cu_se
   // the context rows through the prefill kernel, then the generation rows through the
   // decode kernels, on the caller's stream
   if (num_ctx_seqs > 0 && num_ctx_tokens > 0) {
-    const hipError_t e = pkv::prefill_mfma_supported((int)dtype, head_dim, scale)
+    const hipError_t e = pkv::prefill_mfma_supported(ctx)
                              ? pkv::launch_prefill_mfma(ctx, (hipStream_t)stream)
                              : pkv::launch_prefill_valu(ctx, (hipStream_t)stream);
     if ((rc = launched(e, what)) != PKV_OK) return rc;

@@ -165,6 +165,7 @@ hipError_t decode_scratch(void** ptr);
 // Returns hipErrorNotSupported when no MFMA variant covers the shape.
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_valu(const AttnArgs& a, hipStream_t stream);
-bool prefill_mfma_supported(int dtype, int head_dim, float scale);
+// bf16 / fp16 queries, head_dim 64 or 128, scale > 0, cache blocks below 4 GiB
+bool prefill_mfma_supported(const AttnArgs& a);
 
 }  // namespace pkv

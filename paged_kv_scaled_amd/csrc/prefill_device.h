@@ -281,7 +281,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   using KR = typename std::conditional<kK8, u32x2_t, u32x4_t>::type;
   const uint32_t row_bytes = (uint32_t)p.Hkv * D * CE;
   const uint32_t head_bytes = (uint32_t)kvh * D * CE;
-  const uint64_t blk_bytes = (uint64_t)p.block_stride * CE;
+  // bytes per cache block: below 2^32 (the host routes larger strides elsewhere), so a
+  // block offset is one 32 x 32 -> 64-bit multiply
+  const uint32_t blk_bytes = (uint32_t)((uint64_t)p.block_stride * CE);
   const int bmask = (1 << p.block_shift) - 1;
   const int vc_ld = tid % NC;               // 8-dim chunk
   const int vg_ld = tid / NC;               // token group of TG tokens
@@ -291,15 +293,31 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
 
   // keys past kv_end (seen by no row of this workgroup) re-read key kv_end-1: finite
   // data whose page id is inside the staged window
-  auto load_tile = [&](int k0, KR (&kreg)[TG], KR (&vreg)[TG]) {
-#pragma unroll
-    for (int i = 0; i < TG; ++i) {
-      const int pos = min(k0 + vg_ld * TG + i, kv_end - 1);
+  // PAIRS (pages of >= 2 tokens, two tokens per thread): the thread's tokens k, k + 1
+  // (k even) share a page, so one page-id lookup and one block offset serve both; the
+  // second is the next row, or the same clamped row at the end.
+  auto load_tile = [&](int k0, KR (&kreg)[TG], KR (&vreg)[TG], auto pairs) {
+    if constexpr (decltype(pairs)::value && TG == 2) {
+      const int t0 = k0 + vg_ld * 2;
+      const int pos = min(t0, kv_end - 1);
       const uint32_t blk = (uint32_t)s_tbl[(pos >> p.block_shift) - tbl_base];
-      const uint64_t off = (uint64_t)blk * blk_bytes +
-                           ((uint32_t)(pos & bmask) * row_bytes + head_bytes + vc_ld * 8u * CE);
-      kreg[i] = *reinterpret_cast<const KR*>(kbase + off);
-      vreg[i] = *reinterpret_cast<const KR*>(vbase + off);
+      const uint64_t off0 = (uint64_t)blk * blk_bytes +
+                            ((uint32_t)(pos & bmask) * row_bytes + head_bytes + vc_ld * 8u * CE);
+      const uint64_t off1 = off0 + (t0 + 1 < kv_end ? row_bytes : 0u);
+      kreg[0] = *reinterpret_cast<const KR*>(kbase + off0);
+      vreg[0] = *reinterpret_cast<const KR*>(vbase + off0);
+      kreg[1] = *reinterpret_cast<const KR*>(kbase + off1);
+      vreg[1] = *reinterpret_cast<const KR*>(vbase + off1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TG; ++i) {
+        const int pos = min(k0 + vg_ld * TG + i, kv_end - 1);
+        const uint32_t blk = (uint32_t)s_tbl[(pos >> p.block_shift) - tbl_base];
+        const uint64_t off = (uint64_t)blk * blk_bytes +
+                             ((uint32_t)(pos & bmask) * row_bytes + head_bytes + vc_ld * 8u * CE);
+        kreg[i] = *reinterpret_cast<const KR*>(kbase + off);
+        vreg[i] = *reinterpret_cast<const KR*>(vbase + off);
+      }
     }
   };
   // 8 elements of the compute type from what one load brought
@@ -358,7 +376,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   // One key tile: its K/V registers (loaded two tiles earlier) go to LDS, the registers are
   // refilled with the tile two ahead, then every wave computes on the LDS tile.  Two tiles
   // in flight cover the gather latency when the keys come from HBM rather than L2.
-  auto tile_step = [&](int k0, KR (&kreg)[TG], KR (&vreg)[TG]) {
+  auto tile_step = [&](int k0, KR (&kreg)[TG], KR (&vreg)[TG], auto pairs) {
     // Slot (k0 / kBN) % 2 last held tile k0 - 2 kBN, which every wave finished computing
     // before it reached the previous tile's barrier.
     uint8_t* s_k = s_k2[(k0 / kBN) & 1];
@@ -375,7 +393,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
           s_tbl[i] = table[min(tbl_base + i, last_page)];
         __syncthreads();
       }
-      load_tile(k2, kreg, vreg);
+      load_tile(k2, kreg, vreg, pairs);
     }
     {  // every wave computes every tile of the workgroup (see the note on wmin)
       // ---- S^T = K Q^T for the wave's column block ------------------------------------
@@ -483,16 +501,22 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
       }
     }
   };
-  if (kv_end > 0) {
-    load_tile(0, kra, vra);
-    if (kBN < kv_end) load_tile(kBN, krb, vrb);
-  }
-  int k0 = 0;
-  for (; k0 + kBN < kv_end; k0 += 2 * kBN) {
-    tile_step(k0, kra, vra);
-    tile_step(k0 + kBN, krb, vrb);
-  }
-  if (k0 < kv_end) tile_step(k0, kra, vra);
+  auto run = [&](auto pairs) {
+    if (kv_end > 0) {
+      load_tile(0, kra, vra, pairs);
+      if (kBN < kv_end) load_tile(kBN, krb, vrb, pairs);
+    }
+    int k0 = 0;
+    for (; k0 + kBN < kv_end; k0 += 2 * kBN) {
+      tile_step(k0, kra, vra, pairs);
+      tile_step(k0 + kBN, krb, vrb, pairs);
+    }
+    if (k0 < kv_end) tile_step(k0, kra, vra, pairs);
+  };
+  if (TG == 2 && p.block_shift >= 1)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // ---- normalise and write O (lane: one row, 4 runs of 4 dims per 32-dim block) -------
 #pragma unroll

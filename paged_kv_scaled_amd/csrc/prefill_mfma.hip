@@ -4,13 +4,16 @@
 
 namespace pkv {
 
-bool prefill_mfma_supported(int dtype, int head_dim, float scale) {
-  // the row max is taken on raw scores, which needs a positive scale
-  return (dtype == kBF16 || dtype == kF16) && (head_dim == 64 || head_dim == 128) && scale > 0.f;
+bool prefill_mfma_supported(const AttnArgs& a) {
+  // the row max is taken on raw scores, which needs a positive scale; a block offset is a
+  // 32 x 32 -> 64-bit product, which needs a block of less than 4 GiB
+  const uint64_t block_bytes = (uint64_t)a.block_stride * (a.kv_fp8 ? 1u : 2u);
+  return (a.dtype == kBF16 || a.dtype == kF16) && (a.head_dim == 64 || a.head_dim == 128) &&
+         a.scale > 0.f && block_bytes < ((uint64_t)1 << 32);
 }
 
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream) {
-  if (!prefill_mfma_supported(a.dtype, a.head_dim, a.scale)) return hipErrorNotSupported;
+  if (!prefill_mfma_supported(a)) return hipErrorNotSupported;
   if (a.num_tokens == 0 || a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
   PrefillParams p{};
   int64_t nb = 0;
