@@ -250,7 +250,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
   wmin = __builtin_amdgcn_readfirstlane(wmin);
   // keys the whole workgroup needs: the last row of its tile sees the most
   const int last_row = min(row0 + wg_rows, qn) - 1;
-  const int kv_end = visible_end(p.mask, ctx + last_row, Ls, p.span, p.full_spans, sp0, sp1);
+  // (uniform over the workgroup: kept in a scalar register, so the per-tile tests against
+  // it are scalar branches)
+  const int kv_end = __builtin_amdgcn_readfirstlane(
+      visible_end(p.mask, ctx + last_row, Ls, p.span, p.full_spans, sp0, sp1));
 
   const int last_page = (kv_end - 1) >> p.block_shift;
   int tbl_base = 0;
