@@ -261,18 +261,20 @@ def run_mixed_bench(w, steps, warmup):
                                  w.scale, w.max_seq_len, dws if db else None)
 
     buf = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
-    res = {}
-    for name, call in (("fused", fused), ("separate", separate)):
-        for _ in range(warmup):
+    calls = (("fused", fused), ("separate", separate))
+    for _ in range(warmup):
+        for _, call in calls:
             call()
-        tm = Timer()
-        for _ in range(steps):
+    # the two forms alternate step by step, so that the clock's ramp under load (the
+    # first launches of a run are slower) favours neither
+    tms = {name: Timer() for name, _ in calls}
+    for _ in range(steps):
+        for name, call in calls:
             flush_llc(buf)
-            e = tm.start()
+            e = tms[name].start()
             call()
-            tm.stop(e)
-        res[name] = tm.ms()
-    return res
+            tms[name].stop(e)
+    return {name: tm.ms() for name, tm in tms.items()}
 
 
 def smallseq_train_bytes(w, max_kv=16):
