@@ -57,6 +57,8 @@ constexpr bool mfma_split_shape() {
 template <typename T, int D, int HPW>
 bool launch_main_mfma(const DecodeParams& dp, const DecodePlan& pl, hipStream_t stream) {
   if (dp.block_shift < 3) return false;
+  // the core's offsets inside a page are 32-bit: pages of 4 GiB and more take the vector core
+  if ((uint64_t)dp.block_stride * (KvFp8<T>::value ? 1u : 2u) >= ((uint64_t)1 << 32)) return false;
   constexpr int MS = MSteps<T>::value;
   if (pl.stream) {
     if constexpr (mfma_stream_shape<T, D, HPW>()) {

@@ -108,71 +108,78 @@ struct MState {
   f32x4_t acc[D / 16];        // O rows 4a + j, dim n D/16 + i, in acc[i][j]
 };
 
-// Raw words [w0, w0 + N) of a K or V slice at element offset `off` of a cache.
-template <typename T, int N>
-__device__ __forceinline__ void load_words(uint32_t* dst, const void* base, int64_t off) {
-  if constexpr (KvFp8<T>::value) {
-    const uint8_t* b = reinterpret_cast<const uint8_t*>(base) + off;
-    if constexpr (N % 4 == 0) {
+// N raw words at byte address b (16-, 8- or 4-byte aligned as N requires).
+template <int N>
+__device__ __forceinline__ void load_words(uint32_t* dst, const uint8_t* b) {
+  if constexpr (N % 4 == 0) {
 #pragma unroll
-      for (int i = 0; i < N / 4; ++i) {
-        const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(b) + i);
+    for (int i = 0; i < N / 4; ++i) {
+      const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(b) + i);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) dst[4 * i + w] = x[w];
-      }
-    } else if constexpr (N == 2) {
-      const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(b));
-      dst[0] = x[0];
-      dst[1] = x[1];
-    } else {
-      static_assert(N == 1, "slice width");
-      dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(b));
+      for (int w = 0; w < 4; ++w) dst[4 * i + w] = x[w];
     }
+  } else if constexpr (N == 2) {
+    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(b));
+    dst[0] = x[0];
+    dst[1] = x[1];
   } else {
-    const uint16_t* b = reinterpret_cast<const uint16_t*>(base) + off;
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-      for (int i = 0; i < N / 4; ++i) {
-        const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(b) + i);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) dst[4 * i + w] = x[w];
-      }
-    } else {
-      static_assert(N == 2, "slice width");
-      const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(b));
-      dst[0] = x[0];
-      dst[1] = x[1];
-    }
+    static_assert(N == 1, "slice width");
+    dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(b));
   }
+}
+
+// Byte geometry of a wave's loads that holds for the whole segment.  A page is under
+// 4 GiB (the launch checks it), so the offset inside a page is 32-bit and a page's own
+// offset is one 32 x 32 -> 64-bit multiply of its id.
+struct MAddr {
+  const uint8_t* kc;
+  const uint8_t* vc;
+  uint32_t row_bytes;         // one token row (all kv heads)
+  uint32_t blk_bytes;         // one page
+  uint32_t k_lane;            // the lane's K slice in its row: kv head, unit a, key n % 4
+  uint32_t v_lane;            // the lane's V slice in its row: kv head, dims n D/16
+};
+
+template <typename T, int D>
+__device__ __forceinline__ MAddr maddr(const DecodeParams& p, int kvh, int a, int n) {
+  using M = MShape<T, D>;
+  constexpr uint32_t E = M::kFp8 ? 1u : 2u;         // bytes per cache element
+  MAddr m;
+  m.kc = reinterpret_cast<const uint8_t*>(p.kc);
+  m.vc = reinterpret_cast<const uint8_t*>(p.vc);
+  m.row_bytes = (uint32_t)p.Hkv * D * E;
+  m.blk_bytes = (uint32_t)((uint64_t)p.block_stride * E);
+  const uint32_t head = (uint32_t)kvh * D * E;
+  m.k_lane = head + (uint32_t)a * 16u + (uint32_t)(n & 3) * m.row_bytes;
+  m.v_lane = head + (uint32_t)n * (M::VD * E);
+  return m;
 }
 
 // Loads of the step starting at key sb (a multiple of 8) of a segment ending at hi.
 template <typename T, int D>
 __device__ __forceinline__ void mload_step(MStep<T, D>& st, const DecodeParams& p,
-                                           const TableWindow& tw, int64_t head_off, int sb,
+                                           const TableWindow& tw, const MAddr& ma, int sb,
                                            int hi, int a, int n) {
   using M = MShape<T, D>;
-  const int64_t row_elems = (int64_t)p.Hkv * D;
-  const int bmask = (1 << p.block_shift) - 1;
+  const uint32_t bmask = (1u << p.block_shift) - 1u;
   const int last_group = (hi - 1) & ~(kMGroup - 1);
   // K: group of row n; V: group a
   const int gk = min(sb + kMGroup * (n >> 2), last_group);
   const int gv = min(sb + kMGroup * a, last_group);
-  const int64_t bk = __shfl(tw.ids, ((gk >> p.block_shift) - tw.chunk_base) & (kWave - 1), kWave);
-  const int64_t bv = __shfl(tw.ids, ((gv >> p.block_shift) - tw.chunk_base) & (kWave - 1), kWave);
-  const int64_t kbase = bk * p.block_stride + (int64_t)(gk & bmask) * row_elems + head_off +
-                        a * M::U;
-  const int64_t vbase = bv * p.block_stride + (int64_t)(gv & bmask) * row_elems + head_off +
-                        n * M::VD;
+  const uint32_t bk = (uint32_t)__shfl(tw.ids, ((gk >> p.block_shift) - tw.chunk_base) & (kWave - 1), kWave);
+  const uint32_t bv = (uint32_t)__shfl(tw.ids, ((gv >> p.block_shift) - tw.chunk_base) & (kWave - 1), kWave);
+  const uint8_t* kp = ma.kc + ((uint64_t)bk * ma.blk_bytes + (((uint32_t)gk & bmask) * ma.row_bytes + ma.k_lane));
+  const uint8_t* vp = ma.vc + ((uint64_t)bv * ma.blk_bytes + (((uint32_t)gv & bmask) * ma.row_bytes + ma.v_lane));
+  // tile t: key 4t + n % 4 of the group; instruction i: units 4i .. 4i+3 of the row
+  // (64 contiguous bytes, unit a of them for this lane)
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < M::KW / 4; ++i)   // unit 4i + a of the row: words 4i .. 4i+3
-      load_words<T, 4>(st.k[t] + 4 * i, p.kc,
-                       kbase + (int64_t)(4 * t + (n & 3)) * row_elems + 4 * i * M::U);
+    for (int i = 0; i < M::KW / 4; ++i)
+      load_words<4>(st.k[t] + 4 * i, kp + (uint64_t)(4 * t) * ma.row_bytes + 64 * i);
 #pragma unroll
   for (int k = 0; k < kMGroup; ++k)
-    load_words<T, M::VW>(st.v[k], p.vc, vbase + (int64_t)k * row_elems);
+    load_words<M::VW>(st.v[k], vp + (uint64_t)k * ma.row_bytes);
 }
 
 // Compute-type words 4j .. 4j+3 of a K slice (product j's A operand).
@@ -189,7 +196,9 @@ __device__ __forceinline__ u32x4_t k_operand(const uint32_t (&raw)[MShape<T, D>:
 }
 
 // One step: scores, softmax update, O += P V.  FULL: every key of the step lies in
-// [lo, hi) (decided per step, uniformly over the wave).
+// [lo, hi) (decided per step, uniformly over the wave).  scale_log2 >= 0 (a negative
+// scale is taken by negating the queries), so the largest raw score is the largest
+// scaled one and each exponent is one fma of the raw score.
 template <typename T, int D, bool FULL>
 __device__ __forceinline__ void mcompute_step(MStep<T, D>& st, const u32x4_t (&q)[MShape<T, D>::NSC],
                                               MState<D>& s, float scale_log2, int sb, int lo,
@@ -204,25 +213,25 @@ __device__ __forceinline__ void mcompute_step(MStep<T, D>& st, const u32x4_t (&q
 #pragma unroll
     for (int j = 0; j < M::NSC; ++j) sc[t] = Mma<B>::run(k_operand<T, D>(st.k[t], j), q[j], sc[t]);
   }
-  float x[kMGroup];
+  float x[kMGroup];                          // raw scores q . k
+  bool in[kMGroup];
   const int k0 = sb + kMGroup * a;           // this lane's first key
 #pragma unroll
   for (int r = 0; r < kMGroup; ++r) {
-    const float v = sc[r >> 2][r & 3] * scale_log2;
-    x[r] = (FULL || (k0 + r >= lo && k0 + r < hi)) ? v : -INFINITY;
+    in[r] = FULL || (k0 + r >= lo && k0 + r < hi);
+    x[r] = in[r] ? sc[r >> 2][r & 3] : -INFINITY;
   }
   if constexpr (!FULL) {
     // keys outside the segment: zero V so that nothing but finite zeros reaches O
 #pragma unroll
-    for (int r = 0; r < kMGroup; ++r) {
-      const bool ok = k0 + r >= lo && k0 + r < hi;
+    for (int r = 0; r < kMGroup; ++r)
 #pragma unroll
-      for (int w = 0; w < M::VW; ++w) st.v[r][w] = ok ? st.v[r][w] : 0u;
-    }
+      for (int w = 0; w < M::VW; ++w) st.v[r][w] = in[r] ? st.v[r][w] : 0u;
   }
   float mx = x[0];
 #pragma unroll
   for (int r = 1; r < kMGroup; ++r) mx = fmaxf(mx, x[r]);
+  mx *= scale_log2;
   if (__builtin_expect(__any(mx > s.m + kLazyRescale), 0)) {
     float mt = fmaxf(mx, shfl_xor_f(mx, 16));
     mt = fmaxf(mt, shfl_xor_f(mt, 32));
@@ -240,9 +249,12 @@ __device__ __forceinline__ void mcompute_step(MStep<T, D>& st, const u32x4_t (&q
   }
   // (at an edge the running max may still be -inf: masked keys get 0 explicitly)
   float pr[kMGroup];
+  const float nm = -s.m;
 #pragma unroll
-  for (int r = 0; r < kMGroup; ++r)
-    pr[r] = (!FULL && x[r] == -INFINITY) ? 0.f : fast_exp2(x[r] - s.m);
+  for (int r = 0; r < kMGroup; ++r) {
+    const float e = fast_exp2(__builtin_fmaf(x[r], scale_log2, nm));
+    pr[r] = FULL ? e : (in[r] ? e : 0.f);
+  }
   u32x4_t pp;
 #pragma unroll
   for (int w = 0; w < 4; ++w) pp[w] = pack2(B{}, pr[2 * w], pr[2 * w + 1]);
@@ -286,6 +298,13 @@ __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s
   using M = MShape<T, D>;
   using S = typename T::storage;
   const int a = lane >> 4, n = lane & 15;
+  // the bounds are the same in every lane: scalar registers, scalar branches
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+  // a negative scale: negated queries (exact) give negated raw scores, and the scale's
+  // magnitude then applies
+  const float sl2 = fabsf(p.scale_log2);
+  const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   u32x4_t q[M::NSC];
   {
     // columns past the group's heads get zeros (finite scores, never written)
@@ -293,7 +312,8 @@ __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s
 #pragma unroll
     for (int j = 0; j < M::NSC; ++j) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + kdim<T, D>(j, a));
-      q[j] = n < nh ? v : (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) q[j][w] = n < nh ? (v[w] ^ qsign) : 0u;
     }
   }
   st.m = -INFINITY;
@@ -302,16 +322,16 @@ __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s
   for (int i = 0; i < M::VD; ++i) st.acc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   if (lo < hi) {
     const int32_t* table = p.block_tables + (int64_t)s * p.mb;
-    const int64_t head_off = (int64_t)kvh * D;
+    const MAddr ma = maddr<T, D>(p, kvh, a, n);
     const int last_page = (hi - 1) >> p.block_shift;
     const int start = lo & ~(kMGroup - 1);
     TableWindow tw;
     table_window_load(tw, table, start >> p.block_shift, last_page, lane);
     auto compute = [&](MStep<T, D>& b, int sb) {
       if (sb >= lo && sb + kMStep <= hi)
-        mcompute_step<T, D, true>(b, q, st, p.scale_log2, sb, lo, hi, a);
+        mcompute_step<T, D, true>(b, q, st, sl2, sb, lo, hi, a);
       else
-        mcompute_step<T, D, false>(b, q, st, p.scale_log2, sb, lo, hi, a);
+        mcompute_step<T, D, false>(b, q, st, sl2, sb, lo, hi, a);
     };
     if constexpr (ROLL) {
       // batches past the end re-read the last group (no branch around a load) and are
@@ -329,7 +349,7 @@ __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s
         }
 #pragma unroll
         for (int k = 0; k < NSTEP; ++k)
-          mload_step<T, D>(b[k], p, tw, head_off, base + k * kMStep, hi, a, n);
+          mload_step<T, D>(b[k], p, tw, ma, base + k * kMStep, hi, a, n);
       };
       auto compute_batch = [&](MStep<T, D> (&b)[NSTEP], int base) {
 #pragma unroll
@@ -358,7 +378,7 @@ __device__ __forceinline__ void attend_segment_mfma(const DecodeParams& p, int s
         MStep<T, D> ms[NSTEP];
 #pragma unroll
         for (int k = 0; k < NSTEP; ++k)
-          mload_step<T, D>(ms[k], p, tw, head_off, base + k * kMStep, hi, a, n);
+          mload_step<T, D>(ms[k], p, tw, ma, base + k * kMStep, hi, a, n);
 #pragma unroll
         for (int k = 0; k < NSTEP; ++k) {
           const int sb = base + k * kMStep;
