@@ -25,9 +25,13 @@
 // Work decomposition (picked on the host from the sizes):
 //  * stream mode (some sequence longer than one split): the concatenated key axis of
 //    all sequences is cut into `nranges` equal ranges per head group, one wave each,
-//    so every wave does the same work whatever the length mix.  A sequence that lies
-//    inside one range is finished by that wave; a range boundary inside a sequence
-//    leaves (acc, m, l) partials that the merge kernel combines.  Up to kStreamScanSeqs
+//    so every wave does the same work whatever the length mix.  On that axis every
+//    sequence after the first is preceded by kStreamSeqCost positions that hold no key: a
+//    wave pays about that much for each sequence it starts (page ids, the first loads,
+//    the partial it leaves), so a range that crosses more sequence boundaries holds
+//    fewer keys.  A
+//    sequence that lies inside one range is finished by that wave; a range boundary
+//    inside a sequence leaves (acc, m, l) partials that the merge kernel combines.  Up to kStreamScanSeqs
 //    sequences each wave finds its range's first sequence by scanning the lengths;
 //    beyond, a one-block planning kernel writes the length prefix sums and every range's
 //    first sequence into the workspace, and the waves read them;
@@ -55,6 +59,10 @@ constexpr int kStreamScanSeqs = 256;   // plain decode: up to here every stream 
 constexpr int kStreamWavesPerCu = 4;       // waves of the stream grid (all head groups): one
                                            // wave per SIMD (1024 on a whole MI355X)
 constexpr int kStreamMinRange = 64;    // shortest range, keys
+// Positions charged on the stream key axis for each sequence a range starts (measured:
+// a segment costs a wave ~1.2-1.8 us besides its keys, 30-45 keys of an FP8 decode and
+// 20-25 of a bf16 one; waves crossing three sequences ended ~4.5 us after those with one).
+constexpr int kStreamSeqCost = 32;
 
 template <typename T, int D>
 struct DecodeShape {
@@ -729,10 +737,11 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
   return x;
 }
 
-// Total keys of the batch, and the range length every stream kernel derives from it.
-// len0: this lane's entry of the first 64 lengths (0 past the batch), loaded once.
+// Length of the stream key axis (every key, plus kStreamSeqCost before each sequence but
+// the first), from which every stream kernel derives the range length.  len0: this lane's
+// entry of the first 64 lengths (0 past the batch), loaded once.
 __device__ __forceinline__ int64_t stream_total(const DecodeParams& p, int lane, int len0) {
-  int64_t total = 0;
+  int64_t total = (int64_t)(p.S - 1) * kStreamSeqCost;
   for (int c0 = 0; c0 < p.S; c0 += kWave) {
     int x = c0 == 0 ? len0 : ((c0 + lane < p.S) ? p.seq_lens[c0 + lane] : 0);
 #pragma unroll
@@ -747,17 +756,18 @@ __device__ __forceinline__ int64_t stream_range_len(int64_t total, int nranges) 
   return r < kStreamMinRange ? kStreamMinRange : r;
 }
 
-// First sequence whose keys reach past position x of the concatenated key axis, and the
-// position where that sequence starts.
+// First sequence whose span (its charge, then its keys) reaches past position x of the
+// stream key axis, and the position of that sequence's first key.
 __device__ __forceinline__ void stream_locate(const DecodeParams& p, int64_t x, int lane, int len0,
                                               int& s0, int64_t& start0) {
   int count = 0;
   int64_t carry = 0, before = 0;
   for (int c0 = 0; c0 < p.S; c0 += kWave) {
     const bool in = c0 + lane < p.S;
-    const int Ls = c0 == 0 ? len0 : (in ? p.seq_lens[c0 + lane] : 0);
+    const int Ls = (c0 == 0 ? len0 : (in ? p.seq_lens[c0 + lane] : 0)) + (in ? kStreamSeqCost : 0);
+    // incl: first key of the next sequence; this one's span ends kStreamSeqCost before
     const int64_t incl = carry + wave_inclusive_scan(Ls, lane);
-    const bool done = in && incl <= x;                 // sequence ends at or before x
+    const bool done = in && incl - kStreamSeqCost <= x;   // sequence ends at or before x
     count += __popcll(__ballot(done));
     int64_t b = done ? incl : 0;
 #pragma unroll
@@ -787,7 +797,7 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item)
   int len0 = 0;
   int64_t total;
   if constexpr (PFX) {
-    total = p.cu[p.S];
+    total = p.cu[p.S] + (int64_t)(p.S - 1) * kStreamSeqCost;
   } else {
     len0 = lane < p.S ? p.seq_lens[lane] : 0;
     total = stream_total(p, lane, len0);
@@ -807,13 +817,14 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item)
   } else {
     stream_locate(p, lo, lane, len0, s, P);
   }
-  bool first = true;
+  // P: position of sequence s's first key.  A range leaves at most two partials: slot 0
+  // for a sequence begun before the range, slot 1 for one that runs past its end.
   for (; s < p.S && P < hi; ++s) {
     const int L = p.seq_lens[s];
     const int seg_lo = (int)((lo > P ? lo : P) - P);
     const int seg_hi = (int)((hi < P + L ? hi : P + L) - P);
     if (seg_hi > seg_lo) {
-      const int64_t slot = (int64_t)r * 2 + (first ? 0 : 1);
+      const int64_t slot = (int64_t)r * 2 + (seg_lo > 0 ? 0 : 1);
       if constexpr (MF) {
         MState<D> ms;
         // one wave per SIMD: a rolling buffer where a load batch would be one step
@@ -833,9 +844,8 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, int64_t item)
             write_partial<T, D, HPW>(p, (int64_t)p.nranges * 2, slot, h0, nh, c, m, l, acc);
         }
       }
-      first = false;
     }
-    P += L;
+    P += L + kStreamSeqCost;
   }
 }
 
@@ -884,17 +894,18 @@ decode_stream_plan_kernel(const DecodeParams p) {
   if (tid == 0) p.cu[0] = 0;
   __threadfence_block();
   __syncthreads();                   // cu complete and visible to the block
-  const int64_t R = stream_range_len(carry, p.nranges);
+  // the stream key axis: sequence s's keys start at cu[s] + s kStreamSeqCost
+  const int64_t R = stream_range_len(carry + (int64_t)(p.S - 1) * kStreamSeqCost, p.nranges);
   for (int r = tid; r < p.nranges; r += kPlanThreads) {
     const int64_t x = (int64_t)r * R;
-    // smallest s with cu[s + 1] > x (S when the range is empty)
+    // smallest s whose span ends past x (S when the range is empty)
     int a = 0, b = p.S;
     while (a < b) {
       const int mid = (a + b) >> 1;
-      if (p.cu[mid + 1] > x) b = mid; else a = mid + 1;
+      if (p.cu[mid + 1] + (int64_t)mid * kStreamSeqCost > x) b = mid; else a = mid + 1;
     }
     p.rstart[r] = a;
-    p.rpos[r] = p.cu[min(a, p.S)];
+    p.rpos[r] = p.cu[min(a, p.S)] + (int64_t)a * kStreamSeqCost;   // its first key
   }
 }
 
@@ -1016,9 +1027,9 @@ decode_merge_split_kernel(const DecodeParams p) {
   merge_slots<T, D>(p, sh, h, (int64_t)p.S * p.nsplit, ns, lane, base, base + 1, 1);
 }
 
-// Where sequence s sits on the concatenated key axis: its length L, its start P and the
-// batch total, all from one round of loads: the planning kernel's prefix sums, or one pass
-// of the wave over the lengths (L taken from the pass itself).
+// Where sequence s sits on the stream key axis: its length L, the position P of its first
+// key and the axis length, all from one round of loads: the planning kernel's prefix sums,
+// or one pass of the wave over the lengths (L taken from the pass itself).
 struct SeqPos {
   int64_t total = 0, P = 0;
   int L = 0;
@@ -1046,6 +1057,8 @@ __device__ __forceinline__ SeqPos stream_seq_pos(const DecodeParams& p, int s, i
       q.P += before;
     }
   }
+  q.total += (int64_t)(p.S - 1) * kStreamSeqCost;
+  q.P += (int64_t)s * kStreamSeqCost;
   return q;
 }
 
@@ -1059,8 +1072,8 @@ __device__ __forceinline__ void store_zero_row(const DecodeParams& p, int64_t sh
 
 // Stream mode: one wave per (sequence, head).  Sequences inside one range were written
 // by the stream kernel; empty sequences get zeros; the others combine one partial per
-// range they touch (the first range's partial is its second slot unless the sequence
-// starts exactly at that range's start).
+// range they touch: the second slot of the range holding their first key, the first slot
+// of every later one.
 template <typename T, int D, bool PFX = false>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_merge_stream_kernel(const DecodeParams p) {
@@ -1077,7 +1090,7 @@ decode_merge_stream_kernel(const DecodeParams p) {
   const int64_t R = stream_range_len(q.total, p.nranges);
   const int64_t r0 = q.P / R, r1 = (q.P + q.L - 1) / R;
   if (r0 == r1) return;
-  const int64_t slot0 = r0 * 2 + ((r0 * R < q.P) ? 1 : 0);
+  const int64_t slot0 = r0 * 2 + 1;
   merge_slots<T, D>(p, sh, h, (int64_t)p.nranges * 2, (int)(r1 - r0 + 1), lane, slot0,
                     (r0 + 1) * 2, 2);
 }
@@ -1104,7 +1117,7 @@ decode_merge_stream_wide_kernel(const DecodeParams p) {
   const int64_t R = stream_range_len(q.total, p.nranges);
   const int64_t r0 = q.P / R, r1 = (q.P + q.L - 1) / R;
   if (r0 == r1) return;
-  const int64_t slot0 = r0 * 2 + ((r0 * R < q.P) ? 1 : 0);
+  const int64_t slot0 = r0 * 2 + 1;
   const int n = (int)(r1 - r0 + 1);
   const int per = (n + kWavesPerBlock - 1) / kWavesPerBlock;
   const int jb = min(n, wave * per), je = min(n, jb + per);
