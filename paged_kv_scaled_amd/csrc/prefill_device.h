@@ -16,8 +16,10 @@
 //    MFMA operand reads hit distinct banks;
 //  * S^T = K Q^T on MFMA (A = K rows from LDS, B = Q rows held in registers): each lane
 //    then holds 32 scores of one query row, so the row max needs one cross-lane step;
-//  * online softmax in fp32 registers (exp2 with scale*log2(e) folded; the max only
-//    moves when a score exceeds it by more than 2^8, so the O rescale is rare);
+//  * online softmax in fp32 registers (exp2 with scale*log2(e) folded).  The probabilities
+//    are taken against the running max as it stands, and the tile's row max is computed
+//    (and O rescaled) only when a row's probabilities of the tile sum past 2^13, which
+//    is rare after the first tile;
 //  * the probabilities stay where the S^T accumulator put them and are used directly as
 //    the B operand of O^T = V^T P^T: the V^T tile stores each 16-token group in the
 //    token order that accumulator layout implies;
@@ -39,7 +41,9 @@ namespace {
 constexpr int kWaves = 8;          // waves per workgroup: 2 per SIMD
 constexpr int kBN = 64;            // keys per tile
 constexpr int kTableChunk = 1024;  // page ids staged in LDS at a time
-constexpr float kLazy = 8.0f;
+// bound on the sum of one lane's 32 probabilities of a key tile before the running max
+// moves (log2 13: every probability stays <= 2^13)
+constexpr float kSumCap = 8192.0f;
 static_assert(kTableChunk % (kWaves * 64) == 0, "page-id staging: whole loads per thread");
 
 struct PrefillParams {
@@ -401,96 +405,117 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int bid) {
     {  // every wave computes every tile of the workgroup (see the note on wmin)
       // ---- S^T = K Q^T for the wave's column block ------------------------------------
       f32x16_t sacc[NCB][2];
-      // K fragments read one k-step ahead of their MFMAs (two register sets)
-      u32x4_t ka[2][2];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        ka[0][tb] = *reinterpret_cast<const u32x4_t*>(s_k + L::k_off(tb * 32 + lc, hl));
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            ka[(ks + 1) & 1][tb] =
-                *reinterpret_cast<const u32x4_t*>(s_k + L::k_off(tb * 32 + lc, (ks + 1) * 2 + hl));
-        }
+      auto scores = [&]() {
+        // K fragments read one k-step ahead of their MFMAs (two register sets)
+        u32x4_t ka[2][2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
+          ka[0][tb] = *reinterpret_cast<const u32x4_t*>(s_k + L::k_off(tb * 32 + lc, hl));
 #pragma unroll
-          for (int j = 0; j < NCB; ++j)
-            sacc[j][tb] = Mfma<TB>::run(ka[ks & 1][tb], qf[j][ks], ks == 0 ? (f32x16_t){} : sacc[j][tb]);
-      }
-      // keep the read-ahead: the scheduler would otherwise pull each read down to its MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // LDS reads of k-steps 0, 1
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) {
 #pragma unroll
-      for (int ks = 0; ks + 2 < KS; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NCB, 0);   // MFMAs of k-step ks
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // reads of k-step ks + 2
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NCB, 0);     // the last two k-steps
+            for (int tb = 0; tb < 2; ++tb)
+              ka[(ks + 1) & 1][tb] =
+                  *reinterpret_cast<const u32x4_t*>(s_k + L::k_off(tb * 32 + lc, (ks + 1) * 2 + hl));
+          }
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int j = 0; j < NCB; ++j)
+              sacc[j][tb] = Mfma<TB>::run(ka[ks & 1][tb], qf[j][ks], ks == 0 ? (f32x16_t){} : sacc[j][tb]);
+        }
+        // keep the read-ahead: the scheduler would otherwise pull each read down to its MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // LDS reads of k-steps 0, 1
+#pragma unroll
+        for (int ks = 0; ks + 2 < KS; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * NCB, 0);   // MFMAs of k-step ks
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // reads of k-step ks + 2
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NCB, 0);     // the last two k-steps
+        // keys a row cannot see get -inf (only tiles that cross some row's visible end)
+        if (k0 + kBN > wmin) {
+#pragma unroll
+          for (int j = 0; j < NCB; ++j) {
+            // element i of token block tb holds key k0 + tb*32 + (i/4)*8 + hl*4 + i%4;
+            // compare its compile-time part against a per-lane threshold
+            const int thr = vis[j] - k0 - hl * 4;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                if (tb * 32 + (i >> 2) * 8 + (i & 3) >= thr) sacc[j][tb][i] = -INFINITY;
+          }
+        }
+      };
+      scores();
       // ---- online softmax (lane = one query row of each column block) ---------------
-      // keys a row cannot see get -inf (only tiles that cross some row's visible end)
-      if (k0 + kBN > wmin) {
+      // probabilities -> packed B fragments of O^T = V^T P^T, against the running max as
+      // it stands; the lane's sum of its rounded probabilities (dot2 against ones: the
+      // values the P.V product consumes) comes with them
+      u32x4_t pf[NCB][4];
+      float lt[NCB];
+      auto probabilities = [&]() {
 #pragma unroll
         for (int j = 0; j < NCB; ++j) {
-          // element i of token block tb holds key k0 + tb*32 + (i/4)*8 + hl*4 + i%4;
-          // compare its compile-time part against a per-lane threshold
-          const int thr = vis[j] - k0 - hl * 4;
+          float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (tb * 32 + (i >> 2) * 8 + (i & 3) >= thr) sacc[j][tb][i] = -INFINITY;
+            for (int h2 = 0; h2 < 2; ++h2) {
+              float pr[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                pr[e] = fast_exp2(__builtin_fmaf(sacc[j][tb][h2 * 8 + e], c, -m[j]));
+              const u32x4_t q4 = (u32x4_t){pack2(TB{}, pr[0], pr[1]), pack2(TB{}, pr[2], pr[3]),
+                                           pack2(TB{}, pr[4], pr[5]), pack2(TB{}, pr[6], pr[7])};
+              ls0 = dot2(TB{}, q4[0], kOnes2<TB>(), ls0);
+              ls1 = dot2(TB{}, q4[1], kOnes2<TB>(), ls1);
+              ls0 = dot2(TB{}, q4[2], kOnes2<TB>(), ls0);
+              ls1 = dot2(TB{}, q4[3], kOnes2<TB>(), ls1);
+              pf[j][tb * 2 + h2] = q4;
+            }
+          lt[j] = ls0 + ls1;
         }
+      };
+      // The running max moves only when the probabilities of some row of this tile sum past
+      // kSumCap (so each of them stays <= kSumCap, finite in bf16 and fp32), or on the
+      // workgroup's first tile, where it is still -inf (every row sees key 0, so it is
+      // finite afterwards).  Only then is the tile's row max taken, O and l rescaled, and
+      // the probabilities recomputed.
+      bool redo = k0 == 0;
+      if (!redo) {
+        probabilities();
+        bool over = false;
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) over |= !(lt[j] <= kSumCap);
+        redo = __any(over);
       }
-      // row max on raw scores (scale > 0 on this path), scaled to log2 units
-      bool grow = false;
-      float tmax[NCB];
-#pragma unroll
-      for (int j = 0; j < NCB; ++j) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int i = 0; i < 16; i += 2)
-            mx = __builtin_fmaxf(__builtin_fmaxf(mx, sacc[j][tb][i]), sacc[j][tb][i + 1]);   // v_max3
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-        tmax[j] = mx;
-        grow |= mx > m[j] + kLazy;
-      }
-      if (__builtin_expect(__any(grow), 0)) {
+      if (__builtin_expect(redo, 0)) {
+        // the scores again (the K tile is still in its slot): the first ones are not kept
+        // alive past the probabilities, which keeps the tile within 256 registers
+        if (k0 != 0) scores();
 #pragma unroll
         for (int j = 0; j < NCB; ++j) {
-          const float mn = fmaxf(m[j], tmax[j]);
+          // row max on raw scores (scale > 0 on this path), scaled to log2 units
+          float mx = -INFINITY;
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2)
+              mx = __builtin_fmaxf(__builtin_fmaxf(mx, sacc[j][tb][i]), sacc[j][tb][i + 1]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+          const float mn = fmaxf(m[j], mx);
           const float alpha = (m[j] == -INFINITY) ? 0.f : fast_exp2(m[j] - mn);
           lsum[j] *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[j][db] *= alpha;
           m[j] = mn;
         }
+        probabilities();
       }
-      // probabilities -> packed B fragments of O^T = V^T P^T
-      u32x4_t pf[NCB][4];
 #pragma unroll
-      for (int j = 0; j < NCB; ++j) {
-        // the row sum uses the rounded pairs the P.V product uses (dot2 against ones)
-        float ls = lsum[j];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            float pr[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              pr[e] = fast_exp2(__builtin_fmaf(sacc[j][tb][h2 * 8 + e], c, -m[j]));
-            const u32x4_t q4 = (u32x4_t){pack2(TB{}, pr[0], pr[1]), pack2(TB{}, pr[2], pr[3]),
-                                         pack2(TB{}, pr[4], pr[5]), pack2(TB{}, pr[6], pr[7])};
-#pragma unroll
-            for (int w = 0; w < 4; ++w) ls = dot2(TB{}, q4[w], kOnes2<TB>(), ls);
-            pf[j][tb * 2 + h2] = q4;
-          }
-        lsum[j] = ls;
-      }
+      for (int j = 0; j < NCB; ++j) lsum[j] += lt[j];
       // ---- O^T += V^T P^T --------------------------------------------------------------
 #pragma unroll
       for (int ks = 0; ks < kBN / 16; ++ks) {
