@@ -61,6 +61,20 @@ def test_chunked_prefill_scaled(gpu):
     _run(wl.chunked_prefill())
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "fp8"])
+def test_prefill_large_scores_rescale(gpu, dtype):
+    """Scores spread over tens of log2 units (scale 2): key tiles after the first often lift
+    some row's probabilities past the bound the kernel keeps them under, so the running
+    max moves mid-row (row max, O and l rescaled, probabilities taken again), and the
+    result stays on the oracle."""
+    w = wl.chunked_prefill(seed=41, num_seqs=3, ctx_hi=700, q_lo=70, q_hi=260,
+                           dtype="bf16" if dtype == "fp8" else dtype)
+    w.scale = 2.0
+    if dtype == "fp8":
+        w = wl.with_fp8_cache(w)
+    _run(w)
+
+
 def test_long_block_causal_sampled(gpu):
     """4 x 8192 tokens, 64 q heads, block-causal spans of 2048: sampled rows and heads."""
     w = wl.long_block_causal()
