@@ -61,15 +61,18 @@ def test_chunked_prefill_scaled(gpu):
     _run(wl.chunked_prefill())
 
 
+@pytest.mark.parametrize("mask", [wl.MASK_CAUSAL, wl.MASK_BLOCK_CAUSAL])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "fp8"])
-def test_prefill_large_scores_rescale(gpu, dtype):
+def test_prefill_large_scores_rescale(gpu, dtype, mask):
     """Scores spread over tens of log2 units (scale 2): key tiles after the first often lift
     some row's probabilities past the bound the kernel keeps them under, so the running
-    max moves mid-row (row max, O and l rescaled, probabilities taken again), and the
-    result stays on the oracle."""
+    max moves mid-row (row max, O and l rescaled, probabilities taken again), also on the
+    masked tiles of a block-causal mask, and the result stays on the oracle."""
     w = wl.chunked_prefill(seed=41, num_seqs=3, ctx_hi=700, q_lo=70, q_hi=260,
                            dtype="bf16" if dtype == "fp8" else dtype)
     w.scale = 2.0
+    w.mask = mask
+    w.span_len = 96
     if dtype == "fp8":
         w = wl.with_fp8_cache(w)
     _run(w)
